@@ -1,0 +1,231 @@
+"""Pins of the oracle's FP4 codec against definitions it does not use.
+
+The oracle rounds by exhaustive nearest-value search in double precision.
+These tests check it against (a) literal tables from the format
+specifications (tests/golden), (b) torch's own E4M3 decoder, (c) exact
+rational arithmetic (fractions.Fraction) for every rounding midpoint, and
+(d) invariants of block quantization.  Format: E2M1 codes with one E4M3 scale
+per 16 channels, no global scale (helmcode.com/deepseek-v41-flash, section
+"04 · FP4"); scale = amax/6.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden_e2m1():
+    out = {}
+    for line in open(os.path.join(GOLDEN, "e2m1_grid.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        c, v = line.split()
+        out[int(c)] = float(v)
+    return out
+
+
+def torch_e4m3():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+
+
+def nearest_even(x: Fraction, table):
+    """table: list of (value Fraction, code int); nearest value, ties to
+    the even code.  Exact rational arithmetic."""
+    best = None
+    for v, c in table:
+        d = abs(x - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0 and best[1] % 2 == 1):
+            best = (d, c)
+    return best[1]
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def f32_neighbours(x):
+    x = np.float32(x)
+    return [float(np.nextafter(x, np.float32(-np.inf))), float(x),
+            float(np.nextafter(x, np.float32(np.inf)))]
+
+
+def test_e2m1_table(oracle):
+    g = golden_e2m1()
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        assert v == g[c]
+        assert math.copysign(1.0, v) == math.copysign(1.0, g[c])
+
+
+def test_e4m3_table(oracle):
+    ref = torch_e4m3()
+    for b in range(256):
+        v = oracle.e4m3_value(b)
+        if np.isnan(ref[b]):
+            assert math.isnan(v) and b in (0x7F, 0xFF)
+        else:
+            assert v == ref[b], b
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def _scale_table():
+    ref = torch_e4m3()
+    return [(Fraction(float(ref[b])), b) for b in range(127)]
+
+
+def test_scale_rounding_all_midpoints(oracle):
+    """Every midpoint between adjacent E4M3 values (times 6), and its fp32
+    neighbours, rounds as exact nearest-even rounding of amax/6 says."""
+    tab = _scale_table()
+    vals = sorted(tab)
+    checked = 0
+    for (v0, _), (v1, _) in zip(vals[:-1], vals[1:]):
+        mid = (v0 + v1) / 2
+        for amax in f32_neighbours(float(6 * mid)):
+            if amax < 0:
+                continue
+            want = nearest_even(Fraction(amax) / 6, tab)
+            assert oracle.scale_byte(amax) == want, (amax, want)
+            checked += 1
+    assert checked > 3 * 120
+    # saturation: beyond 448 (no NaN is ever produced)
+    for amax in (6 * 448.0, 6 * 460.0, 6 * 1000.0, 1e30):
+        assert oracle.scale_byte(amax) == 0x7E
+    assert oracle.scale_byte(0.0) == 0
+
+
+def test_scale_rounding_matches_torch_cast(oracle):
+    """Away from saturation, torch's RNE cast of amax/6 agrees (the fp32
+    quotient is used only where it cannot sit on a midpoint)."""
+    rng = np.random.default_rng(1)
+    amax = (10.0 ** rng.uniform(-3.5, 3.3, 4000)).astype(np.float32)
+    q = torch.from_numpy(amax.astype(np.float64) / 6.0)
+    ref = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for a, r in zip(amax, ref):
+        assert oracle.scale_byte(float(a)) == int(r)
+
+
+def test_e2m1_code_all_midpoints(oracle):
+    """For all 126 positive finite scales, every E2M1 midpoint t*s and its
+    fp32 neighbours (both signs) round as exact nearest-even says, and
+    magnitudes past 6*s clamp to 6."""
+    g = golden_e2m1()
+    grid = [(Fraction(g[c]), c) for c in range(8)]
+    mids = [Fraction(1, 4), Fraction(3, 4), Fraction(5, 4), Fraction(7, 4),
+            Fraction(5, 2), Fraction(7, 2), Fraction(5)]
+    ref = torch_e4m3()
+    n = 0
+    for b in range(1, 127):
+        s = float(ref[b])
+        sf = Fraction(s)
+        for t in mids + [Fraction(6), Fraction(7), Fraction(100)]:
+            for x in f32_neighbours(float(t * sf)):
+                want = nearest_even(Fraction(x) / sf, grid)
+                assert oracle.e2m1_code(x, s) == want, (b, x)
+                assert oracle.e2m1_code(-x, s) == (want | 8), (b, -x)
+                n += 2
+    assert n > 126 * 10 * 3 * 2 - 1
+    # the documented tie cases at scale 1
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for x, c in ties.items():
+        assert oracle.e2m1_code(x, 1.0) == c
+
+
+def test_zero_and_sign(oracle):
+    assert oracle.e2m1_code(0.0, 1.0) == 0
+    assert oracle.e2m1_code(-0.0, 1.0) == 8
+    assert oracle.e2m1_code(-0.1, 1.0) == 8
+    assert oracle.e2m1_code(5.0, 0.0) == 0
+    assert oracle.e2m1_code(-5.0, 0.0) == 8
+
+
+def _parse_blocks():
+    blocks, cur = [], {}
+    for line in open(os.path.join(GOLDEN, "block_quant_example.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, val = line.split(":", 1)
+        cur[key.strip()] = val.split()
+        if key.strip() == "codes":
+            blocks.append(cur)
+            cur = {}
+    return blocks
+
+
+def test_golden_blocks(oracle):
+    blocks = _parse_blocks()
+    assert len(blocks) == 3
+    for blk in blocks:
+        x = np.array([float(v) for v in blk["x"]], np.float32)[None, :]
+        codes, scales = oracle.quantize(x)
+        assert scales[0, 0] == int(blk["scale"][0], 16)
+        want = [int(c) for c in blk["codes"]]
+        got = [(codes[0, i // 2] >> (4 * (i % 2))) & 15 for i in range(16)]
+        assert got == want
+
+
+def test_roundtrip_grid_and_error(oracle):
+    """Dequantized values lie on grid x scale; the per-element error is at
+    most the scale (plus the clamp excess when the scale rounded down)."""
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((512, 64)) * 10.0 ** rng.uniform(-4, 3, (512, 1))).astype(np.float32)
+    x[5] = 0.0
+    x[6, :16] = -0.0
+    codes, scales = oracle.quantize(x)
+    deq = oracle.dequant(codes, scales)
+    ref = torch_e4m3()
+    g = np.array([golden_e2m1()[c] for c in range(8)])
+    for r in range(x.shape[0]):
+        for b in range(4):
+            s = ref[scales[r, b]]
+            blk = x[r, b * 16:(b + 1) * 16].astype(np.float64)
+            d = deq[r, b * 16:(b + 1) * 16]
+            for v in d:
+                assert np.any(np.abs(np.abs(v) - g * s) == 0.0)
+            amax = np.abs(blk).max()
+            assert np.all(np.abs(blk - d) <= max(s, amax - 6 * s) + 0.0)
+    assert (codes[5] == 0).all() and (scales[5] == 0).all()
+    assert (codes[6, :8] == 0x88).all()
+
+
+def test_requantize_is_identity_for_normal_scales(oracle):
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((1024, 32)) * 10.0 ** rng.uniform(-2, 2.5, (1024, 1))).astype(np.float32)
+    c1, s1 = oracle.quantize(x)
+    d1 = oracle.dequant(c1, s1).astype(np.float32)
+    c2, s2 = oracle.quantize(d1)
+    normal = (s1 >= 8)  # E4M3 exponent field != 0
+    for r in range(x.shape[0]):
+        for b in range(2):
+            if normal[r, b]:
+                assert s2[r, b] == s1[r, b]
+                assert (c2[r, b * 8:(b + 1) * 8] == c1[r, b * 8:(b + 1) * 8]).all()
+
+
+def test_block_max_maps_to_code_6(oracle):
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((2000, 16)) * 10.0 ** rng.uniform(-2, 2.5, (2000, 1))).astype(np.float32)
+    codes, scales = oracle.quantize(x)
+    for r in range(x.shape[0]):
+        if scales[r, 0] < 8:
+            continue
+        i = int(np.argmax(np.abs(x[r])))
+        c = (codes[r, i // 2] >> (4 * (i % 2))) & 7
+        assert c == 7
+
+
+def test_bytes_per_token(oracle):
+    assert oracle.bytes_per_token(576) == 324
+    assert oracle.bytes_per_token(128) == 72
+    x = np.zeros((3, 576), np.float32)
+    c, s = oracle.quantize(x)
+    assert c.nbytes + s.nbytes == 3 * 324
+    # a 1,048,576-token main cache is about 0.3 GB (0.34 GB)
+    gb = 1048576 * 324 / 1e9
+    assert 0.3 <= gb < 0.35
