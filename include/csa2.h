@@ -1,0 +1,267 @@
+/*
+ * csa2.h -- C ABI of libcsa2.so: the CSA2 compressed-sparse-attention step
+ * with an FP4 (E2M1) global KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The step has five parts, each an entry point below:
+ *   quantize-on-write of KV rows into FP4, indexer scoring of cached
+ *   positions, per-query Top-K selection (optionally through a candidate
+ *   pool), sparse attention over the Top-K rows plus an FP8 sliding window,
+ *   and the per-layer Full / Reindex / Reuse modes that chain them.
+ *
+ * Pages cited (address and section):
+ *   [P1] helmcode.com/deepseek-v41-flash
+ *   [P4] louisbouchard.ai/deepseek-v41-flash-kv-cache-writing-benchmark
+ *   [P5] 0x0moeen.in/writes/deepseek-v4-1-flash-kv-cache
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.  Scratch memory is
+ *    a caller-owned device workspace sized by the matching *_workspace_bytes
+ *    query.  A workspace must be zero-filled once before its first use
+ *    (csa2_workspace_init); every successful call leaves its control words
+ *    zero again, so it can be reused by the next call without clearing.  One
+ *    workspace must not be used by two calls that may run concurrently.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous; results are valid once the stream has been synchronised.
+ *  - Every argument is checked on the host before anything is launched; an
+ *    invalid argument returns an error status and launches nothing.  A HIP
+ *    launch failure returns CSA2_ERR_HIP; outputs are then undefined and
+ *    the workspace must be re-initialised.  csa2_last_error() gives a
+ *    per-thread message for the last failure.  No C++ exception crosses
+ *    this interface.
+ *  - Non-finite inputs are unsupported (results unspecified).
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *
+ * FP4 cache layout ([P1 §04 "FP4"]: E2M1 elements, one E4M3 scale per 16
+ * channels, no extra global scale).  For a row of `dim` channels:
+ *    codes  : dim/2 bytes, channel 2i in the low nibble of byte i,
+ *             nibble = sign | 2 exponent bits (bias 1) | 1 mantissa bit;
+ *    scales : dim/16 bytes, E4M3 ("FN": bias 7, 0x7F/0xFF NaN, max 448),
+ *             scale of channels [16j, 16j+16).
+ * A cache holds `cap` rows per sequence, sequences back to back:
+ *    codes[B][cap][dim/2], scales[B][cap][dim/16]  (two planes).
+ * Row value = e2m1(code) * e4m3(scale) (exact in fp16 and bf16).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,        /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  CSA2_ERR_DTYPE = 3,       /* unknown dtype code */
+  CSA2_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  CSA2_ERR_UNSUPPORTED = 5, /* valid request outside what the kernels cover */
+  CSA2_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} csa2_status;
+
+/* Static per-layer mode ([P1 §03 "CSA2"]; [P5 "Then every layer stops asking
+ * the same question"]: the mode is fixed per layer, not chosen at run time). */
+typedef enum {
+  CSA2_MODE_FULL = 0,    /* writes its KV, scores every visible position, selects */
+  CSA2_MODE_REINDEX = 1, /* reuses another layer's KV, rescores with its own query */
+  CSA2_MODE_REUSE = 2    /* reuses another layer's KV and Top-K selection */
+} csa2_mode;
+
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+
+/* An FP4 cache: two device planes, see the layout above. */
+typedef struct {
+  uint8_t* codes;  /* [B][cap][dim/2] */
+  uint8_t* scales; /* [B][cap][dim/16] */
+  int32_t dim;     /* channels per row, a multiple of 16 */
+  int64_t cap;     /* rows per sequence */
+} csa2_fp4_cache;
+
+/* Limits of the kernels in this build. */
+#define CSA2_MAX_K 16384        /* Top-K and pool size */
+#define CSA2_HEADS 16           /* query heads of the attention kernel */
+#define CSA2_MAX_INDEX_HEADS 16 /* indexer heads */
+
+/* ------------------------------------------------------------------ */
+/* Quantize-on-write ([P1 §04 "FP4"]: E2M1 codes with an E4M3 scale per 16
+ * channels, applied after RoPE, so the rows passed here are post-RoPE).
+ *
+ * For every 16-channel block: amax = max |x|; scale = the E4M3 value nearest
+ * to amax/6 (ties to the even mantissa, saturating at 448); each element's
+ * code = the E2M1 value nearest to x/scale (ties to the even code, clamped
+ * at +-6, sign bit = sign bit of x; a zero scale gives magnitude 0).
+ *
+ *   x           : device, `rows` rows of `dim` elements (dtype), row i at
+ *                 x + i * x_row_stride elements.
+ *   dst_rows    : device int64 [rows] destination row of each input row in
+ *                 the planes (row index counted over all sequences, i.e.
+ *                 b * cap + position), or NULL for rows 0..rows-1.
+ *   codes/scales: device planes receiving dim/2 and dim/16 bytes per row.
+ * Errors: NULL pointers, rows < 0, dim % 16 != 0 or dim > 4096, stride < dim,
+ * unknown dtype.  rows == 0 launches nothing. */
+csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                             int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
+                             uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Indexer scoring ([P1 §03 "CSA2"]: a Reindex layer scores positions again
+ * with its own query; [P4 "Share the cache and the search work"]: the first
+ * global indexing layer scans the visible context; [P5]: layers share the
+ * indexer keys, stored in FP4).  For query row r (sequence b = r / T):
+ *
+ *   score[r][s] = sum_h w[r][h] * max(0, q_idx[r][h] . key_b(pos(s)))
+ *
+ * where pos(s) = s (flat) or pool[r][s] (pool given), for s < n_valid[r].
+ * Entries s >= n_valid[r] of the score row are left unspecified.
+ *
+ *   icache   : FP4 index-key cache (dim = D_I, a multiple of 128, <= 512).
+ *   q_idx    : device bf16 [B*T][H_I][D_I];  w : device f32 [B*T][H_I].
+ *   n_valid  : device int32 [B*T]; flat: positions [0, n_valid) are
+ *              visible (must be <= cap); pool: the number of valid slots.
+ *   pool     : device int32 [B*T][P] ascending positions (< cap) or NULL.
+ *   scores   : device f32 [B*T][n_out]; n_out >= every n_valid.
+ * Precision: products of the bf16 query and the exactly dequantized keys are
+ * accumulated in fp32 (each head's query is scaled by a power of two into
+ * fp16 range for the matrix cores; the scaling is undone exactly).
+ * Errors: NULL pointers, H_I outside [1,16], D_I not a multiple of 128 or
+ * > 512, B/T < 1, n_out < 1, P < 1 with a pool. */
+csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
+                             const uint16_t* q_idx, const float* w, int32_t H_I,
+                             const int32_t* n_valid, const int32_t* pool, int32_t P,
+                             int64_t n_out, float* scores, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Top-K selection ([P4 "Share the cache and the search work"]: sparse
+ * attention selects a fixed number of global entries from the indexer
+ * scores; a candidate pool is selected the same way).  For each row r:
+ * order slots s < n_valid[r] by score descending, equal scores (-0 == +0)
+ * by slot ascending; keep the first min(k, n_valid[r]); write their
+ * positions (slot_pos[r][s] when slot_pos is given, else s) ascending into
+ * idx_out[r][0..), padding with -1 up to k.  count_out[r] (optional)
+ * receives min(k, n_valid[r]).  slot_pos, when given, must be strictly
+ * increasing over the valid slots of each row.
+ *
+ *   scores : device f32 [rows][n];  n_valid : device int32 [rows] (<= n).
+ *   ws     : workspace of csa2_topk_workspace_bytes(rows, n, k) bytes.
+ * Errors: NULL pointers, rows < 1, n < 1, k < 1 or k > CSA2_MAX_K,
+ * n > 2^31 - 1, workspace too small. */
+size_t csa2_topk_workspace_bytes(int32_t rows, int64_t n, int32_t k);
+csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
+                      const int32_t* slot_pos, int32_t k, int32_t* idx_out, int32_t* count_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Sparse attention ([P4 "Share the cache and the search work"]: attention
+ * over the selected global entries alongside a local 128-token window;
+ * [P1 §04 "FP4"]: the window KV stays in FP8).  For query row r (sequence
+ * b = r / T, position p = q_pos[r]) and head h, one softmax over the union
+ * of
+ *   - the main-cache rows idx[r][j] (entries < 0 skipped), dequantized, and
+ *   - the window rows holding positions [p-W+1, p] that are present in the
+ *     window array (row i of sequence b holds position swa_pos0[b] + i),
+ *     valued e4m3(byte) * swa_scale[b];
+ * with logit = sm_scale * q[r][h] . k and value = the first dv channels of
+ * the same row:
+ *   out[r][h] = sum_j softmax_j(logit) * v_j,  lse[r][h] = log sum_j exp(logit_j).
+ * The same position in both sets counts twice.  No entries: out = 0,
+ * lse = -inf.
+ *
+ *   q        : device bf16 [B*T][H][D], H == CSA2_HEADS, D = kv->dim.
+ *   kv       : FP4 main cache (dim a multiple of 64, <= 1024).
+ *   idx      : device int32 [B*T][K], entries < kv->cap or negative.
+ *   swa      : device uint8 [B][S][D] E4M3;  swa_scale : device f32 [B];
+ *   swa_pos0 : device int32 [B];  W >= 0 window length; S >= 0 rows.
+ *   q_pos    : device int32 [B*T].
+ *   out      : device f32 [B*T][H][dv] (dv a multiple of 64, <= D);
+ *   lse      : device f32 [B*T][H] or NULL.
+ *   ws       : workspace of csa2_sparse_attn_workspace_bytes(B*T, K, W, dv).
+ * Precision: logits accumulate in fp32 from exact fp16 key values and the
+ * bf16 query scaled per head by a power of two; probabilities are rounded
+ * to fp16 for the value product, accumulated in fp32.
+ * Errors: NULL pointers, H != CSA2_HEADS, bad D/dv, K < 0 (K == 0 allowed),
+ * W or S < 0, workspace too small. */
+size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int32_t dv);
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                             const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                             const uint8_t* swa, const float* swa_scale, const int32_t* swa_pos0,
+                             int32_t S, int32_t W, const int32_t* q_pos, float sm_scale,
+                             int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------ */
+/* One CSA2 layer for B sequences of T query tokens each ([P1 §03 "CSA2"]:
+ * Full builds its KV and searches, Reindex reuses an earlier Full layer's
+ * KV and rescores with its own query, Reuse reuses both KV and selection,
+ * each layer keeping its own query and window; [P4]: the first indexing
+ * layer keeps a candidate pool that later indexing layers search).
+ *
+ *   FULL    : quantize new_kv / new_ikey into kv / icache at rows q_pos;
+ *             score positions [0, q_pos] of icache with q_idx, w_idx;
+ *             if P > 0: pool_out = Top-P (ascending), pool_count_out =
+ *             its size, idx_out = Top-K inside the pool (== flat Top-K);
+ *             else idx_out = Top-K; attend over idx_out and the window.
+ *   REINDEX : no write; score icache with its own q_idx, w_idx over
+ *             [0, q_pos] (pool_in == NULL) or over pool_in's
+ *             pool_count_in valid slots; Top-K -> idx_out; attend.
+ *   REUSE   : attend over idx_in.
+ * kv / icache are the layer's own caches for FULL and the referenced
+ * layer's caches otherwise. */
+typedef struct {
+  int32_t B, T;          /* sequences, query tokens per sequence */
+  int32_t H, D, dv;      /* 16 query heads, row channels, value channels */
+  int32_t H_I, D_I;      /* indexer heads and channels */
+  int32_t K;             /* Top-K (<= CSA2_MAX_K) */
+  int32_t P;             /* FULL: pool size to keep (0 = none) */
+  int32_t S, W;          /* window array rows per sequence, window length */
+  float sm_scale;
+  csa2_fp4_cache kv;     /* main cache, dim D */
+  csa2_fp4_cache icache; /* index-key cache, dim D_I (unused by REUSE) */
+  const int32_t* q_pos;  /* [B*T] position of each query token */
+  const void* new_kv;    /* FULL: [B*T][D] rows to write */
+  const void* new_ikey;  /* FULL: [B*T][D_I] rows to write */
+  csa2_dtype new_dtype;  /* dtype of new_kv / new_ikey */
+  const uint16_t* q;     /* bf16 [B*T][H][D] */
+  const uint16_t* q_idx; /* bf16 [B*T][H_I][D_I] (FULL, REINDEX) */
+  const float* w_idx;    /* [B*T][H_I] (FULL, REINDEX) */
+  const uint8_t* swa;    /* [B][S][D] E4M3 */
+  const float* swa_scale;   /* [B] */
+  const int32_t* swa_pos0;  /* [B] */
+  const int32_t* idx_in;    /* REUSE: [B*T][K] */
+  int32_t* idx_out;         /* FULL, REINDEX: [B*T][K] */
+  const int32_t* pool_in;   /* REINDEX (optional): [B*T][P_in] */
+  const int32_t* pool_count_in; /* REINDEX with pool_in: [B*T] */
+  int32_t P_in;             /* row length of pool_in */
+  int32_t* pool_out;        /* FULL with P > 0: [B*T][P] */
+  int32_t* pool_count_out;  /* FULL with P > 0: [B*T] */
+  float* out;               /* [B*T][H][dv] */
+  float* lse;               /* [B*T][H] or NULL */
+} csa2_layer_args;
+
+size_t csa2_workspace_bytes(csa2_mode mode, const csa2_layer_args* a);
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Helpers. */
+/* Stored bytes per token of an FP4 row: dim/2 + dim/16 (324 for 576). */
+int64_t csa2_fp4_bytes_per_token(int32_t dim);
+/* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
+csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream);
+const char* csa2_status_string(csa2_status s);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* csa2_last_error(void);
+/* Library version string. */
+const char* csa2_version(void);
+/* sizeof(csa2_layer_args) and sizeof(csa2_fp4_cache) as compiled into the
+ * library, so bindings can check their struct layout. */
+size_t csa2_layer_args_size(void);
+size_t csa2_fp4_cache_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -204,7 +204,7 @@ def layer_step(mode: int, *, q, swa, swa_scale, swa_pos0, W, sm_scale, dv, K,
                kv_codes, kv_scales, q_pos, ix_codes=None, ix_scales=None,
                q_idx=None, w_idx=None, new_kv=None, new_ikey=None,
                idx_in=None, P: int = 0, pool_in=None, pool_count_in=None,
-               keep_scores: bool = False) -> LayerResult:
+               keep_scores: bool = False, write_pos=None) -> LayerResult:
     """One CSA2 layer for one sequence ([P1 §03 CSA2]; [P5 "Then every layer
     stops asking the same question"]: static Full / Reindex / Reuse modes).
 
@@ -213,7 +213,9 @@ def layer_step(mode: int, *, q, swa, swa_scale, swa_pos0, W, sm_scale, dv, K,
     attends.  REINDEX scores the referenced caches with its own indexer
     query (inside pool_in when given).  REUSE attends over idx_in.  The
     caches passed in are modified in place by FULL (the write is part of
-    the step).  Positions visible to token t: [0, q_pos[t]]."""
+    the step).  Positions visible to token t: [0, q_pos[t]].  ``write_pos``
+    (default q_pos) lists the rows FULL writes, so a sample of a prefill
+    chunk's tokens can be evaluated after the whole chunk is written."""
     q = np.asarray(q, np.float32)
     T = q.shape[0]
     H = q.shape[1]
@@ -224,12 +226,13 @@ def layer_step(mode: int, *, q, swa, swa_scale, swa_pos0, W, sm_scale, dv, K,
     pool_counts = np.zeros(T, np.int32) if pools is not None else None
     kept = [] if keep_scores else None
     if mode == FULL:
+        wp = q_pos if write_pos is None else write_pos
         nc, ns = quantize(new_kv)
-        kv_codes[q_pos] = nc
-        kv_scales[q_pos] = ns
+        kv_codes[wp] = nc
+        kv_scales[wp] = ns
         ic, iS = quantize(new_ikey)
-        ix_codes[q_pos] = ic
-        ix_scales[q_pos] = iS
+        ix_codes[wp] = ic
+        ix_scales[wp] = iS
     for t in range(T):
         p = int(q_pos[t])
         if mode in (FULL, REINDEX):

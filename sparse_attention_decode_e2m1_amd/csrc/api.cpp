@@ -1,0 +1,435 @@
+// api.cpp -- host side of libcsa2.so: argument checks, workspace layout and
+// the launch sequence of each entry point declared in include/csa2.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/csa2.h"
+#include "csa2_internal.hpp"
+
+using namespace csa2;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa2_status fail(csa2_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+csa2_status fail(csa2_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+csa2_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA2_OK;
+  return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define CSA2_TRY(expr, what)                         \
+  do {                                               \
+    csa2_status _s = hip_check((expr), (what));      \
+    if (_s != CSA2_OK) return _s;                    \
+  } while (0)
+
+#define CSA2_REQUIRE(cond, status, ...)              \
+  do {                                               \
+    if (!(cond)) return fail((status), __VA_ARGS__); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int32_t kRowChunk = 256;  // query rows scored / selected / attended per pass
+
+int32_t cand_cap_for(int32_t k) {
+  int64_t c = 8LL * k;
+  c = std::max<int64_t>(c, 16384);
+  c = std::min<int64_t>(c, 131072);
+  return (int32_t)c;
+}
+
+// A bump allocator over the caller's workspace.  The per-row control block
+// (kCtlWordsPerRow words) always comes first, so every kind of call finds
+// its control words at the same offsets.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* ws) : base((char*)ws) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+struct TopkLayout {
+  TopkWs tw;
+  size_t bytes;
+};
+
+// Control block of row r: [0,4096) histogram, [4096,4098) TopkCtl,
+// [4098] attention split counter.
+void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
+  uint32_t* ctl = c.take<uint32_t>((size_t)rows * kCtlWordsPerRow);
+  if (tw) {
+    tw->hist = ctl;
+    tw->hist_stride = kCtlWordsPerRow;
+    tw->ctl = reinterpret_cast<TopkCtl*>(ctl ? ctl + 4096 : nullptr);
+    tw->ctl_stride = kCtlWordsPerRow / 2;
+  }
+  if (aw) {
+    aw->cnt = ctl ? ctl + 4098 : nullptr;
+    aw->cnt_stride = kCtlWordsPerRow;
+  }
+}
+
+void carve_topk(Carve& c, int32_t rows, int64_t n, int32_t k, TopkWs* tw) {
+  tw->cand_cap = cand_cap_for(k);
+  tw->cand = c.take<uint64_t>((size_t)rows * tw->cand_cap);
+  tw->bm_words = (n + 31) / 32;
+  tw->bitmap = c.take<uint32_t>((size_t)rows * tw->bm_words);
+}
+
+void carve_attn(Carve& c, int32_t rows, int32_t K, int32_t W, int32_t dv, AttnWs* aw) {
+  const AttnSplit sp = attn_split(K, W);
+  aw->part = c.take<float>((size_t)rows * sp.nsplit * (16 * (size_t)dv + 32));
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool attn_shape_ok(int32_t D, int32_t dv) { return (D == 576 && dv == 512) || (D == 128 && dv == 128); }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "null pointer";
+    case CSA2_ERR_SHAPE: return "bad shape";
+    case CSA2_ERR_DTYPE: return "bad dtype";
+    case CSA2_ERR_WORKSPACE: return "workspace too small";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported";
+    case CSA2_ERR_HIP: return "hip error";
+  }
+  return "unknown status";
+}
+
+const char* csa2_last_error(void) { return g_last_error.c_str(); }
+
+const char* csa2_version(void) { return "csa2-mi355x 0.1 (gfx950)"; }
+
+size_t csa2_layer_args_size(void) { return sizeof(csa2_layer_args); }
+size_t csa2_fp4_cache_size(void) { return sizeof(csa2_fp4_cache); }
+
+int64_t csa2_fp4_bytes_per_token(int32_t dim) {
+  if (dim <= 0 || dim % 16) return -1;
+  return dim / 2 + dim / 16;
+}
+
+csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (ws_bytes == 0) return CSA2_OK;
+  CSA2_REQUIRE(ws, CSA2_ERR_NULL, "workspace is NULL");
+  CSA2_TRY(launch_fill_zero(ws, ws_bytes, as_stream(stream)), "workspace fill");
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------ quantize
+csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                             int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
+                             uint8_t* scales, void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(dtype == CSA2_F32 || dtype == CSA2_BF16, CSA2_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  CSA2_REQUIRE(rows >= 0, CSA2_ERR_SHAPE, "rows < 0");
+  CSA2_REQUIRE(dim > 0 && dim % 16 == 0 && dim <= 4096, CSA2_ERR_SHAPE,
+               "dim must be a positive multiple of 16 <= 4096 (got %d)", dim);
+  CSA2_REQUIRE(x_row_stride >= dim, CSA2_ERR_SHAPE, "row stride %lld < dim %d",
+               (long long)x_row_stride, dim);
+  if (rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(x && codes && scales, CSA2_ERR_NULL, "x, codes and scales are required");
+  CSA2_TRY(launch_quantize(x, dtype == CSA2_BF16, rows, dim, x_row_stride, dst_rows, codes, scales,
+                           as_stream(stream)),
+           "quantize launch");
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------ index score
+static csa2_status check_icache(const csa2_fp4_cache* c, const char* name) {
+  CSA2_REQUIRE(c, CSA2_ERR_NULL, "%s cache descriptor is NULL", name);
+  CSA2_REQUIRE(c->codes && c->scales, CSA2_ERR_NULL, "%s cache planes are NULL", name);
+  CSA2_REQUIRE(c->cap >= 1, CSA2_ERR_SHAPE, "%s cache capacity < 1", name);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
+                             const uint16_t* q_idx, const float* w, int32_t H_I,
+                             const int32_t* n_valid, const int32_t* pool, int32_t P,
+                             int64_t n_out, float* scores, void* stream) {
+  g_last_error.clear();
+  csa2_status s = check_icache(icache, "index");
+  if (s) return s;
+  CSA2_REQUIRE(B >= 1 && T >= 1, CSA2_ERR_SHAPE, "B and T must be >= 1");
+  CSA2_REQUIRE(H_I >= 1 && H_I <= CSA2_MAX_INDEX_HEADS, CSA2_ERR_SHAPE, "H_I must be in [1,16]");
+  CSA2_REQUIRE(icache->dim % 128 == 0 && icache->dim >= 128 && icache->dim <= 512,
+               CSA2_ERR_UNSUPPORTED, "index dim must be 128, 256, 384 or 512 (got %d)",
+               icache->dim);
+  CSA2_REQUIRE(q_idx && w && n_valid && scores, CSA2_ERR_NULL,
+               "q_idx, w, n_valid and scores are required");
+  CSA2_REQUIRE(n_out >= 1, CSA2_ERR_SHAPE, "n_out < 1");
+  CSA2_REQUIRE(!pool || P >= 1, CSA2_ERR_SHAPE, "pool given with P < 1");
+  CSA2_REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_SHAPE, "B*T must be <= 65535");
+  const int64_t n_max = pool ? std::min<int64_t>(P, n_out) : std::min<int64_t>(icache->cap, n_out);
+  CSA2_TRY(launch_index_score(icache->codes, icache->scales, icache->dim, icache->cap, B * T, T,
+                              q_idx, w, H_I, n_valid, 0, pool, pool ? P : 0, n_max, scores, n_out,
+                              nullptr, 0, as_stream(stream)),
+           "index score launch");
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------ top-k
+size_t csa2_topk_workspace_bytes(int32_t rows, int64_t n, int32_t k) {
+  if (rows < 1 || n < 1 || k < 1) return 0;
+  Carve c(nullptr);
+  TopkWs tw;
+  carve_ctl(c, rows, &tw, nullptr);
+  carve_topk(c, rows, n, k, &tw);
+  return c.off;
+}
+
+csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
+                      const int32_t* slot_pos, int32_t k, int32_t* idx_out, int32_t* count_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(rows >= 1 && rows <= 65535, CSA2_ERR_SHAPE, "rows must be in [1,65535]");
+  CSA2_REQUIRE(n >= 1 && n <= 0x7FFFFFFF, CSA2_ERR_SHAPE, "n must be in [1, 2^31-1]");
+  CSA2_REQUIRE(k >= 1 && k <= CSA2_MAX_K, CSA2_ERR_SHAPE, "k must be in [1,%d]", CSA2_MAX_K);
+  CSA2_REQUIRE(scores && n_valid && idx_out, CSA2_ERR_NULL, "scores, n_valid and idx_out are required");
+  const size_t need = csa2_topk_workspace_bytes(rows, n, k);
+  CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
+               need, ws_bytes);
+  Carve c(ws);
+  TopkWs tw;
+  carve_ctl(c, rows, &tw, nullptr);
+  carve_topk(c, rows, n, k, &tw);
+  const hipStream_t st = as_stream(stream);
+  CSA2_TRY(launch_topk_hist(scores, rows, n, n_valid, 0, n, tw.hist, tw.hist_stride, st),
+           "top-k histogram launch");
+  CSA2_TRY(launch_topk_select(scores, rows, n, n_valid, 0, n, slot_pos, k, idx_out, count_out, tw, st),
+           "top-k select launch");
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------ attention
+size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int32_t dv) {
+  if (rows < 1 || K < 0 || W < 0 || dv < 1) return 0;
+  Carve c(nullptr);
+  AttnWs aw;
+  carve_ctl(c, rows, nullptr, &aw);
+  carve_attn(c, rows, K, W, dv, &aw);
+  return c.off;
+}
+
+static csa2_status check_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                              const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                              const uint8_t* swa, const float* swa_scale,
+                              const int32_t* swa_pos0, int32_t S, int32_t W,
+                              const int32_t* q_pos, int32_t dv, const float* out) {
+  csa2_status s = check_icache(kv, "main");
+  if (s) return s;
+  CSA2_REQUIRE(B >= 1 && T >= 1, CSA2_ERR_SHAPE, "B and T must be >= 1");
+  CSA2_REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_SHAPE, "B*T must be <= 65535");
+  CSA2_REQUIRE(H == CSA2_HEADS, CSA2_ERR_UNSUPPORTED, "H must be %d (got %d)", CSA2_HEADS, H);
+  CSA2_REQUIRE(attn_shape_ok(kv->dim, dv), CSA2_ERR_UNSUPPORTED,
+               "(D, dv) must be (576, 512) or (128, 128) (got (%d, %d))", kv->dim, dv);
+  CSA2_REQUIRE(K >= 0 && K <= CSA2_MAX_K, CSA2_ERR_SHAPE, "K must be in [0,%d]", CSA2_MAX_K);
+  CSA2_REQUIRE(W >= 0 && S >= 0, CSA2_ERR_SHAPE, "W and S must be >= 0");
+  CSA2_REQUIRE(q && q_pos && out, CSA2_ERR_NULL, "q, q_pos and out are required");
+  CSA2_REQUIRE(K == 0 || idx, CSA2_ERR_NULL, "idx is required when K > 0");
+  CSA2_REQUIRE(W == 0 || S == 0 || (swa && swa_scale && swa_pos0), CSA2_ERR_NULL,
+               "swa, swa_scale and swa_pos0 are required when W > 0 and S > 0");
+  return CSA2_OK;
+}
+
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                             const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                             const uint8_t* swa, const float* swa_scale, const int32_t* swa_pos0,
+                             int32_t S, int32_t W, const int32_t* q_pos, float sm_scale,
+                             int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  csa2_status s = check_attn(q, B, T, H, kv, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, dv, out);
+  if (s) return s;
+  const int32_t rows = B * T;
+  const int32_t Weff = (S > 0) ? W : 0;
+  const size_t need = csa2_sparse_attn_workspace_bytes(rows, K, Weff, dv);
+  CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
+               need, ws_bytes);
+  Carve c(ws);
+  AttnWs aw;
+  carve_ctl(c, rows, nullptr, &aw);
+  carve_attn(c, rows, K, Weff, dv, &aw);
+  CSA2_TRY(launch_sparse_attn(q, rows, T, kv->dim, dv, kv->codes, kv->scales, kv->cap, idx, K,
+                              swa, swa_scale, swa_pos0, S, Weff, q_pos, sm_scale, out, lse, aw,
+                              as_stream(stream)),
+           "sparse attention launch");
+  return CSA2_OK;
+}
+
+// ------------------------------------------------------------ layer step
+namespace {
+
+struct StepLayout {
+  int32_t rc;         // rows per pass
+  int64_t n_out;      // score row length
+  TopkWs tw;
+  AttnWs aw;
+  float* scores;
+  float* pscores;     // FULL with a pool: pool members' scores
+  size_t bytes;
+};
+
+StepLayout step_layout(csa2_mode mode, const csa2_layer_args* a, void* ws) {
+  StepLayout L{};
+  const int32_t rows = a->B * a->T;
+  L.rc = std::min(rows, kRowChunk);
+  const bool pooled_in = (mode == CSA2_MODE_REINDEX && a->pool_in);
+  L.n_out = (mode == CSA2_MODE_REUSE) ? 1 : (pooled_in ? a->P_in : a->icache.cap);
+  const int32_t Weff = (a->S > 0) ? a->W : 0;
+  Carve c(ws);
+  carve_ctl(c, L.rc, &L.tw, &L.aw);
+  if (mode != CSA2_MODE_REUSE) {
+    L.scores = c.take<float>((size_t)L.rc * L.n_out);
+    const int32_t kmax = (mode == CSA2_MODE_FULL && a->P > 0) ? std::max(a->P, a->K) : a->K;
+    if (mode == CSA2_MODE_FULL && a->P > 0) L.pscores = c.take<float>((size_t)L.rc * a->P);
+    carve_topk(c, L.rc, std::max<int64_t>(L.n_out, a->P), kmax, &L.tw);
+  }
+  carve_attn(c, L.rc, a->K, Weff, a->dv, &L.aw);
+  L.bytes = c.off;
+  return L;
+}
+
+csa2_status check_step(csa2_mode mode, const csa2_layer_args* a) {
+  CSA2_REQUIRE(a, CSA2_ERR_NULL, "layer args are NULL");
+  CSA2_REQUIRE(mode == CSA2_MODE_FULL || mode == CSA2_MODE_REINDEX || mode == CSA2_MODE_REUSE,
+               CSA2_ERR_SHAPE, "unknown mode %d", (int)mode);
+  csa2_status s = check_attn(a->q, a->B, a->T, a->H, &a->kv,
+                             mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out, a->K, a->swa,
+                             a->swa_scale, a->swa_pos0, a->S, a->W, a->q_pos, a->dv, a->out);
+  if (s) return s;
+  CSA2_REQUIRE(a->D == a->kv.dim, CSA2_ERR_SHAPE, "D (%d) != kv.dim (%d)", a->D, a->kv.dim);
+  if (mode == CSA2_MODE_REUSE) {
+    CSA2_REQUIRE(a->K == 0 || a->idx_in, CSA2_ERR_NULL, "REUSE needs idx_in");
+    return CSA2_OK;
+  }
+  s = check_icache(&a->icache, "index");
+  if (s) return s;
+  CSA2_REQUIRE(a->K >= 1, CSA2_ERR_SHAPE, "FULL/REINDEX need K >= 1");
+  CSA2_REQUIRE(a->D_I == a->icache.dim, CSA2_ERR_SHAPE, "D_I (%d) != icache.dim (%d)", a->D_I,
+               a->icache.dim);
+  CSA2_REQUIRE(a->D_I % 128 == 0 && a->D_I >= 128 && a->D_I <= 512, CSA2_ERR_UNSUPPORTED,
+               "index dim must be 128, 256, 384 or 512");
+  CSA2_REQUIRE(a->H_I >= 1 && a->H_I <= CSA2_MAX_INDEX_HEADS, CSA2_ERR_SHAPE, "H_I must be in [1,16]");
+  CSA2_REQUIRE(a->q_idx && a->w_idx && a->idx_out, CSA2_ERR_NULL,
+               "q_idx, w_idx and idx_out are required");
+  CSA2_REQUIRE(a->icache.cap <= 0x7FFFFFFF, CSA2_ERR_SHAPE, "index cache capacity too large");
+  if (mode == CSA2_MODE_FULL) {
+    CSA2_REQUIRE(a->new_kv && a->new_ikey, CSA2_ERR_NULL, "FULL needs new_kv and new_ikey");
+    CSA2_REQUIRE(a->new_dtype == CSA2_F32 || a->new_dtype == CSA2_BF16, CSA2_ERR_DTYPE,
+                 "unknown dtype %d", (int)a->new_dtype);
+    CSA2_REQUIRE(a->P >= 0 && a->P <= CSA2_MAX_K, CSA2_ERR_SHAPE, "P must be in [0,%d]", CSA2_MAX_K);
+    CSA2_REQUIRE(a->P == 0 || a->P >= a->K, CSA2_ERR_SHAPE, "P must be >= K");
+    CSA2_REQUIRE(a->P == 0 || (a->pool_out && a->pool_count_out), CSA2_ERR_NULL,
+                 "FULL with P > 0 needs pool_out and pool_count_out");
+  } else {
+    CSA2_REQUIRE(!a->pool_in || (a->pool_count_in && a->P_in >= 1), CSA2_ERR_SHAPE,
+                 "pool_in needs pool_count_in and P_in >= 1");
+  }
+  return CSA2_OK;
+}
+
+}  // namespace
+
+size_t csa2_workspace_bytes(csa2_mode mode, const csa2_layer_args* a) {
+  if (check_step(mode, a) != CSA2_OK) return 0;
+  return step_layout(mode, a, nullptr).bytes;
+}
+
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_last_error.clear();
+  csa2_status s = check_step(mode, a);
+  if (s) return s;
+  const size_t need = step_layout(mode, a, nullptr).bytes;
+  CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
+               need, ws_bytes);
+  const StepLayout L = step_layout(mode, a, ws);
+  const hipStream_t st = as_stream(stream);
+  const int32_t rows = a->B * a->T;
+  const int32_t Weff = (a->S > 0) ? a->W : 0;
+
+  if (mode == CSA2_MODE_FULL)
+    CSA2_TRY(launch_quantize_step(a->new_kv, a->new_ikey, a->new_dtype == CSA2_BF16, rows, a->T,
+                                  a->q_pos, a->D, a->kv.cap, a->kv.codes, a->kv.scales, a->D_I,
+                                  a->icache.cap, a->icache.codes, a->icache.scales, st),
+             "quantize-on-write launch");
+
+  for (int32_t r0 = 0; r0 < rows; r0 += L.rc) {
+    const int32_t nr = std::min(L.rc, rows - r0);
+    // Row r0+j of this pass is row j of every per-pass buffer; the kernels
+    // see the pass as B' = nr / T' sequences only when T divides it, so the
+    // sequence index is recovered from the absolute row below.
+    const int32_t* qpos = a->q_pos + r0;
+    if (mode != CSA2_MODE_REUSE) {
+      const bool pooled_in = (mode == CSA2_MODE_REINDEX && a->pool_in);
+      const uint16_t* qi = a->q_idx + (size_t)r0 * a->H_I * a->D_I;
+      const float* wi = a->w_idx + (size_t)r0 * a->H_I;
+      const int32_t* nvp = pooled_in ? a->pool_count_in + r0 : qpos;
+      const int32_t nv_add = pooled_in ? 0 : 1;
+      const int32_t* pool = pooled_in ? a->pool_in + (size_t)r0 * a->P_in : nullptr;
+      const int64_t n_max = pooled_in ? a->P_in : a->icache.cap;
+      CSA2_TRY(launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
+                                  qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
+                                  L.scores, L.n_out, L.tw.hist, L.tw.hist_stride, st, r0),
+               "index score launch");
+      int32_t* idx = a->idx_out + (size_t)r0 * a->K;
+      if (mode == CSA2_MODE_FULL && a->P > 0) {
+        int32_t* pool_out = a->pool_out + (size_t)r0 * a->P;
+        int32_t* pcount = a->pool_count_out + r0;
+        CSA2_TRY(launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
+                                    pcount, L.tw, st),
+                 "pool select launch");
+        CSA2_TRY(launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
+                                      L.tw.hist, L.tw.hist_stride, st),
+                 "pool gather launch");
+        CSA2_TRY(launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
+                                    nullptr, L.tw, st),
+                 "top-k select launch");
+      } else {
+        CSA2_TRY(launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,
+                                    pooled_in ? pool : nullptr, a->K, idx, nullptr, L.tw, st),
+                 "top-k select launch");
+      }
+    }
+    const int32_t* idx_att = (mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out) + (size_t)r0 * a->K;
+    CSA2_TRY(launch_sparse_attn(a->q + (size_t)r0 * a->H * a->D, nr, a->T, a->D, a->dv, a->kv.codes,
+                                a->kv.scales, a->kv.cap, idx_att, a->K, a->swa, a->swa_scale,
+                                a->swa_pos0, a->S, Weff, qpos, a->sm_scale,
+                                a->out + (size_t)r0 * a->H * a->dv,
+                                a->lse ? a->lse + (size_t)r0 * a->H : nullptr, L.aw, st, r0),
+             "sparse attention launch");
+  }
+  return CSA2_OK;
+}
+
+}  // extern "C"

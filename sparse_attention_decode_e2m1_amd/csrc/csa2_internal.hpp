@@ -1,0 +1,95 @@
+// csa2_internal.hpp -- launchers and workspace layout shared by the HIP
+// translation units of libcsa2.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int32_t kScoreChunk = 4096;  // positions per scoring block
+constexpr int32_t kTopkChunk = 8192;   // scores per select block
+constexpr int32_t kAttnTilesPerSplit = 8;
+
+// Per-row control words of the Top-K pass, zero between calls.
+struct TopkCtl {
+  uint32_t cand;  // candidates appended
+  uint32_t done;  // select blocks finished
+};
+
+// Every call keeps the control words of query row r in one fixed-size block
+// at the start of the workspace, so any workspace left zero by a previous
+// call (of any kind or shape) is ready for the next.
+constexpr int64_t kCtlWordsPerRow = 4096 + 8;  // histogram, TopkCtl, attention counter, pad
+inline uint32_t* row_hist(void* ws) { return reinterpret_cast<uint32_t*>(ws); }
+
+struct TopkWs {
+  uint32_t* hist;       // row r at hist + r * hist_stride (4096 bins)
+  int64_t hist_stride;  // in words
+  TopkCtl* ctl;         // row r at ctl + r * ctl_stride
+  int64_t ctl_stride;   // in TopkCtl units
+  uint64_t* cand;       // [rows][cand_cap]
+  int32_t cand_cap;
+  uint32_t* bitmap;   // [rows][bm_words]
+  int64_t bm_words;
+};
+
+struct AttnWs {
+  float* part;        // [rows][nsplit][16*dv + 32]
+  uint32_t* cnt;      // row r at cnt + r * cnt_stride
+  int64_t cnt_stride;
+};
+
+struct AttnSplit {
+  int32_t tps, nsg, nsw, nsplit;
+};
+inline AttnSplit attn_split(int32_t K, int32_t W) {
+  AttnSplit s;
+  s.tps = kAttnTilesPerSplit;
+  const int32_t tg = (K + 15) / 16, tw = (W + 15) / 16;
+  s.nsg = (tg + s.tps - 1) / s.tps;
+  if (s.nsg < 1) s.nsg = 1;
+  s.nsw = (tw + s.tps - 1) / s.tps;
+  s.nsplit = s.nsg + s.nsw;
+  return s;
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
+                           const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                           hipStream_t st);
+hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32_t DI,
+                              int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
+                              const float* w, int32_t HI, const int32_t* n_valid,
+                              int32_t nv_add, const int32_t* pool, int32_t P, int64_t n_max,
+                              float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
+                              hipStream_t st, int32_t row0 = 0);
+hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
+                            int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
+                            hipStream_t st);
+hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
+                              const int32_t* n_valid, int32_t nv_add, int64_t n_max,
+                              const int32_t* slot_pos, int32_t k, int32_t* idx_out,
+                              int32_t* count_out, const TopkWs& w, hipStream_t st);
+size_t topk_lds_bytes(int32_t k);
+hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_t D, int32_t dv,
+                              const uint8_t* codes, const uint8_t* scales, int64_t cap,
+                              const int32_t* idx, int32_t K, const uint8_t* swa,
+                              const float* swa_scale, const int32_t* swa_pos0, int32_t S,
+                              int32_t W, const int32_t* q_pos, float sm_scale, float* out,
+                              float* lse, const AttnWs& w, hipStream_t st, int32_t row0 = 0);
+size_t attn_lds_bytes(int32_t dv);
+// out[r][s] = scores[r][pool[r][s]] for s < count[r], and the histogram of
+// those scores into hist (row stride hist_stride).
+hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* pool, int32_t P,
+                                const int32_t* count, int32_t rows, float* out,
+                                uint32_t* hist, int64_t hist_stride, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// Quantize-on-write of one decode/prefill step: rows r of x1 (dim1) and x2
+// (dim2) go to cache row (r / T) * cap + q_pos[r] of their planes.
+hipError_t launch_quantize_step(const void* x1, const void* x2, bool bf16, int32_t rows,
+                                int32_t T, const int32_t* q_pos, int32_t dim1, int64_t cap1,
+                                uint8_t* codes1, uint8_t* scales1, int32_t dim2, int64_t cap2,
+                                uint8_t* codes2, uint8_t* scales2, hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,174 @@
+// quantize.hip -- quantize-on-write of KV rows into the FP4 cache.
+//
+// helmcode.com/deepseek-v41-flash, section "04 · FP4": the global KV is
+// stored as E2M1 elements with one E4M3 scale per 16 channels and no extra
+// global scale; quantisation is applied after RoPE.  Per block the scale is
+// the E4M3 value nearest to amax/6 and each element takes the nearest E2M1
+// grid value of x/scale.  Both roundings are decided by comparing against
+// thresholds that are exact in fp32, so no division (and no double
+// rounding) is involved.
+#include "csa2_device.hpp"
+#include "csa2_internal.hpp"
+
+namespace csa2 {
+
+// Positive finite E4M3 value of byte b (0..126); exact in fp32.
+__device__ __forceinline__ float e4m3_pos(int b) {
+  const int e = b >> 3, m = b & 7;
+  return (e == 0) ? (float)m * 0x1p-9f : ldexpf(1.0f + 0.125f * (float)m, e - 7);
+}
+
+// Scale byte = E4M3 value nearest to amax/6, ties to the even mantissa,
+// saturating at 448.  Threshold b lies halfway between bytes b and b+1,
+// times 6: 3*(v_b + v_{b+1}) has at most 8 significant bits, so it is exact.
+// The byte is the number of thresholds amax passes (a tie passes when the
+// upper neighbour b+1 has an even mantissa).
+__device__ __forceinline__ int scale_byte(float amax) {
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const float t = 3.0f * (e4m3_pos(mid) + e4m3_pos(mid + 1));
+    const bool pass = amax > t || (amax == t && ((mid + 1) & 1) == 0);
+    if (pass)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// E2M1 magnitude code of |x| under scale s: nearest of {0,.5,1,1.5,2,3,4,6}*s
+// with ties to the even code.  Midpoints t*s (t = .25,.75,1.25,1.75,2.5,3.5,5)
+// are exact in fp32; ">=" at a midpoint rounds up onto an even code.
+__device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
+  if (s == 0.0f) return 0u;
+  uint32_t c = 0;
+  c += a > 0.25f * s;
+  c += a >= 0.75f * s;
+  c += a > 1.25f * s;
+  c += a >= 1.75f * s;
+  c += a > 2.5f * s;
+  c += a >= 3.5f * s;
+  c += a > 5.0f * s;
+  return c;
+}
+
+template <typename In>
+__device__ __forceinline__ float load_elem(const In* p);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p) {
+  return *p;
+}
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) {
+  return bf16_to_f32(*p);
+}
+
+// Quantize one 16-channel block: 8 code bytes and one scale byte.
+template <typename In>
+__device__ __forceinline__ void quantize_block(const In* __restrict__ src, uint8_t* code_dst,
+                                               uint8_t* scale_dst) {
+  float v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    v[c] = load_elem<In>(src + c);
+    amax = fmaxf(amax, fabsf(v[c]));
+  }
+  const int sb = scale_byte(amax);
+  const float s = e4m3_pos(sb);
+  uint64_t packed = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const uint32_t sign = (__float_as_uint(v[c]) >> 31) << 3;
+    const uint32_t code = sign | e2m1_mag(fabsf(v[c]), s);
+    packed |= (uint64_t)code << (4 * c);
+  }
+  *reinterpret_cast<uint64_t*>(code_dst) = packed;
+  *scale_dst = (uint8_t)sb;
+}
+
+// One thread per 16-channel block.
+template <typename In>
+__global__ __launch_bounds__(256) void quantize_kernel(const In* __restrict__ x, int64_t rows,
+                                                       int32_t dim, int64_t stride,
+                                                       const int64_t* __restrict__ dst_rows,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int32_t nb = dim >> 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * nb) return;
+  const int64_t r = t / nb;
+  const int32_t blk = (int32_t)(t - r * nb);
+  const int64_t dr = dst_rows ? dst_rows[r] : r;
+  quantize_block<In>(x + r * stride + (int64_t)blk * 16, codes + dr * (dim >> 1) + (int64_t)blk * 8,
+                     scales + dr * nb + blk);
+}
+
+// The write of a decode or prefill step: query row r of x1 and x2 lands on
+// cache row (r / T) * cap + q_pos[r] of each cache (one launch for both).
+template <typename In>
+__global__ __launch_bounds__(256) void quantize_step_kernel(
+    const In* __restrict__ x1, const In* __restrict__ x2, int32_t rows, int32_t T,
+    const int32_t* __restrict__ q_pos, int32_t dim1, int64_t cap1, uint8_t* __restrict__ codes1,
+    uint8_t* __restrict__ scales1, int32_t dim2, int64_t cap2, uint8_t* __restrict__ codes2,
+    uint8_t* __restrict__ scales2) {
+  const int64_t n1 = (int64_t)rows * (dim1 >> 4);
+  const int64_t n2 = (int64_t)rows * (dim2 >> 4);
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const In* x = x1;
+  int32_t dim = dim1;
+  int64_t cap = cap1;
+  uint8_t* codes = codes1;
+  uint8_t* scales = scales1;
+  if (t >= n1) {
+    t -= n1;
+    if (t >= n2) return;
+    x = x2;
+    dim = dim2;
+    cap = cap2;
+    codes = codes2;
+    scales = scales2;
+  }
+  const int32_t nb = dim >> 4;
+  const int64_t r = t / nb;
+  const int32_t blk = (int32_t)(t - r * nb);
+  const int64_t dr = (r / T) * cap + q_pos[r];
+  quantize_block<In>(x + r * dim + (int64_t)blk * 16, codes + dr * (dim >> 1) + (int64_t)blk * 8,
+                     scales + dr * nb + blk);
+}
+
+hipError_t launch_quantize_step(const void* x1, const void* x2, bool bf16, int32_t rows,
+                                int32_t T, const int32_t* q_pos, int32_t dim1, int64_t cap1,
+                                uint8_t* codes1, uint8_t* scales1, int32_t dim2, int64_t cap2,
+                                uint8_t* codes2, uint8_t* scales2, hipStream_t st) {
+  const int64_t n = (int64_t)rows * (dim1 / 16 + dim2 / 16);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(quantize_step_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)x1,
+                       (const uint16_t*)x2, rows, T, q_pos, dim1, cap1, codes1, scales1, dim2,
+                       cap2, codes2, scales2);
+  else
+    hipLaunchKernelGGL(quantize_step_kernel<float>, grid, block, 0, st, (const float*)x1,
+                       (const float*)x2, rows, T, q_pos, dim1, cap1, codes1, scales1, dim2, cap2,
+                       codes2, scales2);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
+                           const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                           hipStream_t st) {
+  const int64_t n = rows * (dim / 16);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(quantize_kernel<uint16_t>, grid, block, 0, st,
+                       (const uint16_t*)x, rows, dim, stride, dst_rows, codes, scales);
+  else
+    hipLaunchKernelGGL(quantize_kernel<float>, grid, block, 0, st, (const float*)x, rows, dim,
+                       stride, dst_rows, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

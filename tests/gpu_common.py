@@ -1,0 +1,55 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+and the comparison rules (bit-exact bytes and indices; Top-K sets equal or
+differing only among scores within 1e-6 relative of the K-th score;
+attention within max-abs 2e-3 and rel-L2 1e-3 of the fp64 oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOPK_BAND = 1e-6
+ATT_MAX_ABS = 2e-3
+ATT_REL_L2 = 1e-3
+
+
+def dev(x, dtype=None):
+    t = torch.as_tensor(x)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous().cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def assert_topk_band(gpu_idx, ora_idx, ora_scores, k, slot_pos=None, what=""):
+    """GPU and oracle Top-K sets may differ only among entries whose oracle
+    score lies within TOPK_BAND (relative) of the oracle's k-th score."""
+    g = set(int(x) for x in gpu_idx if x >= 0)
+    o = set(int(x) for x in ora_idx if x >= 0)
+    assert len(g) == len(o), (what, len(g), len(o))
+    assert list(gpu_idx) == sorted(gpu_idx[gpu_idx >= 0].tolist()) + [-1] * int((gpu_idx < 0).sum())
+    if g == o:
+        return 0
+    # scores by position
+    if slot_pos is not None:
+        pos_score = {int(p): float(s) for p, s in zip(slot_pos, ora_scores)}
+    else:
+        pos_score = {i: float(s) for i, s in enumerate(ora_scores)}
+    kth = min(pos_score[p] for p in o)
+    tol = TOPK_BAND * max(abs(kth), 1e-300)
+    for p in g ^ o:
+        assert abs(pos_score[p] - kth) <= tol, (what, p, pos_score[p], kth)
+    return len(g ^ o)
+
+
+def assert_attention_close(gpu_out, ora_out, what=""):
+    g = np.asarray(gpu_out, np.float64)
+    o = np.asarray(ora_out, np.float64)
+    err = np.abs(g - o)
+    assert np.isfinite(g).all(), what
+    assert err.max() <= ATT_MAX_ABS, (what, err.max())
+    rel = np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30)
+    assert rel <= ATT_REL_L2, (what, rel)
+    return err.max(), rel

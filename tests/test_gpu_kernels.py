@@ -1,0 +1,319 @@
+"""GPU parity of each entry point, called through the C ABI, against the oracle.
+
+Bit-exact: FP4 codes and scale bytes, Top-K index sets fed the same fp32
+scores.  Floating point: indexer scores within an fp32-accumulation bound of
+the fp64 oracle; attention within max-abs 2e-3 and rel-L2 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_e2m1_amd import api
+from sparse_attention_decode_e2m1_amd import inputs as I
+from tests.gpu_common import (assert_attention_close, assert_topk_band, dev, host)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    print("\n[gpu] device:", torch.cuda.get_device_name(0), flush=True)
+    api.lib()
+
+
+def ctl_words_zero(ws, rows):
+    """The per-row control blocks at the start of a workspace are zero."""
+    words = ws[: rows * (4096 + 8) * 4].view(torch.int32)
+    return int(torch.count_nonzero(words)) == 0
+
+
+# ------------------------------------------------------------ quantize
+def special_rows(dim):
+    rng = np.random.default_rng(100)
+    rows = []
+    rows.append(np.zeros(dim))
+    rows.append(-np.zeros(dim))
+    rows.append(np.full(dim, 1e-30))
+    rows.append(rng.standard_normal(dim) * 1e4)          # saturating scales
+    rows.append(rng.standard_normal(dim) * 1e-3)         # subnormal scales
+    e4 = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = (e4[:-1] + e4[1:]) / 2
+    for j in range(0, 126, 3):                           # amax exactly 6 x midpoint
+        r = rng.standard_normal(dim) * 0.1 * mids[j]
+        r[::16] = 6 * mids[j]
+        rows.append(r)
+    for b in (8, 33, 56, 62, 90, 120):                    # elements exactly on E2M1 midpoints
+        s = e4[b]
+        t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+        r = np.resize(np.concatenate([t, -t]) * s, dim)
+        rows.append(r)
+    x = np.stack(rows).astype(np.float32)
+    # fp32 neighbours of every value, to probe both sides of each threshold
+    up = np.nextafter(x, np.float32(np.inf))
+    dn = np.nextafter(x, np.float32(-np.inf))
+    return np.concatenate([x, up, dn])
+
+
+@pytest.mark.parametrize("dim", [576, 128])
+def test_quantize_fp32_bit_exact(dim):
+    rng = np.random.default_rng(dim)
+    x = (rng.standard_normal((3000, dim)) * 10.0 ** rng.uniform(-4, 3, (3000, 1))).astype(np.float32)
+    x = np.concatenate([x, special_rows(dim)])
+    codes = torch.zeros((x.shape[0], dim // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((x.shape[0], dim // 16), dtype=torch.uint8, device="cuda")
+    api.quantize_kv(dev(x), codes, scales)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize(x)
+    assert np.array_equal(host(scales), os_)
+    assert np.array_equal(host(codes), oc)
+
+
+def test_quantize_bf16_and_scatter():
+    rng = np.random.default_rng(5)
+    xb = torch.from_numpy(rng.standard_normal((777, 576)).astype(np.float32)).to(torch.bfloat16)
+    dst = torch.from_numpy(rng.permutation(1000)[:777].astype(np.int64))
+    codes = torch.zeros((1000, 288), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((1000, 36), dtype=torch.uint8, device="cuda")
+    api.quantize_kv(xb.cuda(), codes, scales, dst_rows=dst.cuda())
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize(xb.float().numpy())
+    hc, hs = host(codes), host(scales)
+    assert np.array_equal(hc[dst.numpy()], oc) and np.array_equal(hs[dst.numpy()], os_)
+    untouched = np.setdiff1d(np.arange(1000), dst.numpy())
+    assert (hc[untouched] == 0).all()
+
+
+# ------------------------------------------------------------ index score
+def _index_case(seed, B, cap, DI, HI, n_valid):
+    rng = np.random.default_rng(seed)
+    keys = rng.standard_normal((B * cap, DI)).astype(np.float32)
+    ic, isc = oracle.quantize(keys)
+    q = torch.randn(B, HI, DI, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    w = torch.rand(B, HI, generator=torch.Generator().manual_seed(seed + 1))
+    return ic, isc, q, w
+
+
+def _abs_bound(ic, isc, q, w, rows):
+    k = oracle.dequant(ic[rows], isc[rows])
+    qa = np.abs(q.float().numpy().astype(np.float64))
+    return (np.abs(k) @ qa.T * np.abs(w.numpy().astype(np.float64))).sum(1)
+
+
+@pytest.mark.parametrize("DI,HI", [(128, 4), (128, 1), (128, 16), (256, 4)])
+def test_index_score_flat(DI, HI):
+    B, cap = 3, 9000
+    nv = np.array([9000, 4097, 1], np.int32)
+    ic, isc, q, w = _index_case(11 + DI + HI, B, cap, DI, HI, nv)
+    scores = torch.full((B, cap), np.nan, device="cuda")
+    cache = api.cache(dev(ic), dev(isc), DI, cap)
+    api.index_score(cache, B, 1, q.cuda(), w.cuda(), dev(nv), scores)
+    torch.cuda.synchronize()
+    g = host(scores)
+    for b in range(B):
+        rows = np.arange(b * cap, b * cap + nv[b])
+        o = oracle.index_scores(ic, isc, q[b].float().numpy(), w[b].numpy(), rows)
+        bound = _abs_bound(ic, isc, q[b], w[b], rows)
+        err = np.abs(g[b, : nv[b]] - o)
+        assert (err <= 1e-5 * bound + 1e-30).all(), (b, err.max())
+        assert np.isnan(g[b, nv[b]:]).all() or nv[b] == cap  # untouched beyond n_valid
+
+
+def test_index_score_pool():
+    B, cap, P = 2, 20000, 3000
+    rng = np.random.default_rng(3)
+    ic, isc, q, w = _index_case(21, B, cap, 128, 4, None)
+    pool = np.stack([np.sort(rng.choice(cap, P, replace=False)) for _ in range(B)]).astype(np.int32)
+    count = np.array([P, 1234], np.int32)
+    scores = torch.zeros((B, P), device="cuda")
+    cache = api.cache(dev(ic), dev(isc), 128, cap)
+    api.index_score(cache, B, 1, q.cuda(), w.cuda(), dev(count), scores, pool=dev(pool))
+    torch.cuda.synchronize()
+    g = host(scores)
+    for b in range(B):
+        rows = b * cap + pool[b, : count[b]].astype(np.int64)
+        o = oracle.index_scores(ic, isc, q[b].float().numpy(), w[b].numpy(), rows)
+        bound = _abs_bound(ic, isc, q[b], w[b], rows)
+        assert (np.abs(g[b, : count[b]] - o) <= 1e-5 * bound + 1e-30).all()
+
+
+def test_index_score_special_cases():
+    """One head, w = 1, q = e_c: score = relu(k[c]) exactly; negative query: 0."""
+    cap = 3000
+    rng = np.random.default_rng(9)
+    keys = rng.standard_normal((cap, 128)).astype(np.float32)
+    ic, isc = oracle.quantize(keys)
+    k_hat = oracle.dequant(ic, isc)
+    cache = api.cache(dev(ic), dev(isc), 128, cap)
+    for c in (0, 17, 64, 127):
+        q = torch.zeros(1, 1, 128)
+        q[0, 0, c] = 1.0
+        s = torch.zeros((1, cap), device="cuda")
+        api.index_score(cache, 1, 1, q.to(torch.bfloat16).cuda(), torch.ones(1, 1).cuda(),
+                        dev(np.array([cap], np.int32)), s)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(s)[0], np.maximum(k_hat[:, c], 0.0).astype(np.float32))
+    pos_keys = np.abs(keys)
+    pc, ps = oracle.quantize(pos_keys)
+    cache2 = api.cache(dev(pc), dev(ps), 128, cap)
+    q = -torch.ones(1, 4, 128)
+    s = torch.full((1, cap), 5.0, device="cuda")
+    api.index_score(cache2, 1, 1, q.to(torch.bfloat16).cuda(), torch.full((1, 4), 0.5).cuda(),
+                    dev(np.array([cap], np.int32)), s)
+    torch.cuda.synchronize()
+    assert (host(s) == 0).all()
+
+
+# ------------------------------------------------------------ top-k
+def _run_topk(scores_np, nv, k, slot_pos=None):
+    rows, n = scores_np.shape
+    ws = api.workspace(api.topk_workspace_bytes(rows, n, k))
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    api.topk(dev(scores_np), dev(np.asarray(nv, np.int32)), k, idx, ws,
+             slot_pos=None if slot_pos is None else dev(slot_pos), count_out=cnt)
+    torch.cuda.synchronize()
+    assert ctl_words_zero(ws, rows), "control words not cleared"
+    return host(idx), host(cnt), ws
+
+
+def _check_topk(scores_np, nv, k, slot_pos=None):
+    g, cnt, _ = _run_topk(scores_np, nv, k, slot_pos)
+    for r in range(scores_np.shape[0]):
+        sp = None if slot_pos is None else slot_pos[r]
+        o, c = oracle.topk(scores_np[r].astype(np.float64), int(nv[r]), k, slot_pos=sp)
+        assert np.array_equal(g[r], o), (r, k, int(nv[r]))
+        assert cnt[r] == c
+
+
+@pytest.mark.parametrize("n,k", [(1000, 1), (1000, 7), (4097, 256), (65536 + 5, 2048),
+                                 (20000, 16384), (300, 2048)])
+def test_topk_random(n, k):
+    rng = np.random.default_rng(n + k)
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    nv = np.array([n, max(1, n // 2 + 3), min(n, k + 1)], np.int32)
+    _check_topk(s, nv, k)
+
+
+def test_topk_ties_and_signed_zero():
+    rng = np.random.default_rng(1)
+    n = 50000
+    s = np.stack([
+        np.round(rng.standard_normal(n), 1),          # heavy ties
+        np.zeros(n),                                   # one tie storm (overflows the candidates)
+        np.where(rng.random(n) < 0.5, -0.0, 0.0),     # -0 == +0
+        rng.integers(0, 3, n).astype(np.float64),      # three values
+    ]).astype(np.float32)
+    nv = np.full(4, n, np.int32)
+    for k in (1, 100, 2048, 16384):
+        _check_topk(s, nv, k)
+
+
+def test_topk_large_rows():
+    rng = np.random.default_rng(2)
+    n = 1 << 20
+    s = rng.standard_normal((2, n)).astype(np.float32)
+    s[1, 123456] = 50.0
+    _check_topk(s, np.array([n, n - 77], np.int32), 2048)
+    _check_topk(s[:1], np.array([n], np.int32), 16384)
+
+
+def test_topk_slot_map():
+    rng = np.random.default_rng(4)
+    P = 16384
+    pool = np.stack([np.sort(rng.choice(1 << 20, P, replace=False)) for _ in range(2)]).astype(np.int32)
+    s = rng.standard_normal((2, P)).astype(np.float32)
+    _check_topk(s, np.array([P, 9000], np.int32), 2048, slot_pos=pool)
+
+
+def test_topk_deterministic_and_reusable_workspace():
+    rng = np.random.default_rng(6)
+    s = np.round(rng.standard_normal((2, 100000)), 2).astype(np.float32)
+    nv = np.array([100000, 99999], np.int32)
+    g1, _, ws = _run_topk(s, nv, 2048)
+    idx = torch.empty((2, 2048), dtype=torch.int32, device="cuda")
+    for _ in range(3):  # same workspace, no re-initialisation
+        api.topk(dev(s), dev(nv), 2048, idx, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), g1)
+
+
+# ------------------------------------------------------------ attention
+def _attn_case(seed, N, D=576, S=128):
+    rng = np.random.default_rng(seed)
+    kv = rng.standard_normal((N, D)).astype(np.float32)
+    codes, scales = oracle.quantize(kv)
+    swa_b, swa_s = I.fp8_rows(torch.from_numpy(rng.standard_normal((S, D)).astype(np.float32)))
+    return codes, scales, swa_b.numpy(), swa_s
+
+
+@pytest.mark.parametrize("K,W,npad", [(2048, 128, 0), (2048, 128, 37), (256, 0, 5), (0, 128, 0),
+                                      (100, 128, 0), (16, 1, 0)])
+def test_sparse_attn_parity(K, W, npad):
+    N, T = 6000, 3
+    codes, scales, swa, swa_s = _attn_case(K + W, N)
+    rng = np.random.default_rng(K * 7 + W)
+    idx = np.full((T, max(K, 1)), -1, np.int32)[:, :K]
+    for t in range(T):
+        sel = np.sort(rng.choice(N, K - npad, replace=False)) if K else np.zeros(0, np.int32)
+        idx[t, : len(sel)] = sel
+    q = torch.randn(T, 16, 576, generator=torch.Generator().manual_seed(K + W)).to(torch.bfloat16)
+    q_pos = np.array([N - 1, N - 50, N - 200], np.int32)   # window partly outside the array
+    S = 128
+    pos0 = N - S
+    sm = 1.0 / np.sqrt(576)
+    out = torch.full((T, 16, 512), np.nan, device="cuda")
+    lse = torch.full((T, 16), np.nan, device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(T, K, W, 512))
+    kvc = api.cache(dev(codes), dev(scales), 576, N)
+    api.sparse_attn(q.cuda(), 1, T, kvc, dev(idx) if K else None, K, dev(swa[None]),
+                    dev(np.array([swa_s], np.float32)), dev(np.array([pos0], np.int32)), S, W,
+                    dev(q_pos), float(np.float32(sm)), 512, out, lse, ws)
+    torch.cuda.synchronize()
+    assert ctl_words_zero(ws, T)
+    go, gl = host(out), host(lse)
+    for t in range(T):
+        wrows = oracle.window_rows(swa, pos0, int(q_pos[t]), W)
+        o, l = oracle.sparse_attn(q[t].float().numpy(), codes, scales, idx[t], wrows, swa_s,
+                                  float(np.float32(sm)), 512)
+        assert_attention_close(go[t], o, what=(K, W, t))
+        assert np.allclose(gl[t], l, atol=1e-4, rtol=1e-5)
+
+
+def test_sparse_attn_no_entries():
+    N = 100
+    codes, scales, swa, swa_s = _attn_case(1, N)
+    q = torch.randn(1, 16, 576).to(torch.bfloat16)
+    idx = np.full((1, 64), -1, np.int32)
+    out = torch.full((1, 16, 512), np.nan, device="cuda")
+    lse = torch.zeros((1, 16), device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(1, 64, 0, 512))
+    api.sparse_attn(q.cuda(), 1, 1, api.cache(dev(codes), dev(scales), 576, N), dev(idx), 64,
+                    None, None, None, 0, 0, dev(np.array([N - 1], np.int32)), 0.04, 512, out, lse, ws)
+    torch.cuda.synchronize()
+    assert (host(out) == 0).all() and np.isneginf(host(lse)).all()
+
+
+def test_sparse_attn_small_dims_and_batch():
+    """D = dv = 128 kernel variant, several sequences."""
+    B, N, K = 3, 2000, 300
+    rng = np.random.default_rng(8)
+    kv = rng.standard_normal((B * N, 128)).astype(np.float32)
+    codes, scales = oracle.quantize(kv)
+    swa_list = [I.fp8_rows(torch.from_numpy(rng.standard_normal((64, 128)).astype(np.float32)))
+                for _ in range(B)]
+    swa = np.stack([s[0].numpy() for s in swa_list])
+    swa_s = np.array([s[1] for s in swa_list], np.float32)
+    idx = np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(B)]).astype(np.int32)
+    q = torch.randn(B, 16, 128).to(torch.bfloat16)
+    q_pos = np.full(B, N - 1, np.int32)
+    pos0 = np.full(B, N - 64, np.int32)
+    out = torch.zeros((B, 16, 128), device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(B, K, 64, 128))
+    api.sparse_attn(q.cuda(), B, 1, api.cache(dev(codes), dev(scales), 128, N), dev(idx), K,
+                    dev(swa), dev(swa_s), dev(pos0), 64, 64, dev(q_pos), 0.09, 128, out, None, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o, _ = oracle.sparse_attn(q[b].float().numpy(), codes[b * N:(b + 1) * N],
+                                  scales[b * N:(b + 1) * N], idx[b], swa[b], float(swa_s[b]),
+                                  float(np.float32(0.09)), 128)
+        assert_attention_close(host(out)[b], o, what=b)
