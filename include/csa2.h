@@ -256,6 +256,16 @@ const char* csa2_status_string(csa2_status s);
 const char* csa2_last_error(void);
 /* Library version string. */
 const char* csa2_version(void);
+/* Optional launch timing for measurement.  After csa2_profile_begin(), every
+ * launch of the kernels below is bracketed by a pair of HIP events recorded
+ * on the launch stream; csa2_profile_end() waits for them, writes the number
+ * of launches and their summed duration (ms) per kernel, and stops
+ * recording.  Kernel ids: 0 quantize-on-write, 1 indexer scoring, 2 Top-K
+ * select, 3 sparse attention, 4 pool gather.  Not thread-safe; not for use
+ * under graph capture.  `counts` and `total_ms` hold 5 entries. */
+#define CSA2_PROFILE_KERNELS 5
+csa2_status csa2_profile_begin(void);
+csa2_status csa2_profile_end(int32_t* counts, double* total_ms);
 /* sizeof(csa2_layer_args) and sizeof(csa2_fp4_cache) as compiled into the
  * library, so bindings can check their struct layout. */
 size_t csa2_layer_args_size(void);

@@ -82,6 +82,8 @@ def lib():
             "csa2_version": (ctypes.c_char_p, []),
             "csa2_layer_args_size": (c_sz, []),
             "csa2_fp4_cache_size": (c_sz, []),
+            "csa2_profile_begin": (c_i32, []),
+            "csa2_profile_end": (c_i32, [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -213,6 +215,22 @@ def workspace_bytes(mode: int, args: LayerArgs) -> int:
 
 def layer_step(mode: int, args: LayerArgs, ws: torch.Tensor, stream=None):
     _check(lib().csa2_layer_step(mode, ctypes.byref(args), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+PROFILE_KERNELS = ("quantize", "index_score", "topk_select", "sparse_attn", "pool_gather")
+
+
+def profile_begin():
+    _check(lib().csa2_profile_begin())
+
+
+def profile_end() -> dict:
+    """{kernel: (launches, summed event time in ms)} since profile_begin()."""
+    n = len(PROFILE_KERNELS)
+    counts = (c_i32 * n)()
+    tot = (ctypes.c_double * n)()
+    _check(lib().csa2_profile_end(counts, tot))
+    return {k: (int(counts[i]), float(tot[i])) for i, k in enumerate(PROFILE_KERNELS)}
 
 
 def raw_call(name: str, *args):

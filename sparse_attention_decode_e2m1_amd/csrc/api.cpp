@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/csa2.h"
 #include "csa2_internal.hpp"
@@ -42,6 +44,50 @@ csa2_status hip_check(hipError_t e, const char* what) {
 #define CSA2_REQUIRE(cond, status, ...)              \
   do {                                               \
     if (!(cond)) return fail((status), __VA_ARGS__); \
+  } while (0)
+
+
+// ---- optional launch timing (csa2_profile_begin / csa2_profile_end)
+struct Profiler {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[CSA2_PROFILE_KERNELS];
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  hipEvent_t get() {
+    if (next == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[next++];
+  }
+};
+Profiler g_prof;
+
+// Records an event before and after one launch when profiling is on.
+struct ProfScope {
+  int id;
+  hipStream_t st;
+  hipEvent_t b = nullptr;
+  ProfScope(int id_, hipStream_t st_) : id(id_), st(st_) {
+    if (g_prof.on && (b = g_prof.get())) hipEventRecord(b, st);
+  }
+  ~ProfScope() {
+    if (!b) return;
+    hipEvent_t e = g_prof.get();
+    if (!e) return;
+    hipEventRecord(e, st);
+    g_prof.ev[id].push_back({b, e});
+  }
+};
+
+// Every entry point names its stream argument `stream`.
+#define PROF_STREAM reinterpret_cast<hipStream_t>(stream)
+#define CSA2_LAUNCH(id, st, expr, what)        \
+  do {                                          \
+    ProfScope _ps((id), (st));                  \
+    csa2_status _s = hip_check((expr), (what)); \
+    if (_s != CSA2_OK) return _s;               \
   } while (0)
 
 constexpr size_t kAlign = 256;
@@ -130,6 +176,33 @@ const char* csa2_last_error(void) { return g_last_error.c_str(); }
 const char* csa2_version(void) { return "csa2-mi355x 0.1 (gfx950)"; }
 
 size_t csa2_layer_args_size(void) { return sizeof(csa2_layer_args); }
+
+csa2_status csa2_profile_begin(void) {
+  g_last_error.clear();
+  for (auto& v : g_prof.ev) v.clear();
+  g_prof.next = 0;
+  g_prof.on = true;
+  return CSA2_OK;
+}
+
+csa2_status csa2_profile_end(int32_t* counts, double* total_ms) {
+  g_last_error.clear();
+  g_prof.on = false;
+  for (int k = 0; k < CSA2_PROFILE_KERNELS; ++k) {
+    double tot = 0.0;
+    for (auto& pr : g_prof.ev[k]) {
+      CSA2_TRY(hipEventSynchronize(pr.second), "profile event wait");
+      float ms = 0.0f;
+      CSA2_TRY(hipEventElapsedTime(&ms, pr.first, pr.second), "profile event time");
+      tot += ms;
+    }
+    if (counts) counts[k] = (int32_t)g_prof.ev[k].size();
+    if (total_ms) total_ms[k] = tot;
+    g_prof.ev[k].clear();
+  }
+  g_prof.next = 0;
+  return CSA2_OK;
+}
 size_t csa2_fp4_cache_size(void) { return sizeof(csa2_fp4_cache); }
 
 int64_t csa2_fp4_bytes_per_token(int32_t dim) {
@@ -158,7 +231,7 @@ csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int3
                (long long)x_row_stride, dim);
   if (rows == 0) return CSA2_OK;
   CSA2_REQUIRE(x && codes && scales, CSA2_ERR_NULL, "x, codes and scales are required");
-  CSA2_TRY(launch_quantize(x, dtype == CSA2_BF16, rows, dim, x_row_stride, dst_rows, codes, scales,
+  CSA2_LAUNCH(0, PROF_STREAM, launch_quantize(x, dtype == CSA2_BF16, rows, dim, x_row_stride, dst_rows, codes, scales,
                            as_stream(stream)),
            "quantize launch");
   return CSA2_OK;
@@ -190,7 +263,7 @@ csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
   CSA2_REQUIRE(!pool || P >= 1, CSA2_ERR_SHAPE, "pool given with P < 1");
   CSA2_REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_SHAPE, "B*T must be <= 65535");
   const int64_t n_max = pool ? std::min<int64_t>(P, n_out) : std::min<int64_t>(icache->cap, n_out);
-  CSA2_TRY(launch_index_score(icache->codes, icache->scales, icache->dim, icache->cap, B * T, T,
+  CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(icache->codes, icache->scales, icache->dim, icache->cap, B * T, T,
                               q_idx, w, H_I, n_valid, 0, pool, pool ? P : 0, n_max, scores, n_out,
                               nullptr, 0, as_stream(stream)),
            "index score launch");
@@ -223,9 +296,9 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
   carve_ctl(c, rows, &tw, nullptr);
   carve_topk(c, rows, n, k, &tw);
   const hipStream_t st = as_stream(stream);
-  CSA2_TRY(launch_topk_hist(scores, rows, n, n_valid, 0, n, tw.hist, tw.hist_stride, st),
+  CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(scores, rows, n, n_valid, 0, n, tw.hist, tw.hist_stride, st),
            "top-k histogram launch");
-  CSA2_TRY(launch_topk_select(scores, rows, n, n_valid, 0, n, slot_pos, k, idx_out, count_out, tw, st),
+  CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(scores, rows, n, n_valid, 0, n, slot_pos, k, idx_out, count_out, tw, st),
            "top-k select launch");
   return CSA2_OK;
 }
@@ -279,7 +352,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
   AttnWs aw;
   carve_ctl(c, rows, nullptr, &aw);
   carve_attn(c, rows, K, Weff, dv, &aw);
-  CSA2_TRY(launch_sparse_attn(q, rows, T, kv->dim, dv, kv->codes, kv->scales, kv->cap, idx, K,
+  CSA2_LAUNCH(3, PROF_STREAM, launch_sparse_attn(q, rows, T, kv->dim, dv, kv->codes, kv->scales, kv->cap, idx, K,
                               swa, swa_scale, swa_pos0, S, Weff, q_pos, sm_scale, out, lse, aw,
                               as_stream(stream)),
            "sparse attention launch");
@@ -379,7 +452,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
   const int32_t Weff = (a->S > 0) ? a->W : 0;
 
   if (mode == CSA2_MODE_FULL)
-    CSA2_TRY(launch_quantize_step(a->new_kv, a->new_ikey, a->new_dtype == CSA2_BF16, rows, a->T,
+    CSA2_LAUNCH(0, PROF_STREAM, launch_quantize_step(a->new_kv, a->new_ikey, a->new_dtype == CSA2_BF16, rows, a->T,
                                   a->q_pos, a->D, a->kv.cap, a->kv.codes, a->kv.scales, a->D_I,
                                   a->icache.cap, a->icache.codes, a->icache.scales, st),
              "quantize-on-write launch");
@@ -398,7 +471,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       const int32_t nv_add = pooled_in ? 0 : 1;
       const int32_t* pool = pooled_in ? a->pool_in + (size_t)r0 * a->P_in : nullptr;
       const int64_t n_max = pooled_in ? a->P_in : a->icache.cap;
-      CSA2_TRY(launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
+      CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
                                   qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
                                   L.scores, L.n_out, L.tw.hist, L.tw.hist_stride, st, r0),
                "index score launch");
@@ -406,23 +479,23 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       if (mode == CSA2_MODE_FULL && a->P > 0) {
         int32_t* pool_out = a->pool_out + (size_t)r0 * a->P;
         int32_t* pcount = a->pool_count_out + r0;
-        CSA2_TRY(launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
+        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
                                     pcount, L.tw, st),
                  "pool select launch");
-        CSA2_TRY(launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
+        CSA2_LAUNCH(4, PROF_STREAM, launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
                                       L.tw.hist, L.tw.hist_stride, st),
                  "pool gather launch");
-        CSA2_TRY(launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
+        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
                                     nullptr, L.tw, st),
                  "top-k select launch");
       } else {
-        CSA2_TRY(launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,
+        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,
                                     pooled_in ? pool : nullptr, a->K, idx, nullptr, L.tw, st),
                  "top-k select launch");
       }
     }
     const int32_t* idx_att = (mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out) + (size_t)r0 * a->K;
-    CSA2_TRY(launch_sparse_attn(a->q + (size_t)r0 * a->H * a->D, nr, a->T, a->D, a->dv, a->kv.codes,
+    CSA2_LAUNCH(3, PROF_STREAM, launch_sparse_attn(a->q + (size_t)r0 * a->H * a->D, nr, a->T, a->D, a->dv, a->kv.codes,
                                 a->kv.scales, a->kv.cap, idx_att, a->K, a->swa, a->swa_scale,
                                 a->swa_pos0, a->S, Weff, qpos, a->sm_scale,
                                 a->out + (size_t)r0 * a->H * a->dv,
