@@ -148,7 +148,7 @@ csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
  *   scores : device f32 [rows][n];  n_valid : device int32 [rows] (<= n).
  *   ws     : workspace of csa2_topk_workspace_bytes(rows, n, k) bytes.
  * Errors: NULL pointers, rows < 1, n < 1, k < 1 or k > CSA2_MAX_K,
- * n > 2^31 - 1, workspace too small. */
+ * n > 2^25, workspace too small. */
 size_t csa2_topk_workspace_bytes(int32_t rows, int64_t n, int32_t k);
 csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                       const int32_t* slot_pos, int32_t k, int32_t* idx_out, int32_t* count_out,
@@ -251,6 +251,10 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws,
 int64_t csa2_fp4_bytes_per_token(int32_t dim);
 /* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream);
+/* Bytes at the start of a workspace that hold control words for `rows`
+ * query rows: they must be zero when a call starts, and every successful
+ * call leaves them zero. */
+size_t csa2_workspace_control_bytes(int32_t rows);
 const char* csa2_status_string(csa2_status s);
 /* Message of the last failing call on this host thread ("" if none). */
 const char* csa2_last_error(void);

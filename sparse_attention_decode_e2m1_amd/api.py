@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcsa2.so")
+LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(HERE, "libcsa2.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "csa2.h")
 
 FULL, REINDEX, REUSE = 0, 1, 2
@@ -82,6 +82,7 @@ def lib():
             "csa2_version": (ctypes.c_char_p, []),
             "csa2_layer_args_size": (c_sz, []),
             "csa2_fp4_cache_size": (c_sz, []),
+            "csa2_workspace_control_bytes": (c_sz, [c_i32]),
             "csa2_profile_begin": (c_i32, []),
             "csa2_profile_end": (c_i32, [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]),
         }

@@ -95,13 +95,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int32_t kRowChunk = 256;  // query rows scored / selected / attended per pass
 
-int32_t cand_cap_for(int32_t k) {
-  int64_t c = 8LL * k;
-  c = std::max<int64_t>(c, 16384);
-  c = std::min<int64_t>(c, 131072);
-  return (int32_t)c;
-}
-
 // A bump allocator over the caller's workspace.  The per-row control block
 // (kCtlWordsPerRow words) always comes first, so every kind of call finds
 // its control words at the same offsets.
@@ -117,32 +110,27 @@ struct Carve {
   }
 };
 
-struct TopkLayout {
-  TopkWs tw;
-  size_t bytes;
-};
-
-// Control block of row r: [0,4096) histogram, [4096,4098) TopkCtl,
-// [4098] attention split counter.
+// Control block of row r: the kHistWords histogram copies.
 void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
   uint32_t* ctl = c.take<uint32_t>((size_t)rows * kCtlWordsPerRow);
   if (tw) {
     tw->hist = ctl;
     tw->hist_stride = kCtlWordsPerRow;
-    tw->ctl = reinterpret_cast<TopkCtl*>(ctl ? ctl + 4096 : nullptr);
-    tw->ctl_stride = kCtlWordsPerRow / 2;
   }
-  if (aw) {
-    aw->cnt = ctl ? ctl + 4098 : nullptr;
-    aw->cnt_stride = kCtlWordsPerRow;
-  }
+  (void)aw;
 }
 
+// Kept-position and candidate regions: one kTopkChunk region of each per
+// select block of a row, and the blocks' counts.
 void carve_topk(Carve& c, int32_t rows, int64_t n, int32_t k, TopkWs* tw) {
-  tw->cand_cap = cand_cap_for(k);
-  tw->cand = c.take<uint64_t>((size_t)rows * tw->cand_cap);
-  tw->bm_words = (n + 31) / 32;
-  tw->bitmap = c.take<uint32_t>((size_t)rows * tw->bm_words);
+  (void)k;
+  const int64_t nblk = std::max<int64_t>(1, (n + kTopkChunk - 1) / kTopkChunk);
+  tw->above_stride = nblk * kTopkChunk;
+  tw->above = c.take<uint32_t>((size_t)rows * tw->above_stride);
+  tw->cand_stride = nblk * kTopkChunk;
+  tw->cand = c.take<uint64_t>((size_t)rows * tw->cand_stride);
+  tw->counts_stride = 2 * nblk;
+  tw->counts = c.take<uint32_t>((size_t)rows * tw->counts_stride);
 }
 
 void carve_attn(Carve& c, int32_t rows, int32_t K, int32_t W, int32_t dv, AttnWs* aw) {
@@ -204,6 +192,11 @@ csa2_status csa2_profile_end(int32_t* counts, double* total_ms) {
   return CSA2_OK;
 }
 size_t csa2_fp4_cache_size(void) { return sizeof(csa2_fp4_cache); }
+
+size_t csa2_workspace_control_bytes(int32_t rows) {
+  if (rows < 1) return 0;
+  return (size_t)std::min(rows, kRowChunk) * kCtlWordsPerRow * sizeof(uint32_t);
+}
 
 int64_t csa2_fp4_bytes_per_token(int32_t dim) {
   if (dim <= 0 || dim % 16) return -1;
@@ -273,10 +266,11 @@ csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
 // ------------------------------------------------------------ top-k
 size_t csa2_topk_workspace_bytes(int32_t rows, int64_t n, int32_t k) {
   if (rows < 1 || n < 1 || k < 1) return 0;
+  const int32_t rc = std::min(rows, kRowChunk);
   Carve c(nullptr);
   TopkWs tw;
-  carve_ctl(c, rows, &tw, nullptr);
-  carve_topk(c, rows, n, k, &tw);
+  carve_ctl(c, rc, &tw, nullptr);
+  carve_topk(c, rc, n, k, &tw);
   return c.off;
 }
 
@@ -285,31 +279,41 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
                       void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   CSA2_REQUIRE(rows >= 1 && rows <= 65535, CSA2_ERR_SHAPE, "rows must be in [1,65535]");
-  CSA2_REQUIRE(n >= 1 && n <= 0x7FFFFFFF, CSA2_ERR_SHAPE, "n must be in [1, 2^31-1]");
+  CSA2_REQUIRE(n >= 1 && n <= kMaxTopkN, CSA2_ERR_SHAPE, "n must be in [1, 2^25]");
   CSA2_REQUIRE(k >= 1 && k <= CSA2_MAX_K, CSA2_ERR_SHAPE, "k must be in [1,%d]", CSA2_MAX_K);
   CSA2_REQUIRE(scores && n_valid && idx_out, CSA2_ERR_NULL, "scores, n_valid and idx_out are required");
   const size_t need = csa2_topk_workspace_bytes(rows, n, k);
   CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
                need, ws_bytes);
+  const int32_t rc = std::min(rows, kRowChunk);
   Carve c(ws);
   TopkWs tw;
-  carve_ctl(c, rows, &tw, nullptr);
-  carve_topk(c, rows, n, k, &tw);
+  carve_ctl(c, rc, &tw, nullptr);
+  carve_topk(c, rc, n, k, &tw);
   const hipStream_t st = as_stream(stream);
-  CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(scores, rows, n, n_valid, 0, n, tw.hist, tw.hist_stride, st),
-           "top-k histogram launch");
-  CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(scores, rows, n, n_valid, 0, n, slot_pos, k, idx_out, count_out, tw, st),
-           "top-k select launch");
+  for (int32_t r0 = 0; r0 < rows; r0 += rc) {
+    const int32_t nr = std::min(rc, rows - r0);
+    const float* sc = scores + (size_t)r0 * n;
+    const int32_t* nv = n_valid + r0;
+    const int32_t* sp = slot_pos ? slot_pos + (size_t)r0 * n : nullptr;
+    CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(sc, nr, n, nv, 0, n, tw.hist, tw.hist_stride, st),
+                "top-k histogram launch");
+    CSA2_LAUNCH(2, PROF_STREAM,
+                launch_topk_select(sc, nr, n, nv, 0, n, sp, k, idx_out + (size_t)r0 * k,
+                                   count_out ? count_out + r0 : nullptr, tw, st),
+                "top-k select launch");
+  }
   return CSA2_OK;
 }
 
 // ------------------------------------------------------------ attention
 size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int32_t dv) {
   if (rows < 1 || K < 0 || W < 0 || dv < 1) return 0;
+  const int32_t rc = std::min(rows, kRowChunk);
   Carve c(nullptr);
   AttnWs aw;
-  carve_ctl(c, rows, nullptr, &aw);
-  carve_attn(c, rows, K, W, dv, &aw);
+  carve_ctl(c, rc, nullptr, &aw);
+  carve_attn(c, rc, K, W, dv, &aw);
   return c.off;
 }
 
@@ -348,14 +352,22 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
   const size_t need = csa2_sparse_attn_workspace_bytes(rows, K, Weff, dv);
   CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
                need, ws_bytes);
+  const int32_t rc = std::min(rows, kRowChunk);
   Carve c(ws);
   AttnWs aw;
-  carve_ctl(c, rows, nullptr, &aw);
-  carve_attn(c, rows, K, Weff, dv, &aw);
-  CSA2_LAUNCH(3, PROF_STREAM, launch_sparse_attn(q, rows, T, kv->dim, dv, kv->codes, kv->scales, kv->cap, idx, K,
-                              swa, swa_scale, swa_pos0, S, Weff, q_pos, sm_scale, out, lse, aw,
-                              as_stream(stream)),
-           "sparse attention launch");
+  carve_ctl(c, rc, nullptr, &aw);
+  carve_attn(c, rc, K, Weff, dv, &aw);
+  const int32_t D = kv->dim;
+  for (int32_t r0 = 0; r0 < rows; r0 += rc) {
+    const int32_t nr = std::min(rc, rows - r0);
+    CSA2_LAUNCH(3, PROF_STREAM,
+                launch_sparse_attn(q + (size_t)r0 * H * D, nr, T, D, dv, kv->codes, kv->scales,
+                                   kv->cap, idx ? idx + (size_t)r0 * K : nullptr, K, swa,
+                                   swa_scale, swa_pos0, S, Weff, q_pos + r0, sm_scale,
+                                   out + (size_t)r0 * H * dv, lse ? lse + (size_t)r0 * H : nullptr,
+                                   aw, as_stream(stream), r0),
+                "sparse attention launch");
+  }
   return CSA2_OK;
 }
 
@@ -415,7 +427,7 @@ csa2_status check_step(csa2_mode mode, const csa2_layer_args* a) {
   CSA2_REQUIRE(a->H_I >= 1 && a->H_I <= CSA2_MAX_INDEX_HEADS, CSA2_ERR_SHAPE, "H_I must be in [1,16]");
   CSA2_REQUIRE(a->q_idx && a->w_idx && a->idx_out, CSA2_ERR_NULL,
                "q_idx, w_idx and idx_out are required");
-  CSA2_REQUIRE(a->icache.cap <= 0x7FFFFFFF, CSA2_ERR_SHAPE, "index cache capacity too large");
+  CSA2_REQUIRE(a->icache.cap <= kMaxTopkN, CSA2_ERR_SHAPE, "index cache capacity above 2^25");
   if (mode == CSA2_MODE_FULL) {
     CSA2_REQUIRE(a->new_kv && a->new_ikey, CSA2_ERR_NULL, "FULL needs new_kv and new_ikey");
     CSA2_REQUIRE(a->new_dtype == CSA2_F32 || a->new_dtype == CSA2_BF16, CSA2_ERR_DTYPE,

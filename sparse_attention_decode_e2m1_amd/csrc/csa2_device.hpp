@@ -18,6 +18,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kHistBins = 4096;       // top 12 bits of the ordered score key
 constexpr int kHistShift = 20;
+// Copies of each row's histogram; block b adds into copy b % kHistCopies.
+// Device-scope atomics on one address serialise (about 11 ns each on
+// MI355X), so the merge of many blocks is spread over the copies.
+constexpr int kHistCopies = 8;
 
 // --------------------------------------------------------------- FP8 / FP4
 // E4M3 byte -> f32 (gfx950 converts the OCP "FN" encoding).  `sel` picks the

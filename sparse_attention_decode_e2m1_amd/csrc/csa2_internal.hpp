@@ -8,31 +8,32 @@
 
 namespace csa2 {
 
-constexpr int32_t kScoreChunk = 4096;  // positions per scoring block
-constexpr int32_t kTopkChunk = 8192;   // scores per select block
-constexpr int32_t kAttnTilesPerSplit = 8;
+constexpr int32_t kScoreChunk = 2048;  // positions per scoring block
+constexpr int kScoreGroup = 4;         // consecutive 16-position tiles per wave load
+constexpr int32_t kTopkChunk = 8192;   // scores per select block (32 per thread)
+constexpr int32_t kAttnTilesPerSplit = 4;  // one round of the 4 waves per split
+constexpr int32_t kMaxSplits = 1024;
+constexpr int64_t kMaxTopkN = int64_t(1) << 25;  // longest score row Top-K accepts
 
-// Per-row control words of the Top-K pass, zero between calls.
-struct TopkCtl {
-  uint32_t cand;  // candidates appended
-  uint32_t done;  // select blocks finished
-};
-
-// Every call keeps the control words of query row r in one fixed-size block
-// at the start of the workspace, so any workspace left zero by a previous
-// call (of any kind or shape) is ready for the next.
-constexpr int64_t kCtlWordsPerRow = 4096 + 8;  // histogram, TopkCtl, attention counter, pad
-inline uint32_t* row_hist(void* ws) { return reinterpret_cast<uint32_t*>(ws); }
+// Every call keeps the control words of query row r -- the Top-K histogram
+// copies -- in one fixed-size block at the start of the workspace.  They are
+// zero between calls, so any workspace left by a previous call (of any kind
+// or shape) is ready for the next.
+constexpr int64_t kHistWords = int64_t(8) * 4096;  // kHistCopies x kHistBins
+constexpr int64_t kCtlWordsPerRow = kHistWords;
 
 struct TopkWs {
-  uint32_t* hist;       // row r at hist + r * hist_stride (4096 bins)
-  int64_t hist_stride;  // in words
-  TopkCtl* ctl;         // row r at ctl + r * ctl_stride
-  int64_t ctl_stride;   // in TopkCtl units
-  uint64_t* cand;       // [rows][cand_cap]
-  int32_t cand_cap;
-  uint32_t* bitmap;   // [rows][bm_words]
-  int64_t bm_words;
+  uint32_t* hist;        // row r at hist + r * hist_stride (kHistCopies x 4096 bins)
+  int64_t hist_stride;   // in words
+  // Per select block b of row r, regions of kTopkChunk entries at offset
+  // r * stride + b * kTopkChunk: the positions kept outright and the
+  // candidates' 64-bit rank values, each in position order.
+  uint32_t* above;
+  int64_t above_stride;
+  uint64_t* cand;
+  int64_t cand_stride;
+  uint32_t* counts;      // row r at counts + r * counts_stride: (kept, candidates) per block
+  int64_t counts_stride;
 };
 
 struct AttnWs {
@@ -46,8 +47,9 @@ struct AttnSplit {
 };
 inline AttnSplit attn_split(int32_t K, int32_t W) {
   AttnSplit s;
-  s.tps = kAttnTilesPerSplit;
   const int32_t tg = (K + 15) / 16, tw = (W + 15) / 16;
+  s.tps = kAttnTilesPerSplit;
+  while ((tg + s.tps - 1) / s.tps + (tw + s.tps - 1) / s.tps > kMaxSplits) s.tps *= 2;
   s.nsg = (tg + s.tps - 1) / s.tps;
   if (s.nsg < 1) s.nsg = 1;
   s.nsw = (tw + s.tps - 1) / s.tps;
@@ -71,7 +73,6 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st);
-size_t topk_lds_bytes(int32_t k);
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_t D, int32_t dv,
                               const uint8_t* codes, const uint8_t* scales, int64_t cap,
                               const int32_t* idx, int32_t K, const uint8_t* swa,

@@ -101,70 +101,80 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int32_t* prow = pool ? pool + (int64_t)r * P : nullptr;
   float* srow = scores + (int64_t)r * n_out;
 
+  // Each wave takes groups of G consecutive tiles (G KiB of contiguous codes
+  // in flat mode); the four waves of a round cover 4G consecutive tiles.
+  // The next group's loads are issued before the current group is computed,
+  // so about 2G tiles per wave are in flight.
+  constexpr int G = kScoreGroup;
   const int ntiles = (int)((end - start + 15) >> 4);
+  const int nrounds = (ntiles + 4 * G - 1) / (4 * G);
   auto row_of = [&](int tile) -> int64_t {
     int64_t s = start + (int64_t)tile * 16 + i;
     if (s >= end) s = end - 1;  // clamp: keep the load in bounds, masked later
     return prow ? (int64_t)prow[s] : s;
   };
+  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of the row's scales;
+  // they are fetched as the aligned 32-bit word holding them, so nothing has
+  // to wait for the loads until the group is computed.
+  auto load_group = [&](int rnd, u32x4 (&cw)[G][NCH], uint32_t (&sw)[G][NCH]) {
+    int64_t rows[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) rows[j] = row_of((rnd * 4 + wave) * G + j);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        cw[j][c2] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(cbase + rows[j] * ROWB + 64 * c2 + 16 * g));
+        sw[j][c2] =
+            *reinterpret_cast<const uint32_t*>(sbase + rows[j] * ROWS + 8 * c2 + 4 * (g >> 1));
+      }
+    }
+  };
+  const int sshift = 16 * (g & 1);
 
-  u32x4 cw[NCH];
-  uint32_t sw[NCH];
-  int tile = wave;
-  if (tile < ntiles) {
-    const int64_t row = row_of(tile);
+  u32x4 cw[G][NCH], ncw[G][NCH];
+  uint32_t sw[G][NCH], nsw[G][NCH];
+  if (nrounds > 0) load_group(0, cw, sw);
+  for (int rnd = 0; rnd < nrounds; ++rnd) {
+    if (rnd + 1 < nrounds) load_group(rnd + 1, ncw, nsw);
 #pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) {
-      cw[c2] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(cbase + row * ROWB + 64 * c2 + 16 * g));
-      sw[c2] = *reinterpret_cast<const uint16_t*>(sbase + row * ROWS + 8 * c2 + 2 * g);
-    }
-  }
-  for (; tile < ntiles; tile += 4) {
-    // prefetch the next tile of this wave
-    u32x4 ncw[NCH];
-    uint32_t nsw[NCH];
-    const int nt = tile + 4;
-    if (nt < ntiles) {
-      const int64_t row = row_of(nt);
+    for (int j = 0; j < G; ++j) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) {
-        ncw[c2] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(cbase + row * ROWB + 64 * c2 + 16 * g));
-        nsw[c2] = *reinterpret_cast<const uint16_t*>(sbase + row * ROWS + 8 * c2 + 2 * g);
+        const uint32_t s2b = sw[j][c2] >> sshift;
+        const f16x2 s_lo = scale_pair(s2b & 0xFFu);
+        const f16x2 s_hi = scale_pair((s2b >> 8) & 0xFFu);
+        acc = mfma16x16x32(qa[c2][0], fp4x8_to_f16(cw[j][c2].x, s_lo), acc);
+        acc = mfma16x16x32(qa[c2][1], fp4x8_to_f16(cw[j][c2].y, s_lo), acc);
+        acc = mfma16x16x32(qa[c2][2], fp4x8_to_f16(cw[j][c2].z, s_hi), acc);
+        acc = mfma16x16x32(qa[c2][3], fp4x8_to_f16(cw[j][c2].w, s_hi), acc);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part += wr[rr] * fmaxf(ldexpf(acc[rr], -er[rr]), 0.0f);
+      part += shfl_xor(part, 16);
+      part += shfl_xor(part, 32);
+      const int64_t s = start + (int64_t)((rnd * 4 + wave) * G + j) * 16 + i;
+      if (g == 0 && s < end) {
+        srow[s] = part;
+        if (hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
       }
     }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (rnd + 1 < nrounds) {
 #pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) {
-      const f16x2 s_lo = scale_pair(sw[c2] & 0xFFu);
-      const f16x2 s_hi = scale_pair(sw[c2] >> 8);
-      acc = mfma16x16x32(qa[c2][0], fp4x8_to_f16(cw[c2].x, s_lo), acc);
-      acc = mfma16x16x32(qa[c2][1], fp4x8_to_f16(cw[c2].y, s_lo), acc);
-      acc = mfma16x16x32(qa[c2][2], fp4x8_to_f16(cw[c2].z, s_hi), acc);
-      acc = mfma16x16x32(qa[c2][3], fp4x8_to_f16(cw[c2].w, s_hi), acc);
-    }
-    float part = 0.0f;
+      for (int j = 0; j < G; ++j)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) part += wr[rr] * fmaxf(ldexpf(acc[rr], -er[rr]), 0.0f);
-    part += shfl_xor(part, 16);
-    part += shfl_xor(part, 32);
-    const int64_t s = start + (int64_t)tile * 16 + i;
-    if (g == 0 && s < end) {
-      srow[s] = part;
-      if (hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
-    }
-    if (nt < ntiles) {
-#pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        cw[c2] = ncw[c2];
-        sw[c2] = nsw[c2];
-      }
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          cw[j][c2] = ncw[j][c2];
+          sw[j][c2] = nsw[j][c2];
+        }
     }
   }
   if (hist) {
     __syncthreads();
-    uint32_t* gh = hist + (int64_t)r * hist_stride;
+    uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
     for (int k = tid; k < kHistBins; k += 256) {
       const uint32_t c = lhist[k];
       if (c) atomicAdd(gh + k, c);

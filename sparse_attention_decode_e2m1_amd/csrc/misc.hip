@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void gather_scores_kernel(
     atomicAdd(&lhist[score_key(v) >> kHistShift], 1u);
   }
   __syncthreads();
-  uint32_t* gh = hist + (int64_t)r * hist_stride;
+  uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
   for (int k = threadIdx.x; k < kHistBins; k += 256)
     if (lhist[k]) atomicAdd(gh + k, lhist[k]);
 }

@@ -23,7 +23,7 @@ def setup_module(module):
 
 def ctl_words_zero(ws, rows):
     """The per-row control blocks at the start of a workspace are zero."""
-    words = ws[: rows * (4096 + 8) * 4].view(torch.int32)
+    words = ws[: api.lib().csa2_workspace_control_bytes(rows)].view(torch.int32)
     return int(torch.count_nonzero(words)) == 0
 
 

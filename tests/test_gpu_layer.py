@@ -135,5 +135,5 @@ def test_step_is_deterministic_and_leaves_workspace_clean():
     torch.cuda.synchronize()
     for L, (i0, o0, l0) in zip(dw.layers, first):
         assert torch.equal(L.idx_out, i0) and torch.equal(L.out, o0) and torch.equal(L.lse, l0)
-    ctl = dw.ws[: min(dw.rows, 256) * (4096 + 8) * 4].view(torch.int32)
+    ctl = dw.ws[: api.lib().csa2_workspace_control_bytes(dw.rows)].view(torch.int32)
     assert int(torch.count_nonzero(ctl)) == 0
