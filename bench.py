@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-kernel-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 5 times (the "
+                         "reference kernel that calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the path shards by sequence or by "
@@ -92,8 +95,19 @@ def main():
         sys.exit(2)
 
     import torch
-    from sparse_attention_decode_e2m1_amd import api, harness
+    from sparse_attention_decode_e2m1_amd import api, harness, profiling
     from sparse_attention_decode_e2m1_amd import inputs as I
+
+    if args.copy_kernel_bytes:
+        n = args.copy_kernel_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)  # one elementwise pass: reads n*4, writes n*4 bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "passes": 5}), flush=True)
+        return
 
     w = I.WORKLOADS[args.workload]
     api.lib()  # fails loudly if the HIP library is missing
@@ -141,9 +155,13 @@ def main():
             # their summed duration
             scan_bytes = kvb["index_scan_per_step"] * args.steps
             achieved = scan_bytes / (ms_sc * 1e-3) / 1e9
+            traffic = profiling.read_traffic(
+                os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                             f"index_score_kernel.{w.name}.traffic.txt"), "index_score_kernel")
             roofline = {"bound": "hbm", "kernel": "index_score_kernel", "achieved": round(achieved, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": None if traffic is None else round(traffic),
                         "avg_launch_us": round(ms_sc * 1e3 / n_sc, 2), "launches": n_sc,
                         "bytes_per_launch": scan_bytes // n_sc}
         prof = {k: {"launches": c, "avg_us": round(t * 1e3 / c, 2) if c else 0.0}
