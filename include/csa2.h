@@ -83,6 +83,7 @@ typedef struct {
 
 /* Limits of the kernels in this build. */
 #define CSA2_MAX_K 16384        /* Top-K and pool size */
+#define CSA2_MAX_W 16384        /* sliding-window length */
 #define CSA2_HEADS 16           /* query heads of the attention kernel */
 #define CSA2_MAX_INDEX_HEADS 16 /* indexer heads */
 
@@ -174,7 +175,7 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
  *   kv       : FP4 main cache (dim a multiple of 64, <= 1024).
  *   idx      : device int32 [B*T][K], entries < kv->cap or negative.
  *   swa      : device uint8 [B][S][D] E4M3;  swa_scale : device f32 [B];
- *   swa_pos0 : device int32 [B];  W >= 0 window length; S >= 0 rows.
+ *   swa_pos0 : device int32 [B];  0 <= W <= CSA2_MAX_W window length; S >= 0 rows.
  *   q_pos    : device int32 [B*T].
  *   out      : device f32 [B*T][H][dv] (dv a multiple of 64, <= D);
  *   lse      : device f32 [B*T][H] or NULL.
@@ -183,7 +184,7 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
  * bf16 query scaled per head by a power of two; probabilities are rounded
  * to fp16 for the value product, accumulated in fp32.
  * Errors: NULL pointers, H != CSA2_HEADS, bad D/dv, K < 0 (K == 0 allowed),
- * W or S < 0, workspace too small. */
+ * W < 0 or W > CSA2_MAX_W, S < 0, workspace too small. */
 size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int32_t dv);
 csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
                              const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,

@@ -110,14 +110,20 @@ struct Carve {
   }
 };
 
-// Control block of row r: the kHistWords histogram copies.
+// Control block of row r: the kHistWords histogram copies, then the
+// attention merge counters.
 void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
   uint32_t* ctl = c.take<uint32_t>((size_t)rows * kCtlWordsPerRow);
   if (tw) {
     tw->hist = ctl;
     tw->hist_stride = kCtlWordsPerRow;
+    tw->ctr = ctl ? ctl + kHistWords + 2 : nullptr;
+    tw->ctr_stride = kCtlWordsPerRow;
   }
-  (void)aw;
+  if (aw) {
+    aw->cnt = ctl ? ctl + kHistWords : nullptr;
+    aw->cnt_stride = kCtlWordsPerRow;
+  }
 }
 
 // Kept-position and candidate regions: one kTopkChunk region of each per
@@ -330,7 +336,8 @@ static csa2_status check_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H
   CSA2_REQUIRE(attn_shape_ok(kv->dim, dv), CSA2_ERR_UNSUPPORTED,
                "(D, dv) must be (576, 512) or (128, 128) (got (%d, %d))", kv->dim, dv);
   CSA2_REQUIRE(K >= 0 && K <= CSA2_MAX_K, CSA2_ERR_SHAPE, "K must be in [0,%d]", CSA2_MAX_K);
-  CSA2_REQUIRE(W >= 0 && S >= 0, CSA2_ERR_SHAPE, "W and S must be >= 0");
+  CSA2_REQUIRE(W >= 0 && W <= CSA2_MAX_W && S >= 0, CSA2_ERR_SHAPE,
+               "W must be in [0,%d] and S >= 0", CSA2_MAX_W);
   CSA2_REQUIRE(q && q_pos && out, CSA2_ERR_NULL, "q, q_pos and out are required");
   CSA2_REQUIRE(K == 0 || idx, CSA2_ERR_NULL, "idx is required when K > 0");
   CSA2_REQUIRE(W == 0 || S == 0 || (swa && swa_scale && swa_pos0), CSA2_ERR_NULL,

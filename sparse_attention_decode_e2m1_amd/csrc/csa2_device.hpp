@@ -115,6 +115,34 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
+// DPP move inside each row of 16 lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// Maximum over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_move<kDppXor1>(v));
+  v = fmaxf(v, dpp_move<kDppXor2>(v));
+  v = fmaxf(v, dpp_move<kDppRor4>(v));
+  v = fmaxf(v, dpp_move<kDppRor8>(v));
+  return v;
+}
+// Sum over the 16 lanes of each row (every lane holds the sum; lanes of
+// different quads may differ in the order of the additions).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_move<kDppXor1>(v);
+  v += dpp_move<kDppXor2>(v);
+  v += dpp_move<kDppRor4>(v);
+  v += dpp_move<kDppRor8>(v);
+  return v;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -10,17 +10,18 @@ namespace csa2 {
 
 constexpr int32_t kScoreChunk = 2048;  // positions per scoring block
 constexpr int kScoreGroup = 4;         // consecutive 16-position tiles per wave load
-constexpr int32_t kTopkChunk = 8192;   // scores per select block (32 per thread)
-constexpr int32_t kAttnTilesPerSplit = 4;  // one round of the 4 waves per split
-constexpr int32_t kMaxSplits = 1024;
+constexpr int32_t kTopkChunk = 4096;   // scores per select block (4 per thread)
+constexpr int32_t kAttnSplit = 64;      // entries per attention split (one tile per wave)
+constexpr int32_t kMaxSplits = 512;     // (CSA2_MAX_K + CSA2_MAX_W) / kAttnSplit
 constexpr int64_t kMaxTopkN = int64_t(1) << 25;  // longest score row Top-K accepts
 
 // Every call keeps the control words of query row r -- the Top-K histogram
-// copies -- in one fixed-size block at the start of the workspace.  They are
+// copies, then the attention merge counters -- in one fixed-size block at the start of the workspace.  They are
 // zero between calls, so any workspace left by a previous call (of any kind
 // or shape) is ready for the next.
 constexpr int64_t kHistWords = int64_t(8) * 4096;  // kHistCopies x kHistBins
-constexpr int64_t kCtlWordsPerRow = kHistWords;
+// + attention arrival / leave counters (words 0, 1) and the Top-K arrival counter (word 2)
+constexpr int64_t kCtlWordsPerRow = kHistWords + 64;
 
 struct TopkWs {
   uint32_t* hist;        // row r at hist + r * hist_stride (kHistCopies x 4096 bins)
@@ -34,25 +35,24 @@ struct TopkWs {
   int64_t cand_stride;
   uint32_t* counts;      // row r at counts + r * counts_stride: (kept, candidates) per block
   int64_t counts_stride;
+  uint32_t* ctr;         // row r at ctr + r * ctr_stride: select blocks arrived (zero between calls)
+  int64_t ctr_stride;
 };
 
 struct AttnWs {
   float* part;        // [rows][nsplit][16*dv + 32]
-  uint32_t* cnt;      // row r at cnt + r * cnt_stride
+  uint32_t* cnt;      // row r at cnt + r * cnt_stride: arrivals, departures
   int64_t cnt_stride;
 };
 
 struct AttnSplit {
-  int32_t tps, nsg, nsw, nsplit;
+  int32_t nsg, nsw, nsplit;  // splits of global entries, of window entries, total
 };
 inline AttnSplit attn_split(int32_t K, int32_t W) {
   AttnSplit s;
-  const int32_t tg = (K + 15) / 16, tw = (W + 15) / 16;
-  s.tps = kAttnTilesPerSplit;
-  while ((tg + s.tps - 1) / s.tps + (tw + s.tps - 1) / s.tps > kMaxSplits) s.tps *= 2;
-  s.nsg = (tg + s.tps - 1) / s.tps;
-  if (s.nsg < 1) s.nsg = 1;
-  s.nsw = (tw + s.tps - 1) / s.tps;
+  s.nsg = (K + kAttnSplit - 1) / kAttnSplit;
+  if (s.nsg < 1) s.nsg = 1;  // one split still writes the empty result
+  s.nsw = (W + kAttnSplit - 1) / kAttnSplit;
   s.nsplit = s.nsg + s.nsw;
   return s;
 }

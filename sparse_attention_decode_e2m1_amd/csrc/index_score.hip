@@ -9,23 +9,30 @@
 // visible context, later ones only a candidate pool).
 //
 // The scan streams 72 bytes per position (64 code bytes + 8 scale bytes for
-// 128 channels) and is HBM-bound.  One wave scores 16 positions per step with
-// 4 fp16 MFMA 16x16x32 (rows = indexer heads, columns = positions, k =
-// channels): lane (i, g) loads the 16 code bytes [16g, 16g+16) of position i
-// -- the 64 lanes together read 1 KiB of contiguous codes -- plus the two
-// scale bytes of its 32 channels, and dequantizes them exactly to fp16.
-// Channel 32g + 8kk + j of the row feeds k-slot 8g + j of MFMA kk, and the
-// query fragments use the same mapping.
+// 128 channels) and is HBM-bound.  MFMA 16x16x32 (fp16 in, fp32 out) takes
+// rows = indexer heads, columns = 16 positions (a tile), k = channels.  With
+// at most 16/TPA heads, TPA tiles share one accumulator: tile slot j's heads
+// sit in rows [j*16/TPA, (j+1)*16/TPA) of the A operand (zero elsewhere), so
+// after the slots' MFMAs lane (i, g) holds rows 4g..4g+3 of position i and,
+// with four heads, every lane finishes one score by itself.
+//
+// Lane (i, g) of a tile loads the 16 code bytes [16g, 16g+16) of position i
+// -- the 64 lanes together read 1 KiB of contiguous codes -- plus the aligned
+// scale word holding its two scale bytes, and dequantizes them exactly to
+// fp16.  Channel 32g + 8kk + j of a 128-channel chunk feeds k-slot 8g + j of
+// MFMA kk, and the query fragments use the same mapping.  The query is
+// scaled per head by a power of two into fp16 range; that factor is folded
+// into the head weight (exact unless that weight underflows).
 //
 // The block also builds a histogram of the top 12 bits of each score's
-// ordered key and adds it to a per-row global histogram, which the Top-K
-// select pass then uses to find the bin holding the K-th score.
+// ordered key and adds it to one of the row's global histogram copies, which
+// the Top-K select pass then uses to find the bin holding the K-th score.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-template <int NCH>  // index-key channels / 128
+template <int NCH, int TPA, int GT>  // 128-channel chunks, tiles per accumulator, tiles per group
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
@@ -35,6 +42,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   constexpr int DI = 128 * NCH;
   constexpr int ROWB = DI / 2;    // code bytes per row
   constexpr int ROWS = DI / 16;   // scale bytes per row
+  constexpr int HG = 16 / TPA;    // MFMA rows per tile slot
+  constexpr int GPS = HG / 4;     // lane groups g covering one slot
+  constexpr int NACC = GT / TPA;  // accumulators per group
+  static_assert(GT % TPA == 0 && HG >= 4, "tile packing");
   __shared__ uint32_t lhist[kHistBins];
 
   const int r = blockIdx.y;
@@ -52,13 +63,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     for (int k = tid; k < kHistBins; k += 256) lhist[k] = 0u;
   }
 
-  // ---- query fragments: head i (zero rows for i >= HI), scaled into fp16.
-  f16x8 qa[NCH][4];
+  // ---- query fragments: MFMA row i holds head i % HG of tile slot i / HG
+  const int hrow = i % HG, srow_slot = i / HG;
+  f16x8 qv[TPA][NCH][4];
   int qexp;
   {
     float vals[NCH][4][8];
     float amax = 0.0f;
-    const uint16_t* qr = q_idx + ((int64_t)r * HI + (i < HI ? i : 0)) * DI;
+    const bool live = hrow < HI;
+    const uint16_t* qr = q_idx + ((int64_t)r * HI + (live ? hrow : 0)) * DI;
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2)
 #pragma unroll
@@ -79,21 +92,25 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
+        f16x8 a;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          qa[c2][kk][j] = (i < HI) ? (_Float16)ldexpf(vals[c2][kk][j], qexp) : (_Float16)0.0f;
+        for (int j = 0; j < 8; ++j) a[j] = live ? (_Float16)ldexpf(vals[c2][kk][j], qexp) : (_Float16)0.0f;
+#pragma unroll
+        for (int sl = 0; sl < TPA; ++sl) qv[sl][c2][kk] = (sl == srow_slot) ? a : f16x8{};
+      }
   }
-  // Accumulator rows held by this lane: heads 4g + rr.  Fetch their weights
-  // and the exponent that undoes the query scaling.
-  float wr[4];
-  int er[4];
+  // Accumulator rows of lane (i, g): 4g + rr = slot g / GPS, head 4(g % GPS) + rr.
+  // Head weights carry the factor that undoes the query scaling.
+  float wq[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int h = 4 * g + rr;
-    er[rr] = __shfl(qexp, h & 15, kWave);
-    wr[rr] = (h < HI) ? w[(int64_t)r * HI + h] : 0.0f;
+    const int h = 4 * (g % GPS) + rr;
+    const int e = __shfl(qexp, h, kWave);  // lane h holds head h of slot 0
+    wq[rr] = (h < HI) ? ldexpf(w[(int64_t)r * HI + h], -e) : 0.0f;
   }
+  const int my_slot = g / GPS;
+  const bool owner = (g % GPS) == 0;
   if (hist) __syncthreads();
 
   const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
@@ -101,74 +118,77 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int32_t* prow = pool ? pool + (int64_t)r * P : nullptr;
   float* srow = scores + (int64_t)r * n_out;
 
-  // Each wave takes groups of G consecutive tiles (G KiB of contiguous codes
-  // in flat mode); the four waves of a round cover 4G consecutive tiles.
-  // The next group's loads are issued before the current group is computed,
-  // so about 2G tiles per wave are in flight.
-  constexpr int G = kScoreGroup;
+  // Each wave takes groups of GT consecutive tiles (GT KiB of contiguous
+  // codes for 128 channels in flat mode); the four waves of a round cover
+  // 4*GT consecutive tiles.  The next group's loads are issued before the
+  // current group is computed.
   const int ntiles = (int)((end - start + 15) >> 4);
-  const int nrounds = (ntiles + 4 * G - 1) / (4 * G);
+  const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
   auto row_of = [&](int tile) -> int64_t {
     int64_t s = start + (int64_t)tile * 16 + i;
     if (s >= end) s = end - 1;  // clamp: keep the load in bounds, masked later
     return prow ? (int64_t)prow[s] : s;
   };
-  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of the row's scales;
-  // they are fetched as the aligned 32-bit word holding them, so nothing has
-  // to wait for the loads until the group is computed.
-  auto load_group = [&](int rnd, u32x4 (&cw)[G][NCH], uint32_t (&sw)[G][NCH]) {
-    int64_t rows[G];
+  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
+  // scales; they are fetched as the aligned 32-bit word holding them, so
+  // nothing has to wait for the loads until the group is computed.
+  auto load_group = [&](int rnd, u32x4 (&cw)[GT][NCH], uint32_t (&sw)[GT][NCH]) {
+    int64_t rows[GT];
 #pragma unroll
-    for (int j = 0; j < G; ++j) rows[j] = row_of((rnd * 4 + wave) * G + j);
+    for (int t = 0; t < GT; ++t) rows[t] = row_of((rnd * 4 + wave) * GT + t);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int t = 0; t < GT; ++t) {
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) {
-        cw[j][c2] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(cbase + rows[j] * ROWB + 64 * c2 + 16 * g));
-        sw[j][c2] =
-            *reinterpret_cast<const uint32_t*>(sbase + rows[j] * ROWS + 8 * c2 + 4 * (g >> 1));
+        cw[t][c2] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(cbase + rows[t] * ROWB + 64 * c2 + 16 * g));
+        sw[t][c2] =
+            *reinterpret_cast<const uint32_t*>(sbase + rows[t] * ROWS + 8 * c2 + 4 * (g >> 1));
       }
     }
   };
   const int sshift = 16 * (g & 1);
 
-  u32x4 cw[G][NCH], ncw[G][NCH];
-  uint32_t sw[G][NCH], nsw[G][NCH];
+  u32x4 cw[GT][NCH], ncw[GT][NCH];
+  uint32_t sw[GT][NCH], nsw[GT][NCH];
   if (nrounds > 0) load_group(0, cw, sw);
   for (int rnd = 0; rnd < nrounds; ++rnd) {
     if (rnd + 1 < nrounds) load_group(rnd + 1, ncw, nsw);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
+    for (int a = 0; a < NACC; ++a) {
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        const uint32_t s2b = sw[j][c2] >> sshift;
-        const f16x2 s_lo = scale_pair(s2b & 0xFFu);
-        const f16x2 s_hi = scale_pair((s2b >> 8) & 0xFFu);
-        acc = mfma16x16x32(qa[c2][0], fp4x8_to_f16(cw[j][c2].x, s_lo), acc);
-        acc = mfma16x16x32(qa[c2][1], fp4x8_to_f16(cw[j][c2].y, s_lo), acc);
-        acc = mfma16x16x32(qa[c2][2], fp4x8_to_f16(cw[j][c2].z, s_hi), acc);
-        acc = mfma16x16x32(qa[c2][3], fp4x8_to_f16(cw[j][c2].w, s_hi), acc);
+      for (int sl = 0; sl < TPA; ++sl) {
+        const int t = a * TPA + sl;
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          const uint32_t s2b = sw[t][c2] >> sshift;
+          const f16x2 s_lo = scale_pair(s2b & 0xFFu);
+          const f16x2 s_hi = scale_pair((s2b >> 8) & 0xFFu);
+          acc = mfma16x16x32(qv[sl][c2][0], fp4x8_to_f16(cw[t][c2].x, s_lo), acc);
+          acc = mfma16x16x32(qv[sl][c2][1], fp4x8_to_f16(cw[t][c2].y, s_lo), acc);
+          acc = mfma16x16x32(qv[sl][c2][2], fp4x8_to_f16(cw[t][c2].z, s_hi), acc);
+          acc = mfma16x16x32(qv[sl][c2][3], fp4x8_to_f16(cw[t][c2].w, s_hi), acc);
+        }
       }
       float part = 0.0f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part += wr[rr] * fmaxf(ldexpf(acc[rr], -er[rr]), 0.0f);
-      part += shfl_xor(part, 16);
-      part += shfl_xor(part, 32);
-      const int64_t s = start + (int64_t)((rnd * 4 + wave) * G + j) * 16 + i;
-      if (g == 0 && s < end) {
+      for (int rr = 0; rr < 4; ++rr) part += wq[rr] * fmaxf(acc[rr], 0.0f);
+      if constexpr (GPS >= 2) part += shfl_xor(part, 16);
+      if constexpr (GPS >= 4) part += shfl_xor(part, 32);
+      const int64_t s = start + (int64_t)((rnd * 4 + wave) * GT + a * TPA + my_slot) * 16 + i;
+      if (owner && s < end) {
         srow[s] = part;
         if (hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
       }
     }
     if (rnd + 1 < nrounds) {
 #pragma unroll
-      for (int j = 0; j < G; ++j)
+      for (int t = 0; t < GT; ++t)
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
-          cw[j][c2] = ncw[j][c2];
-          sw[j][c2] = nsw[j][c2];
+          cw[t][c2] = ncw[t][c2];
+          sw[t][c2] = nsw[t][c2];
         }
     }
   }
@@ -192,26 +212,30 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   const int64_t nchunks = (n_max + chunk - 1) / chunk;
   if (nchunks == 0 || rows == 0) return hipSuccess;
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
+#define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \
+  hipLaunchKernelGGL((index_score_kernel<NCH, TPA, GT>), grid, block, 0, st, codes, scales, cap, \
+                     q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, hist,             \
+                     hist_stride, chunk, row0)
   switch (DI / 128) {
     case 1:
-      hipLaunchKernelGGL(index_score_kernel<1>, grid, block, 0, st, codes, scales, cap, q_idx, w,
-                         HI, T, n_valid, pool, P, nv_add, scores, n_out, hist, hist_stride, chunk, row0);
+      if (HI <= 4) CSA2_IS_LAUNCH(1, 4, 8);
+      else if (HI <= 8) CSA2_IS_LAUNCH(1, 2, 8);
+      else CSA2_IS_LAUNCH(1, 1, 4);
       break;
     case 2:
-      hipLaunchKernelGGL(index_score_kernel<2>, grid, block, 0, st, codes, scales, cap, q_idx, w,
-                         HI, T, n_valid, pool, P, nv_add, scores, n_out, hist, hist_stride, chunk, row0);
+      if (HI <= 8) CSA2_IS_LAUNCH(2, 2, 4);
+      else CSA2_IS_LAUNCH(2, 1, 4);
       break;
     case 3:
-      hipLaunchKernelGGL(index_score_kernel<3>, grid, block, 0, st, codes, scales, cap, q_idx, w,
-                         HI, T, n_valid, pool, P, nv_add, scores, n_out, hist, hist_stride, chunk, row0);
+      CSA2_IS_LAUNCH(3, 1, 2);
       break;
     case 4:
-      hipLaunchKernelGGL(index_score_kernel<4>, grid, block, 0, st, codes, scales, cap, q_idx, w,
-                         HI, T, n_valid, pool, P, nv_add, scores, n_out, hist, hist_stride, chunk, row0);
+      CSA2_IS_LAUNCH(4, 1, 2);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef CSA2_IS_LAUNCH
   return hipGetLastError();
 }
 

@@ -9,109 +9,221 @@
 //
 // All 16 query heads share each KV row, so q.K and P.V are dense
 // contractions with M = 16 heads: fp16 MFMA 16x16x32.  The entries of a query
-// row are cut into splits of `tps` tiles of 16 entries; one block of 4 waves
-// handles a split.  Each round every wave gathers one tile (lane (i, g) owns
-// entry i and channels 64m + 16g + [0,16)), dequantizes it exactly to fp16 in
-// registers, computes the tile's logits and stores the value channels in LDS;
-// the block then updates a running (max, sum) per head and accumulates P.V
-// (wave w owns value channels [w*dv/4, (w+1)*dv/4)).  The next round's
-// gathers are issued before the current round is computed.  Splits hold
-// either global tiles or window tiles, never both, so window values enter as
-// raw E4M3 and their scale multiplies the split's partial output once.
+// row are cut into splits of 64 (global entries or window entries, never
+// both); one block of 4 waves takes a split, one tile of 16 entries per wave.
+// Lane (i, g) owns entry i and channels 64m + 16g + [0,16): it gathers them,
+// dequantizes exactly to fp16 in registers, and the wave computes the tile's
+// logits.  The block finds each head's maximum and sum over its 64 entries
+// (DPP reductions within a wave, LDS across waves), stores the value
+// channels in LDS, and wave w accumulates P.V for value channels
+// [w*dv/4, (w+1)*dv/4).  Window entries enter as raw E4M3 values and their
+// scale multiplies the split's logits and partial output.
 //
-// A second kernel merges the splits: one block per (query row, head) reads
-// every split's (max, sum, partial output) for that head -- all splits in
-// parallel -- and writes the normalised output and log-sum-exp.
+// Each split writes its partial (o, max, sum) per head.  The merge
+//   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L
+// runs in the same launch when every block of the grid can be resident at
+// once: a block writes its partial with device-coherent stores, waits for
+// them to complete, counts itself in the row's arrival counter and waits for
+// the row's other splits (bounded wait), then merges one slice of the row's
+// output with device-coherent loads.  Otherwise a second kernel merges.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-template <int NM>
-struct TileRaw {
-  uint32_t w0[NM], w1[NM];  // FP4 codes: channels 64m+16g+[0,8) and [8,16)
-  uint32_t w2[NM], w3[NM];  // window rows only: E4M3 bytes 8..15 of the 16
-  uint32_t sc[NM];          // FP4 scale byte (global rows)
-};
+// Longest wait of the merging blocks for the other splits of their row, in
+// polls of about 100 cycles (far beyond any real wait, a guard against a
+// grid that is not co-resident): the row's output is then set to NaN.
+constexpr int kSpinLimit = 1 << 20;
 
-template <int D, int DV>
+// Partials that another block of the same launch reads go through the
+// device-coherent path (agent-scope accesses: written through to, and read
+// from, the level all XCDs share) instead of full L2 write-back and
+// invalidate fences.
+template <bool COH>
+__device__ __forceinline__ void st_part(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ float ld_part(const float* p) {
+  if constexpr (COH)
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float4 ld_part4(const float* p) {
+  if constexpr (COH)
+    return make_float4(ld_part<true>(p), ld_part<true>(p + 1), ld_part<true>(p + 2),
+                       ld_part<true>(p + 3));
+  else
+    return *reinterpret_cast<const float4*>(p);
+}
+
+// Merge of the splits of one query row into output units [u0, u1) (a unit
+// is four channels of one head); `ml` is LDS for nsplit x 32 floats plus 256
+// float4.  All threads of the block call it.  The partial outputs a thread
+// needs are requested before the split maxima are reduced, so the merge
+// costs about two memory round trips.
+template <int DV, bool COH>
+__device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, int u1,
+                            float* __restrict__ orow, float* __restrict__ lrow, bool write_lse,
+                            bool ok, float* ml) {
+  constexpr int PSTRIDE = 16 * DV + 32;
+  constexpr int UPH = DV / 4;  // units per head
+  constexpr int KB = 16;       // partial loads in flight per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_M[16], s_L[16];
+  __shared__ float red[4][16];
+  const int nu = max(u1 - u0, 0);
+  int SUB = 1;  // threads per unit
+  while (SUB < 64 && SUB * 2 * nu <= 256) SUB *= 2;
+  const int per_pass = 256 / SUB;
+  float4* racc = reinterpret_cast<float4*>(ml + nsplit * 32);
+  constexpr int NU = 16 * DV / 4;
+  const int nml = nsplit * 32;
+  for (int ub = 0; ub == 0 || ub < nu; ub += per_pass) {
+    const int uu = ub + tid / SUB, sub = tid % SUB;
+    const bool live = uu < nu;
+    const int u = min(u0 + uu, NU - 1);  // clamped: every load below stays in bounds
+    const int h = u / UPH, c4 = u % UPH;
+    const float* col = prow + h * DV + 4 * c4;
+    // Split maxima and sums first (ml[s][0..15] = m, ml[s][16..31] = l), then
+    // this thread's partial outputs; indices are clamped rather than
+    // branched on, so every load is requested before any is used.
+    float mlv[8];
+    if (ub == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = min(k * 256 + tid, nml - 1);
+        mlv[k] = ld_part<COH>(prow + (int64_t)(j >> 5) * PSTRIDE + 16 * DV + (j & 31));
+      }
+    }
+    float4 v[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int s = min(sub + k * SUB, nsplit - 1);
+      v[k] = ld_part4<COH>(col + (int64_t)s * PSTRIDE);
+    }
+    if (ub == 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = k * 256 + tid;
+        if (j < nml) ml[j] = mlv[k];
+      }
+      for (int j = 8 * 256 + tid; j < nml; j += 256)  // beyond 64 splits
+        ml[j] = ld_part<COH>(prow + (int64_t)(j >> 5) * PSTRIDE + 16 * DV + (j & 31));
+      __syncthreads();
+      // per head hh: max and weighted sum over splits; lanes hh of the four
+      // 16-lane rows of the four waves take every 16th split
+      const int hh = lane & 15, qq = lane >> 4;
+      float mx = -INFINITY;
+      for (int s = wave * 4 + qq; s < nsplit; s += 16) mx = fmaxf(mx, ml[s * 32 + hh]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      if (qq == 0) red[wave][hh] = mx;
+      __syncthreads();
+      const float M = fmaxf(fmaxf(red[0][hh], red[1][hh]), fmaxf(red[2][hh], red[3][hh]));
+      float L = 0.0f;
+      for (int s = wave * 4 + qq; s < nsplit; s += 16) {
+        const float ms = ml[s * 32 + hh];
+        const float wv = (ms == -INFINITY) ? 0.0f : __expf(ms - M);
+        ml[s * 32 + hh] = wv;  // the max slot now holds the split's weight
+        L += wv * ml[s * 32 + 16 + hh];
+      }
+      L += shfl_xor(L, 16);
+      L += shfl_xor(L, 32);
+      __syncthreads();
+      if (qq == 0) red[wave][hh] = L;
+      __syncthreads();
+      if (tid < 16) {
+        s_M[tid] = M;
+        s_L[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      }
+      __syncthreads();
+      if (write_lse && tid < 16) {
+        const float Lt = s_L[tid];
+        lrow[tid] = !ok ? __int_as_float(0x7FC00000) : (Lt > 0.0f) ? s_M[tid] + logf(Lt) : -INFINITY;
+      }
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int s = sub + k * SUB;
+      const float wv = (live && s < nsplit) ? ml[s * 32 + h] : 0.0f;
+      acc.x += wv * v[k].x;
+      acc.y += wv * v[k].y;
+      acc.z += wv * v[k].z;
+      acc.w += wv * v[k].w;
+    }
+    // splits beyond the first KB per thread
+    for (int s0 = sub + KB * SUB; live && s0 < nsplit; s0 += KB * SUB) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) v[k] = ld_part4<COH>(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int s = s0 + k * SUB;
+        const float wv = (s < nsplit) ? ml[s * 32 + h] : 0.0f;
+        acc.x += wv * v[k].x;
+        acc.y += wv * v[k].y;
+        acc.z += wv * v[k].z;
+        acc.w += wv * v[k].w;
+      }
+    }
+    racc[tid] = acc;
+    __syncthreads();
+    if (live && sub == 0) {
+      float4 t = acc;
+      for (int k = 1; k < SUB; ++k) {
+        const float4 o = racc[tid + k];
+        t.x += o.x;
+        t.y += o.y;
+        t.z += o.z;
+        t.w += o.w;
+      }
+      const float L = s_L[h];
+      const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+      float4 res = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+      if (!ok) res = make_float4(NAN, NAN, NAN, NAN);
+      *reinterpret_cast<float4*>(orow + h * DV + 4 * c4) = res;
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int DV, bool FUSED>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, int32_t T, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int64_t cap, const int32_t* __restrict__ idx, int32_t K,
     const uint8_t* __restrict__ swa, const float* __restrict__ swa_scale,
     const int32_t* __restrict__ swa_pos0, int32_t S, int32_t W, const int32_t* __restrict__ q_pos,
-    float sm_scale, float* __restrict__ part, int32_t nsg, int32_t tps, int32_t nsplit,
-    int32_t row0) {
+    float sm_scale, float* __restrict__ part, int32_t nsg, int32_t nsplit, int32_t row0,
+    float* __restrict__ out, float* __restrict__ lse, uint32_t* __restrict__ cnt,
+    int64_t cnt_stride) {
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
   constexpr int VST = DV + 8;       // LDS row stride of V (halves), padded
   constexpr int CPW = DV / 4;       // value channels per wave
   constexpr int NT = CPW / 16;      // P.V output tiles per wave
   constexpr int PSTRIDE = 16 * DV + 32;
-  extern __shared__ _Float16 Vs[];  // [64 entries][VST]
-  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
+  extern __shared__ _Float16 Vs[];  // [64 entries][VST]; the merge reuses it
+  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the split]
   __shared__ float red_max[4][16];
   __shared__ float red_sum[4][16];
 
   const int r = blockIdx.y, b = (row0 + r) / T, sidx = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-
-  const int p = q_pos[r];
-  const int pos0 = (W > 0) ? swa_pos0[b] : 0;  // window arrays may be NULL without a window
-  const int wlo = max(p - W + 1, pos0);
-  const int whi = min(p, pos0 + S - 1);
-  const int nw = max(0, whi - wlo + 1);
   const bool is_win = sidx >= nsg;
-  const int tile0 = (is_win ? sidx - nsg : sidx) * tps;
-  const int ntile_kind = is_win ? (W + 15) / 16 : (K + 15) / 16;
-  const int tile_end = min(tile0 + tps, ntile_kind);
+  const int e = (is_win ? sidx - nsg : sidx) * 64 + wave * 16 + i;  // entry of this lane
 
-  // ---- gather of one tile into raw registers (no use of the data yet)
-  auto load_tile = [&](int tile, TileRaw<NM>& raw) -> bool {
-    const int e = tile * 16 + i;
-    const bool tvalid = tile < tile_end;
-    bool valid;
-    if (!is_win) {
-      const int ix = (tvalid && e < K) ? idx[(int64_t)r * K + e] : -1;
-      valid = ix >= 0 && ix < cap;
-      const int64_t row = (int64_t)b * cap + (valid ? ix : 0);
-      const uint8_t* cr = codes + row * (D / 2);
-      const uint8_t* sr = scales + row * (D / 16);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
-        raw.w0[m] = cw.x;
-        raw.w1[m] = cw.y;
-        raw.sc[m] = sr[4 * m + g];
-      }
-    } else {
-      valid = tvalid && e < nw;
-      const int64_t row = (int64_t)b * S + (valid ? (wlo - pos0 + e) : 0);
-      const uint8_t* wr = swa + row * D;
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
-        raw.w0[m] = v.x;
-        raw.w1[m] = v.y;
-        raw.w2[m] = v.z;
-        raw.w3[m] = v.w;
-      }
-    }
-    return valid;
-  };
-
-  TileRaw<NM> cur, nxt;
-  bool cur_valid = false, nxt_valid = false;
-  if (tile0 < tile_end) cur_valid = load_tile(tile0 + wave, cur);
-
-  // ---- query fragments (head i), scaled per head into fp16 range
-  f16x8 qa[NM][2];
-  int qexp;
+  // ---- loads, in dependency order: the index, then the query, then the row
+  int ix = -1;
+  if (!is_win && e < K) ix = idx[(int64_t)r * K + e];
+  uint32_t rq[NM][8];
   {
     const uint16_t* qr = q + ((int64_t)r * 16 + i) * D;
-    float amax = 0.0f;
-    uint32_t rq[NM][8];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint4 a = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g);
@@ -119,6 +231,45 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       rq[m][0] = a.x; rq[m][1] = a.y; rq[m][2] = a.z; rq[m][3] = a.w;
       rq[m][4] = c.x; rq[m][5] = c.y; rq[m][6] = c.z; rq[m][7] = c.w;
     }
+  }
+  uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
+  bool valid;
+  if (!is_win) {
+    valid = ix >= 0 && ix < cap;
+    const int64_t row = (int64_t)b * cap + (valid ? ix : 0);
+    const uint8_t* cr = codes + row * (D / 2);
+    const uint8_t* sr = scales + row * (D / 16);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
+      w0[m] = cw.x;
+      w1[m] = cw.y;
+      sc[m] = sr[4 * m + g];
+    }
+  } else {
+    const int p = q_pos[r];
+    const int pos0 = swa_pos0[b];
+    const int wlo = max(p - W + 1, pos0);
+    const int whi = min(p, pos0 + S - 1);
+    const int nw = max(0, whi - wlo + 1);
+    valid = e < nw;
+    const int64_t row = (int64_t)b * S + (valid ? (wlo - pos0 + e) : 0);
+    const uint8_t* wr = swa + row * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
+      w0[m] = v.x;
+      w1[m] = v.y;
+      w2[m] = v.z;
+      w3[m] = v.w;
+    }
+  }
+
+  // ---- query fragments (head i), scaled per head into fp16 range
+  f16x8 qa[NM][2];
+  int qexp;
+  {
+    float amax = 0.0f;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -146,226 +297,201 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   const float wscale = is_win ? swa_scale[b] : 1.0f;
   const float lscale = sm_scale * wscale;
 
-  float m_run[4], l_run[4];
-  f32x4 o[NT];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    m_run[rr] = -INFINITY;
-    l_run[rr] = 0.0f;
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int t0 = tile0; t0 < tile_end; t0 += 4) {
-    if (t0 + 4 < tile_end) nxt_valid = load_tile(t0 + 4 + wave, nxt);
-    // dequantize this wave's tile
-    f16x8 k0[NM], k1[NM];
+  // ---- dequantize this wave's tile, logits (rows = heads 4g + rr, column = entry i)
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    _Float16* vrow = Vs + (wave * 16 + i) * VST;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
+      f16x8 k0, k1;
       if (!is_win) {
-        const f16x2 s2 = scale_pair(cur.sc[m]);
-        k0[m] = fp4x8_to_f16(cur.w0[m], s2);
-        k1[m] = fp4x8_to_f16(cur.w1[m], s2);
+        const f16x2 s2 = scale_pair(sc[m]);
+        k0 = fp4x8_to_f16(w0[m], s2);
+        k1 = fp4x8_to_f16(w1[m], s2);
       } else {
         uint4 v;
-        v.x = cur.w0[m];
-        v.y = cur.w1[m];
-        v.z = cur.w2[m];
-        v.w = cur.w3[m];
-        e4m3x16_to_f16(v, k0[m], k1[m]);
+        v.x = w0[m];
+        v.y = w1[m];
+        v.z = w2[m];
+        v.w = w3[m];
+        e4m3x16_to_f16(v, k0, k1);
+      }
+      acc = mfma16x16x32(qa[m][0], k0, acc);
+      acc = mfma16x16x32(qa[m][1], k1, acc);
+      if (m < NMV) {
+        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0;
+        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
       }
     }
-    // logits of this tile: rows = heads 4g + rr, column = entry i
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // ---- softmax statistics of the split, per head
+  float lg[4], mh[4];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      acc = mfma16x16x32(qa[m][0], k0[m], acc);
-      acc = mfma16x16x32(qa[m][1], k1[m], acc);
+  for (int rr = 0; rr < 4; ++rr) {
+    lg[rr] = valid ? ldexpf(acc[rr], -er[rr]) * lscale : -INFINITY;
+    const float mx = row16_max(lg[rr]);
+    if (i == 0) red_max[wave][4 * g + rr] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int h = 4 * g + rr;
+    mh[rr] = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
+    const float pr = (mh[rr] == -INFINITY) ? 0.0f : __expf(lg[rr] - mh[rr]);
+    Ps[h * 64 + wave * 16 + i] = (_Float16)pr;
+    const float ps = row16_sum(pr);  // the sum uses the unrounded probabilities
+    if (i == 0) red_sum[wave][h] = ps;
+  }
+  __syncthreads();
+  // ---- P.V for this wave's channels
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ch = wave * CPW + nt * 16 + i;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
+      f16x8 vb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vb[j] = Vs[(32 * ks + 8 * g + j) * VST + ch];
+      o[nt] = mfma16x16x32(pa, vb, o[nt]);
     }
-    {
-      _Float16* vrow = Vs + (wave * 16 + i) * VST;
-#pragma unroll
-      for (int m = 0; m < NMV; ++m) {
-        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0[m];
-        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1[m];
-      }
-    }
-    float lg[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      lg[rr] = cur_valid ? ldexpf(acc[rr], -er[rr]) * lscale : -INFINITY;
-      float mx = lg[rr];
-      mx = fmaxf(mx, shfl_xor(mx, 1));
-      mx = fmaxf(mx, shfl_xor(mx, 2));
-      mx = fmaxf(mx, shfl_xor(mx, 4));
-      mx = fmaxf(mx, shfl_xor(mx, 8));
-      if (i == 0) red_max[wave][4 * g + rr] = mx;
-    }
-    __syncthreads();
-    float alpha[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      const float mr = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-      const float mnew = fmaxf(m_run[rr], mr);
-      alpha[rr] = (mnew == -INFINITY) ? 1.0f : __expf(m_run[rr] - mnew);
-      const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lg[rr] - mnew);
-      Ps[h * 64 + wave * 16 + i] = (_Float16)pr;
-      float ps = pr;  // the normaliser sums the unrounded probabilities
-      ps += shfl_xor(ps, 1);
-      ps += shfl_xor(ps, 2);
-      ps += shfl_xor(ps, 4);
-      ps += shfl_xor(ps, 8);
-      if (i == 0) red_sum[wave][h] = ps;
-      m_run[rr] = mnew;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      l_run[rr] = l_run[rr] * alpha[rr] + (red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
-    }
-    // P.V for this wave's channels
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) o[nt][rr] *= alpha[rr];
-      const int ch = wave * CPW + nt * 16 + i;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
-        f16x8 vb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vb[j] = Vs[(32 * ks + 8 * g + j) * VST + ch];
-        o[nt] = mfma16x16x32(pa, vb, o[nt]);
-      }
-    }
-    __syncthreads();
-    cur = nxt;
-    cur_valid = nxt_valid;
   }
 
   // ---- partial result of this split: o[16][DV], m[16], l[16]
-  float* pb = part + ((int64_t)r * nsplit + sidx) * PSTRIDE;
+  float* prow = part + (int64_t)r * nsplit * PSTRIDE;
+  float* pb = prow + (int64_t)sidx * PSTRIDE;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      pb[(4 * g + rr) * DV + wave * CPW + nt * 16 + i] = o[nt][rr] * wscale;
+      st_part<FUSED>(pb + (4 * g + rr) * DV + wave * CPW + nt * 16 + i, o[nt][rr] * wscale);
   if (wave == 0 && i == 0) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      pb[16 * DV + 4 * g + rr] = m_run[rr];
-      pb[16 * DV + 16 + 4 * g + rr] = l_run[rr];
+      const int h = 4 * g + rr;
+      st_part<FUSED>(pb + 16 * DV + h, mh[rr]);
+      st_part<FUSED>(pb + 16 * DV + 16 + h,
+                     red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
+    }
+  }
+  if constexpr (FUSED) {
+    // publish the partial, then wait for the row's other splits
+    __shared__ int s_ok;
+    uint32_t* arrive = cnt + (int64_t)r * cnt_stride;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int ok = 0;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        if (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+            (uint32_t)nsplit) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      s_ok = ok;
+    }
+    __syncthreads();
+    const bool ok = s_ok != 0;
+    // this block's slice of the row's output units
+    constexpr int NU = 16 * DV / 4;
+    const int per = (NU + nsplit - 1) / nsplit;
+    const int u0 = min(sidx * per, NU), u1 = min(u0 + per, NU);
+    merge_slice<DV, true>(prow, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
+                    lse ? lse + (int64_t)r * 16 : nullptr, lse && sidx == 0, ok,
+                    reinterpret_cast<float*>(Vs));
+    // the last block to leave clears the row's counters for the next call
+    if (tid == 0) {
+      uint32_t* leave = arrive + 1;
+      if (__hip_atomic_fetch_add(leave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          (uint32_t)nsplit - 1u) {
+        __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(leave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
 
-// Merge of the splits of query row r for head h (blockDim = DV/4 threads,
-// four channels each).
+// Merge kernel for grids that cannot all be resident: block (x, r) merges
+// units [256x, 256x + 256) of row r.
 template <int DV>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
                                                            int32_t nsplit, float* __restrict__ out,
                                                            float* __restrict__ lse) {
+  extern __shared__ float ml[];
   constexpr int PSTRIDE = 16 * DV + 32;
-  constexpr int NTH = DV / 4;
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float red[NTH];
-  __shared__ float s_M, s_L;
-  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const float* prow = part + (int64_t)r * nsplit * PSTRIDE;
-  // split maxima and sums of this head
-  float mloc = -INFINITY;
-  for (int s = tid; s < nsplit; s += NTH) {
-    const float ms = prow[(int64_t)s * PSTRIDE + 16 * DV + h];
-    wgt[s] = ms;
-    mloc = fmaxf(mloc, ms);
-  }
-  red[tid] = mloc;
-  __syncthreads();
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int j = 0; j < NTH; ++j) M = fmaxf(M, red[j]);
-    s_M = M;
-  }
-  __syncthreads();
-  const float M = s_M;
-  float lloc = 0.0f;
-  for (int s = tid; s < nsplit; s += NTH) {
-    const float ms = wgt[s];
-    const float wv = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
-    wgt[s] = wv;
-    lloc += wv * prow[(int64_t)s * PSTRIDE + 16 * DV + 16 + h];
-  }
-  red[tid] = lloc;
-  __syncthreads();
-  if (tid == 0) {
-    float L = 0.0f;
-    for (int j = 0; j < NTH; ++j) L += red[j];
-    s_L = L;
-  }
-  __syncthreads();
-  const float L = s_L;
-  // weighted sum of the partial outputs: four splits' loads in flight at once
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* col = prow + h * DV + 4 * tid;
-  int s = 0;
-  for (; s + 4 <= nsplit; s += 4) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(col + (int64_t)(s + u) * PSTRIDE);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wv = wgt[s + u];
-      acc.x += wv * v[u].x;
-      acc.y += wv * v[u].y;
-      acc.z += wv * v[u].z;
-      acc.w += wv * v[u].w;
-    }
-  }
-  for (; s < nsplit; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(col + (int64_t)s * PSTRIDE);
-    const float wv = wgt[s];
-    acc.x += wv * v.x;
-    acc.y += wv * v.y;
-    acc.z += wv * v.z;
-    acc.w += wv * v.w;
-  }
-  const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-  acc.x *= inv;
-  acc.y *= inv;
-  acc.z *= inv;
-  acc.w *= inv;
-  *reinterpret_cast<float4*>(out + ((int64_t)r * 16 + h) * DV + 4 * tid) = acc;
-  if (lse && tid == 0) lse[(int64_t)r * 16 + h] = (L > 0.0f) ? M + logf(L) : -INFINITY;
+  constexpr int NU = 16 * DV / 4;
+  const int r = blockIdx.y;
+  const int u0 = blockIdx.x * 256, u1 = min(u0 + 256, NU);
+  merge_slice<DV, false>(part + (int64_t)r * nsplit * PSTRIDE, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
+                  lse ? lse + (int64_t)r * 16 : nullptr, lse && blockIdx.x == 0, true, ml);
 }
 
 size_t attn_lds_bytes(int32_t dv) { return (size_t)64 * (dv + 8) * sizeof(_Float16); }
 
+static size_t merge_lds_bytes(int32_t nsplit) {
+  return (size_t)nsplit * 32 * sizeof(float) + 256 * sizeof(float4);
+}
+
+// Blocks of the fused kernel that fit on the device at once.
+template <typename F>
+static int64_t resident_blocks(F kernel, size_t lds) {
+  static int64_t cached = -1;
+  if (cached < 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess)
+      return 0;
+    cached = (int64_t)cus * per_cu;
+  }
+  return cached;
+}
+
 template <int D, int DV>
-static hipError_t launch_attn_pair(const uint16_t* q, int32_t rows, int32_t T,
-                                   const uint8_t* codes, const uint8_t* scales, int64_t cap,
-                                   const int32_t* idx, int32_t K, const uint8_t* swa,
-                                   const float* swa_scale, const int32_t* swa_pos0, int32_t S,
-                                   int32_t W, const int32_t* q_pos, float sm_scale, float* out,
-                                   float* lse, const AttnWs& w, hipStream_t st, int32_t row0) {
+static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const uint8_t* codes,
+                              const uint8_t* scales, int64_t cap, const int32_t* idx, int32_t K,
+                              const uint8_t* swa, const float* swa_scale,
+                              const int32_t* swa_pos0, int32_t S, int32_t W,
+                              const int32_t* q_pos, float sm_scale, float* out, float* lse,
+                              const AttnWs& w, hipStream_t st, int32_t row0) {
+  const size_t lds = attn_lds_bytes(DV);
   static bool lds_raised = false;
   if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)attn_lds_bytes(DV));
+    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attn_combine_kernel<DV>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)merge_lds_bytes(kMaxSplits));
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
   const AttnSplit sp = attn_split(K, W);
-  hipLaunchKernelGGL((sparse_attn_kernel<D, DV>), dim3((unsigned)sp.nsplit, (unsigned)rows),
-                     dim3(256), attn_lds_bytes(DV), st, q, T, codes, scales, cap, idx, K, swa,
-                     swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part, sp.nsg, sp.tps, sp.nsplit,
-                     row0);
+  const dim3 grid((unsigned)sp.nsplit, (unsigned)rows);
+  const bool fused = merge_lds_bytes(sp.nsplit) <= lds && w.cnt != nullptr &&
+                     (int64_t)sp.nsplit * rows <= resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
+  if (fused) {
+    hipLaunchKernelGGL((sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, q, T, codes,
+                       scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
+                       sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, q, T, codes,
+                     scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
+                     sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<DV>), dim3((unsigned)rows, 16u), dim3(DV / 4), 0, st,
-                     w.part, sp.nsplit, out, lse);
+  constexpr int NU = 16 * DV / 4;
+  hipLaunchKernelGGL((attn_combine_kernel<DV>), dim3((NU + 255) / 256, (unsigned)rows), dim3(256),
+                     merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, out, lse);
   return hipGetLastError();
 }
 
@@ -376,11 +502,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_
                               int32_t W, const int32_t* q_pos, float sm_scale, float* out,
                               float* lse, const AttnWs& w, hipStream_t st, int32_t row0) {
   if (D == 576 && dv == 512)
-    return launch_attn_pair<576, 512>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale,
-                                      swa_pos0, S, W, q_pos, sm_scale, out, lse, w, st, row0);
+    return launch_attn<576, 512>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0);
   if (D == 128 && dv == 128)
-    return launch_attn_pair<128, 128>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale,
-                                      swa_pos0, S, W, q_pos, sm_scale, out, lse, w, st, row0);
+    return launch_attn<128, 128>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0);
   return hipErrorInvalidValue;
 }
 

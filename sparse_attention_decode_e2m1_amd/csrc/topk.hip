@@ -15,24 +15,43 @@
 //     (a block adds into copy blockIdx % kHistCopies: device-scope atomics on
 //     one address serialise).  Built by the scoring kernel, or here by
 //     topk_hist_kernel.
-//  2. topk_select_kernel, many blocks per row: each block sums the copies and
-//     finds the bin b1 holding the K-th key.  Its elements above b1 are kept;
-//     those in b1 are candidates.  Both go to the block's own regions as
-//     position-ordered lists (block-wide prefix sums, no atomics), with their
-//     counts.
-//  3. topk_final_kernel, one block per row: gathers the lists into LDS,
-//     resolves the remaining entries among the candidates by radix selection
-//     over the 64-bit rank values, keeps the chosen ones in position order,
-//     merges the two sorted lists by binary search and writes the output.
-//     It then clears the histogram copies for the next call.
+//  2. topk_select_kernel, one 1024-thread block per kTopkChunk (4096) scores
+//     of a row: the block sums the histogram copies and finds the bin b1 holding
+//     the K-th key.  Its scores above b1 are kept outright; those in b1 are
+//     candidates.  Wave w takes a contiguous run of slots, so a count pass
+//     and a prefix over the 16 wave totals place both lists in position
+//     order in the block's own regions.  The regions and the block's counts
+//     are written with device-coherent stores; then the block counts itself
+//     in the row's arrival counter.
+//  3. The row's last block to arrive finishes it: it turns the counts into
+//     offsets, gathers the lists into LDS, resolves the remaining entries
+//     among the candidates by radix selection over the 64-bit rank values,
+//     keeps the chosen ones in position order, merges the two sorted lists
+//     by binary search and writes the output.  It then clears the histogram
+//     copies and the counter for the next call.
 // Every pass over memory issues all of a thread's loads before using them.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-constexpr int kPerThread = kTopkChunk / 256;  // scores per thread per select block
-constexpr int kFinalThreads = 1024;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSlotsPerWave = kTopkChunk / kSelWaves;  // 256 consecutive slots
+constexpr int kPerLane = kSlotsPerWave / 64;           // 4 scores per lane
+constexpr int kHistPerThread = kHistBins / kSelThreads;  // 4 bins per thread
+static_assert(kHistPerThread == 4, "one uint4 of each histogram copy per thread");
+
+// Device-coherent accesses for data one block writes and another block of
+// the same launch reads (agent scope: no full-cache write-back or invalidate).
+template <typename T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ scores,
                                                         int64_t n,
@@ -40,6 +59,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
                                                         int32_t nv_add,
                                                         uint32_t* __restrict__ hist,
                                                         int64_t hist_stride) {
+  constexpr int PT = kTopkChunk / 256;
   __shared__ uint32_t lhist[kHistBins];
   const int r = blockIdx.y;
   const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
@@ -47,15 +67,15 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
   if (start >= nv) return;
   for (int k = threadIdx.x; k < kHistBins; k += 256) lhist[k] = 0u;
   const float* srow = scores + (int64_t)r * n;
-  float v[kPerThread];
+  float v[PT];
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < PT; ++j) {
     const int64_t s = start + j * 256 + threadIdx.x;
     v[j] = (s < nv) ? srow[s] : 0.0f;
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
+  for (int j = 0; j < PT; ++j)
     if (start + j * 256 + threadIdx.x < nv) atomicAdd(&lhist[score_key(v[j]) >> kHistShift], 1u);
   __syncthreads();
   uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
@@ -63,18 +83,29 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
     if (lhist[k]) atomicAdd(gh + k, lhist[k]);
 }
 
-// Exclusive prefix sum over a block of NT threads; `tmp` holds NT/64 words.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_u32<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_u32<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_u32<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_u32<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_u32<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Exclusive prefix sum over the block (NT threads); `tmp` holds NT/64 words.
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   uint32_t off = 0, tot = 0;
 #pragma unroll
@@ -85,322 +116,382 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32
   }
   __syncthreads();
   *total = tot;
-  return off + x - v;
+  return off + inc - v;
 }
 
-__global__ __launch_bounds__(256) void topk_select_kernel(
-    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
-    int32_t nv_add, int32_t k, const uint32_t* __restrict__ hist, int64_t hist_stride,
-    TopkWs w) {
-  __shared__ uint32_t tmp[8];
-  __shared__ uint32_t cnt[kPerThread * 4];  // packed (above << 16 | cand) per (j, wave)
-  __shared__ int s_b1;
-
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
-  if (nv <= k) return;  // the final kernel takes every valid slot
-  const int64_t start = (int64_t)blockIdx.x * kTopkChunk;
-  uint32_t* crow = w.counts + (int64_t)r * w.counts_stride + 2 * blockIdx.x;
-  if (start >= nv) {
-    if (tid == 0) crow[0] = crow[1] = 0u;
-    return;
-  }
-  const float* srow = scores + (int64_t)r * n;
-  // scores of this thread: for each j the 4 waves cover 256 consecutive slots
-  float v[kPerThread];
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t s = start + 256 * j + 64 * wave + lane;
-    v[j] = (s < nv) ? srow[s] : 0.0f;
-  }
-  // histogram of the row summed over its copies; this thread's bins [16t, 16t+16)
-  uint32_t h16[16];
-  {
-    const uint32_t* rh = hist + (int64_t)r * hist_stride;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) h16[j] = 0u;
-#pragma unroll
-    for (int c = 0; c < kHistCopies; ++c) {
-      const uint4* p = reinterpret_cast<const uint4*>(rh + c * kHistBins + 16 * tid);
-      const uint4 a = p[0], b = p[1], d = p[2], e = p[3];
-      h16[0] += a.x; h16[1] += a.y; h16[2] += a.z; h16[3] += a.w;
-      h16[4] += b.x; h16[5] += b.y; h16[6] += b.z; h16[7] += b.w;
-      h16[8] += d.x; h16[9] += d.y; h16[10] += d.z; h16[11] += d.w;
-      h16[12] += e.x; h16[13] += e.y; h16[14] += e.z; h16[15] += e.w;
-    }
-  }
-  if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
-  {
-    uint32_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sum += h16[j];
-    uint32_t total;
-    const uint32_t excl = block_exclusive_scan256(sum, tmp, &total);
-    const uint32_t above = total - excl - sum;  // elements in bins of higher threads
-    if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
-      uint32_t acc = above;
-      bool found = false;
-#pragma unroll
-      for (int j = 15; j >= 0; --j) {
-        if (!found && acc + h16[j] >= (uint32_t)k) {
-          s_b1 = 16 * tid + j;
-          found = true;
-        }
-        acc += h16[j];
-      }
-    }
-    __syncthreads();
-  }
-  const uint32_t b1 = (uint32_t)s_b1;
-  // counts per (j, wave), packed above << 16 | candidates
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t s = start + 256 * j + 64 * wave + lane;
-    const uint32_t bin = (s < nv) ? (score_key(v[j]) >> kHistShift) : 0u;
-    const uint32_t na = (uint32_t)__popcll(__ballot(s < nv && bin > b1));
-    const uint32_t ne = (uint32_t)__popcll(__ballot(s < nv && bin == b1));
-    if (lane == 0) cnt[4 * j + wave] = (na << 16) | ne;
-  }
-  __syncthreads();
-  // exclusive offsets in (j, wave) order = slot order
-  static_assert(kPerThread * 4 <= 256, "one count per thread");
-  uint32_t total;
-  const uint32_t mine = (tid < kPerThread * 4) ? cnt[tid] : 0u;
-  const uint32_t excl = block_exclusive_scan256(mine, tmp, &total);
-  if (tid < kPerThread * 4) cnt[tid] = excl;
-  __syncthreads();
-  uint32_t* ra = w.above + (int64_t)r * w.above_stride + (int64_t)blockIdx.x * kTopkChunk;
-  uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kTopkChunk;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t s = start + 256 * j + 64 * wave + lane;
-    const uint32_t key = (s < nv) ? score_key(v[j]) : 0u;
-    const uint32_t bin = key >> kHistShift;
-    const bool ab = s < nv && bin > b1;
-    const bool eq = s < nv && bin == b1;
-    const uint64_t ma = __ballot(ab), me = __ballot(eq);
-    const uint32_t base = cnt[4 * j + wave];
-    if (ab) ra[(base >> 16) + (uint32_t)__popcll(ma & lanemask_lt())] = (uint32_t)s;
-    if (eq) rc[(base & 0xFFFFu) + (uint32_t)__popcll(me & lanemask_lt())] = rank_value(key, (uint32_t)s);
-  }
-  if (tid == 0) {
-    crow[0] = total >> 16;
-    crow[1] = total & 0xFFFFu;
-  }
-}
-
-__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
-    int64_t n, const int32_t* __restrict__ n_valid, int32_t nv_add,
-    const int32_t* __restrict__ slot_pos, int32_t k, int32_t nblk, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, uint32_t* __restrict__ hist, int64_t hist_stride,
-    TopkWs w, int32_t lds_cand) {
-  extern __shared__ uint32_t smem[];
+// Completion of row r by its last block (all select blocks of the row have
+// written their regions and counts).
+__device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
+                           int32_t k, int nblk, int32_t* __restrict__ idx_out,
+                           int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
+                           uint32_t* smem, uint32_t* tmp) {
+  constexpr int NT = kSelThreads;
   uint32_t* rhist = smem;                      // 2048 radix bins
   uint32_t* offA = rhist + 2048;               // nblk + 1
   uint32_t* offE = offA + (nblk + 1);          // nblk + 1
   uint32_t* list = offE + (nblk + 1);          // k: kept positions (above, then chosen)
   uint64_t* cl = reinterpret_cast<uint64_t*>(list + ((k + 1) & ~1));  // lds_cand candidates
-  __shared__ uint32_t tmp[16];
   __shared__ int s_dig;
   __shared__ uint32_t s_dig_above;
-
-  const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
   int32_t* orow = idx_out + (int64_t)r * k;
   const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
-  uint32_t* rh = hist + (int64_t)r * hist_stride;
 
   if (nv <= k) {
-    for (int j = tid; j < k; j += kFinalThreads) orow[j] = (j < nv) ? (sp ? sp[j] : j) : -1;
+    for (int j = tid; j < k; j += NT) orow[j] = (j < nv) ? (sp ? sp[j] : j) : -1;
     if (count_out && tid == 0) count_out[r] = (int32_t)nv;
-  } else {
-    // ---- per-block counts -> offsets
-    const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
-    const int per = (nblk + kFinalThreads - 1) / kFinalThreads;
-    uint32_t a_loc = 0, e_loc = 0;
-    for (int j = 0; j < per; ++j) {
-      const int b = tid * per + j;
-      if (b < nblk) {
-        a_loc += crow[2 * b];
-        e_loc += crow[2 * b + 1];
-      }
-    }
-    uint32_t A, C;
-    uint32_t ra = block_scan<kFinalThreads>(a_loc, tmp, &A);
-    uint32_t rc = block_scan<kFinalThreads>(e_loc, tmp, &C);
-    for (int j = 0; j < per; ++j) {
-      const int b = tid * per + j;
-      if (b < nblk) {
-        offA[b] = ra;
-        offE[b] = rc;
-        ra += crow[2 * b];
-        rc += crow[2 * b + 1];
-      }
-    }
-    if (tid == 0) {
-      offA[nblk] = A;
-      offE[nblk] = C;
-    }
-    __syncthreads();
-    const uint32_t need = (uint32_t)k - min(A, (uint32_t)k);
-    // list element c of a family of per-block regions: block = last b with off[b] <= c
-    auto block_of = [&](const uint32_t* off, uint32_t c) -> int {
-      int lo = 0, hi = nblk - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= c) lo = mid; else hi = mid - 1;
-      }
-      return lo;
-    };
-    const uint32_t* abase = w.above + (int64_t)r * w.above_stride;
-    const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
-    auto cand_at = [&](uint32_t c) -> uint64_t {
-      const int b = block_of(offE, c);
-      return cbase[(int64_t)b * kTopkChunk + (c - offE[b])];
-    };
-    // ---- gather the kept ("above") positions and the candidates
-    const uint32_t Ak = min(A, (uint32_t)k);
-    for (uint32_t c0 = 0; c0 < Ak; c0 += kFinalThreads * 4) {
-      uint32_t t[4];
+    return;
+  }
+  // ---- per-block counts -> offsets
+  const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
+  constexpr int kMaxPer = (int)(kMaxTopkN / kTopkChunk / NT);  // blocks per thread
+  static_assert(kMaxPer >= 1 && kMaxPer <= 8, "counts held in registers");
+  const int per = (nblk + NT - 1) / NT;
+  uint32_t ca[kMaxPer], ce[kMaxPer];
+  uint32_t a_loc = 0, e_loc = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t c = c0 + u * kFinalThreads + tid;
-        if (c < Ak) {
-          const int b = block_of(offA, c);
-          t[u] = abase[(int64_t)b * kTopkChunk + (c - offA[b])];
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int b = tid * per + j;
+    const bool in = j < per && b < nblk;
+    ca[j] = in ? ld_coh(crow + 2 * b) : 0u;
+    ce[j] = in ? ld_coh(crow + 2 * b + 1) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    a_loc += ca[j];
+    e_loc += ce[j];
+  }
+  uint32_t A, C;
+  uint32_t ra = block_scan<NT>(a_loc, tmp, &A);
+  uint32_t rc = block_scan<NT>(e_loc, tmp, &C);
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int b = tid * per + j;
+    if (j < per && b < nblk) {
+      offA[b] = ra;
+      offE[b] = rc;
+      ra += ca[j];
+      rc += ce[j];
+    }
+  }
+  if (tid == 0) {
+    offA[nblk] = A;
+    offE[nblk] = C;
+  }
+  __syncthreads();
+  const uint32_t need = (uint32_t)k - min(A, (uint32_t)k);
+  // element c of a family of per-block regions: block = last b with off[b] <= c
+  auto block_of = [&](const uint32_t* off, uint32_t c) -> int {
+    int lo = 0, hi = nblk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  const uint32_t* abase = w.above + (int64_t)r * w.above_stride;
+  const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
+  auto cand_at = [&](uint32_t c) -> uint64_t {
+    const int b = block_of(offE, c);
+    return ld_coh(cbase + (int64_t)b * kTopkChunk + (c - offE[b]));
+  };
+  // ---- gather the kept ("above") positions and the candidates
+  const uint32_t Ak = min(A, (uint32_t)k);
+  const bool in_lds = C <= (uint32_t)lds_cand;
+  {
+    // TPB threads per select block (a power of two), each copying every
+    // TPB-th entry of the block's two regions; indices are clamped rather
+    // than branched on, so a thread's loads are in flight together.
+    const uint32_t nC = in_lds ? C : 0u;
+    int tpb = 1;
+    while (tpb * 2 * nblk <= NT) tpb *= 2;
+    const int bpp = NT / tpb;
+    for (int b0 = 0; b0 < nblk; b0 += bpp) {
+      const int b = b0 + tid / tpb, j = tid % tpb;
+      const bool live = b < nblk;
+      const int bb = live ? b : 0;
+      const uint32_t a_lo = min(offA[bb], Ak), a_hi = live ? min(offA[bb + 1], Ak) : a_lo;
+      const uint32_t e_lo = min(offE[bb], nC), e_hi = live ? min(offE[bb + 1], nC) : e_lo;
+      const uint32_t* ar = abase + (int64_t)bb * kTopkChunk;
+      const uint64_t* cr = cbase + (int64_t)bb * kTopkChunk;
+      const uint32_t na = a_hi - a_lo, ne = e_hi - e_lo;
+      for (uint32_t i0 = j; i0 < max(na, ne); i0 += 8 * tpb) {
+        uint32_t ta[8];
+        uint64_t tc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = i0 + u * tpb;
+          ta[u] = ld_coh(ar + min(i, max(na, 1u) - 1u));
+          tc[u] = ld_coh(cr + min(i, max(ne, 1u) - 1u));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = i0 + u * tpb;
+          if (i < na) list[a_lo + i] = ta[u];
+          if (i < ne) cl[e_lo + i] = tc[u];
         }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t c = c0 + u * kFinalThreads + tid;
-        if (c < Ak) list[c] = t[u];
-      }
     }
-    const bool in_lds = C <= (uint32_t)lds_cand;
+  }
+  __syncthreads();
+  auto for_each = [&](auto&& f) {
     if (in_lds) {
-      for (uint32_t c0 = 0; c0 < C; c0 += kFinalThreads * 4) {
+      for (uint32_t c = tid; c < C; c += NT) f(cl[c]);
+    } else {
+      for (uint32_t c0 = 0; c0 < C; c0 += NT * 4) {
         uint64_t t[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t c = c0 + u * kFinalThreads + tid;
+          const uint32_t c = c0 + u * NT + tid;
           if (c < C) t[u] = cand_at(c);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t c = c0 + u * kFinalThreads + tid;
-          if (c < C) cl[c] = t[u];
-        }
+        for (int u = 0; u < 4; ++u)
+          if (c0 + u * NT + tid < C) f(t[u]);
       }
     }
-    __syncthreads();
-    auto for_each = [&](auto&& f) {
-      if (in_lds) {
-        for (uint32_t c = tid; c < C; c += kFinalThreads) f(cl[c]);
-      } else {
-        for (uint32_t c0 = 0; c0 < C; c0 += kFinalThreads * 4) {
-          uint64_t t[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t c = c0 + u * kFinalThreads + tid;
-            if (c < C) t[u] = cand_at(c);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (c0 + u * kFinalThreads + tid < C) f(t[u]);
-        }
+  };
+  // ---- radix selection of the need-th largest rank value among the
+  // candidates (all share the 12 top bits b1): 11-bit digits at shifts 41,
+  // 30, 19, 8, then 8 bits at 0; stop once a whole bucket is taken.
+  uint64_t thr = ~0ull;
+  if (need > 0) {
+    uint64_t prefix = 0;
+    uint32_t rem = need;
+    const int shifts[5] = {41, 30, 19, 8, 0};
+    const int widths[5] = {11, 11, 11, 11, 8};
+    for (int p = 0; p < 5; ++p) {
+      const int sh = shifts[p], wd = widths[p];
+      const int nb = 1 << wd;
+      for (int j = tid; j < 2048; j += NT) rhist[j] = 0u;
+      if (tid == 0) {
+        s_dig = 0;
+        s_dig_above = 0;
       }
-    };
-    // ---- radix selection of the need-th largest rank value among the
-    // candidates (all share the 12 top bits b1): 11-bit digits at shifts 41,
-    // 30, 19, 8, then 8 bits at 0; stop once a whole bucket is taken.
-    uint64_t thr = ~0ull;
-    if (need > 0) {
-      uint64_t prefix = 0;
-      uint32_t rem = need;
-      const int shifts[5] = {41, 30, 19, 8, 0};
-      const int widths[5] = {11, 11, 11, 11, 8};
-      for (int p = 0; p < 5; ++p) {
-        const int sh = shifts[p], wd = widths[p];
-        const int nb = 1 << wd;
-        for (int j = tid; j < 2048; j += kFinalThreads) rhist[j] = 0u;
-        if (tid == 0) {
-          s_dig = 0;
-          s_dig_above = 0;
-        }
-        __syncthreads();
-        const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
-        for_each([&](uint64_t x) {
-          if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
-        });
-        __syncthreads();
-        // digit d with count(> d) < rem <= count(>= d); 2 bins per thread
-        const int b0 = 2 * tid;
-        const uint32_t c0v = (b0 < nb) ? rhist[b0] : 0u, c1v = (b0 + 1 < nb) ? rhist[b0 + 1] : 0u;
-        uint32_t tot;
-        const uint32_t ex = block_scan<kFinalThreads>(c0v + c1v, tmp, &tot);
-        const uint32_t above = tot - ex - c0v - c1v;
-        if (above < rem && above + c1v >= rem) {
-          s_dig = b0 + 1;
-          s_dig_above = above;
-        } else if (above + c1v < rem && above + c1v + c0v >= rem) {
-          s_dig = b0;
-          s_dig_above = above + c1v;
-        }
-        __syncthreads();
-        const uint32_t d = (uint32_t)s_dig;
-        rem -= s_dig_above;
-        prefix |= (uint64_t)d << sh;
-        const bool whole_bucket = rhist[d] == rem;
-        __syncthreads();
-        if (whole_bucket) break;
-      }
-      thr = prefix;
-    }
-    // ---- chosen candidates (rank value within b1 >= thr), kept in slot
-    // order: the concatenated candidate regions are slot-ordered.
-    const uint64_t low52 = (1ull << 52) - 1;
-    uint32_t kept;  // k unless the histogram disagreed with the scores
-    {
-      const uint32_t per_c = (C + kFinalThreads - 1) / kFinalThreads;
-      const uint32_t lo = min(tid * per_c, C), hi = min(lo + per_c, C);
-      uint32_t cnt = 0;
-      for (uint32_t c = lo; c < hi; ++c) {
-        const uint64_t x = in_lds ? cl[c] : cand_at(c);
-        cnt += (need > 0 && (x & low52) >= thr) ? 1u : 0u;
-      }
+      __syncthreads();
+      const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
+      for_each([&](uint64_t x) {
+        if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
+      });
+      __syncthreads();
+      // digit d with count(> d) < rem <= count(>= d); 2 bins per thread
+      const int b0 = 2 * tid;
+      const uint32_t c0v = (b0 < nb) ? rhist[b0] : 0u, c1v = (b0 + 1 < nb) ? rhist[b0 + 1] : 0u;
       uint32_t tot;
-      uint32_t o = Ak + block_scan<kFinalThreads>(cnt, tmp, &tot);
-      kept = Ak + min(tot, need);
-      for (uint32_t c = lo; c < hi; ++c) {
-        const uint64_t x = in_lds ? cl[c] : cand_at(c);
-        if (need > 0 && (x & low52) >= thr && o < kept) list[o++] = rank_slot(x);
+      const uint32_t ex = block_scan<NT>(c0v + c1v, tmp, &tot);
+      const uint32_t above = tot - ex - c0v - c1v;
+      if (above < rem && above + c1v >= rem) {
+        s_dig = b0 + 1;
+        s_dig_above = above;
+      } else if (above + c1v < rem && above + c1v + c0v >= rem) {
+        s_dig = b0;
+        s_dig_above = above + c1v;
       }
+      __syncthreads();
+      const uint32_t d = (uint32_t)s_dig;
+      rem -= s_dig_above;
+      prefix |= (uint64_t)d << sh;
+      const bool whole_bucket = rhist[d] == rem;
+      __syncthreads();
+      if (whole_bucket) break;
     }
-    __syncthreads();
-    // ---- merge list[0, Ak) and list[Ak, kept) (both ascending) into orow
-    for (uint32_t i = tid; i < (uint32_t)k; i += kFinalThreads) {
-      if (i >= kept) {
-        orow[i] = -1;
-        continue;
-      }
-      const uint32_t x = list[i];
-      uint32_t lo, hi;  // lower bound of x in the other list
-      if (i < Ak) { lo = Ak; hi = kept; } else { lo = 0; hi = Ak; }
-      const uint32_t base = lo;
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (list[mid] < x) lo = mid + 1; else hi = mid;
-      }
-      const uint32_t pos = (i < Ak) ? i + (lo - base) : (i - Ak) + lo;
-      orow[pos] = sp ? sp[x] : (int32_t)x;
-    }
-    if (count_out && tid == 0) count_out[r] = (int32_t)kept;
+    thr = prefix;
   }
-  // ---- leave the histogram copies zero for the next call
-  uint4* h4 = reinterpret_cast<uint4*>(rh);
-  for (int j = tid; j < kHistCopies * kHistBins / 4; j += kFinalThreads) h4[j] = make_uint4(0, 0, 0, 0);
+  // ---- chosen candidates (rank value within b1 >= thr), kept in slot
+  // order: the concatenated candidate regions are slot-ordered.
+  const uint64_t low52 = (1ull << 52) - 1;
+  uint32_t kept;  // k unless the histogram disagreed with the scores
+  {
+    const uint32_t per_c = (C + NT - 1) / NT;
+    const uint32_t lo = min(tid * per_c, C), hi = min(lo + per_c, C);
+    uint32_t cnt = 0;
+    for (uint32_t c = lo; c < hi; ++c) {
+      const uint64_t x = in_lds ? cl[c] : cand_at(c);
+      cnt += (need > 0 && (x & low52) >= thr) ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t o = Ak + block_scan<NT>(cnt, tmp, &tot);
+    kept = Ak + min(tot, need);
+    for (uint32_t c = lo; c < hi; ++c) {
+      const uint64_t x = in_lds ? cl[c] : cand_at(c);
+      if (need > 0 && (x & low52) >= thr && o < kept) list[o++] = rank_slot(x);
+    }
+  }
+  __syncthreads();
+  // ---- merge list[0, Ak) and list[Ak, kept) (both ascending) into orow:
+  // an element's output slot is its index in its own list plus the number
+  // of smaller elements in the other (four searches in flight per thread)
+  {
+    const uint32_t nch = kept - Ak;
+    int topA = 1, topC = 1;
+    while (topA * 2 <= (int)Ak) topA *= 2;
+    while (topC * 2 <= (int)nch) topC *= 2;
+    const int topM = max(topA, topC);
+    for (uint32_t i0 = 0; i0 < (uint32_t)k; i0 += NT * 4) {
+      uint32_t x[4], cnt[4], lo[4], len[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * NT + tid;
+        const bool live = i < kept;
+        x[u] = live ? list[i] : 0u;
+        lo[u] = (i < Ak) ? Ak : 0u;        // the other list
+        len[u] = live ? ((i < Ak) ? nch : Ak) : 0u;
+        cnt[u] = 0;
+      }
+      for (int step = topM; step > 0; step >>= 1) {
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = list[lo[u] + min(cnt[u] + (uint32_t)step, max(len[u], 1u)) - 1];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t nx = cnt[u] + (uint32_t)step;
+          cnt[u] = (nx <= len[u] && v[u] < x[u]) ? nx : cnt[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * NT + tid;
+        if (i >= (uint32_t)k) continue;
+        if (i >= kept) {
+          orow[i] = -1;
+          continue;
+        }
+        const uint32_t pos = (i < Ak) ? i + cnt[u] : (i - Ak) + cnt[u];
+        orow[pos] = sp ? sp[x[u]] : (int32_t)x[u];
+      }
+    }
+  }
+  if (count_out && tid == 0) count_out[r] = (int32_t)kept;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
+    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t tmp[kSelWaves];
+  __shared__ uint32_t wtot[2][kSelWaves];  // kept / candidates per wave
+  __shared__ int s_b1, s_last;
+
+  const int r = blockIdx.y, nblk = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
+  const int64_t start = (int64_t)blockIdx.x * kTopkChunk;
+  const int64_t wstart = start + (int64_t)wave * kSlotsPerWave;
+  uint32_t* rh = w.hist + (int64_t)r * w.hist_stride;
+
+  if (nv > k) {
+    uint32_t* crow = w.counts + (int64_t)r * w.counts_stride + 2 * blockIdx.x;
+    if (start >= nv) {
+      if (tid == 0) {
+        st_coh(crow, 0u);
+        st_coh(crow + 1, 0u);
+      }
+    } else {
+      // this wave's scores: slots wstart + 64j + lane
+      const float* srow = scores + (int64_t)r * n;
+      float v[kPerLane];
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
+      // the row's histogram summed over its copies: bins [4t, 4t+4)
+      uint32_t h4[4] = {0u, 0u, 0u, 0u};
+      {
+        uint4 hc[kHistCopies];
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c)
+          hc[c] = *reinterpret_cast<const uint4*>(rh + c * kHistBins + 4 * tid);
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) {
+          h4[0] += hc[c].x;
+          h4[1] += hc[c].y;
+          h4[2] += hc[c].z;
+          h4[3] += hc[c].w;
+        }
+      }
+      if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
+      {
+        const uint32_t sum = h4[0] + h4[1] + h4[2] + h4[3];
+        uint32_t total;
+        const uint32_t excl = block_scan<kSelThreads>(sum, tmp, &total);
+        const uint32_t above = total - excl - sum;  // elements in bins of higher threads
+        if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
+          uint32_t acc = above;
+          bool found = false;
+#pragma unroll
+          for (int j = 3; j >= 0; --j) {
+            if (!found && acc + h4[j] >= (uint32_t)k) {
+              s_b1 = 4 * tid + j;
+              found = true;
+            }
+            acc += h4[j];
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t b1 = (uint32_t)s_b1;
+      // count pass: this wave's kept and candidate totals
+      uint32_t na = 0, ne = 0;
+      uint32_t keys[kPerLane];
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const int64_t s = wstart + 64 * j + lane;
+        keys[j] = score_key(v[j]);
+        const uint32_t bin = keys[j] >> kHistShift;
+        na += (uint32_t)__popcll(__ballot(s < nv && bin > b1));
+        ne += (uint32_t)__popcll(__ballot(s < nv && bin == b1));
+      }
+      if (lane == 0) {
+        wtot[0][wave] = na;
+        wtot[1][wave] = ne;
+      }
+      __syncthreads();
+      uint32_t oa = 0, oe = 0, ta = 0, te = 0;
+#pragma unroll
+      for (int x = 0; x < kSelWaves; ++x) {
+        const uint32_t a = wtot[0][x], c = wtot[1][x];
+        oa += (x < wave) ? a : 0u;
+        oe += (x < wave) ? c : 0u;
+        ta += a;
+        te += c;
+      }
+      // write pass, in slot order
+      uint32_t* ra = w.above + (int64_t)r * w.above_stride + (int64_t)blockIdx.x * kTopkChunk;
+      uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kTopkChunk;
+      const uint64_t lt = lanemask_lt();
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const int64_t s = wstart + 64 * j + lane;
+        const uint32_t bin = keys[j] >> kHistShift;
+        const bool ab = s < nv && bin > b1;
+        const bool eq = s < nv && bin == b1;
+        const uint64_t ma = __ballot(ab), me = __ballot(eq);
+        if (ab) st_coh(ra + oa + (uint32_t)__popcll(ma & lt), (uint32_t)s);
+        if (eq) st_coh(rc + oe + (uint32_t)__popcll(me & lt), rank_value(keys[j], (uint32_t)s));
+        oa += (uint32_t)__popcll(ma);
+        oe += (uint32_t)__popcll(me);
+      }
+      if (tid == 0) {
+        st_coh(crow, ta);
+        st_coh(crow + 1, te);
+      }
+    }
+  }
+  // ---- arrival; the row's last block completes it
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* ctr = w.ctr + (int64_t)r * w.ctr_stride;
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (uint32_t)nblk - 1u;
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, smem, tmp);
+  // ---- leave the histogram copies zero for the next call (every block of
+  // the row has read them)
+  uint4* h4p = reinterpret_cast<uint4*>(rh);
+  for (int j = tid; j < kHistCopies * kHistBins / 4; j += kSelThreads) h4p[j] = make_uint4(0, 0, 0, 0);
 }
 
 static int32_t topk_blocks(int64_t n_max) {
@@ -423,27 +514,25 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st) {
   const int32_t nblk = topk_blocks(n_max);
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(256), 0, st,
-                     scores, n, n_valid, nv_add, k, w.hist, w.hist_stride, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // final kernel: LDS = radix bins + 2 offset arrays + k list + candidates
+  // LDS of the completing block: radix bins + 2 offset arrays + k list +
+  // candidates.  A small budget for small k keeps two blocks per CU.
   const size_t fixed = (size_t)(2048 + 2 * (nblk + 1) + ((k + 1) & ~1)) * 4;
-  const size_t budget = 150 * 1024;
+  const size_t budget = (k <= 2048 && fixed <= 40 * 1024) ? 72 * 1024 : 150 * 1024;
   int32_t lds_cand = (int32_t)((budget - fixed) / 8);
   if (lds_cand > 16384) lds_cand = 16384;
   if (lds_cand < 0) lds_cand = 0;
   const size_t lds = fixed + (size_t)lds_cand * 8;
   static bool lds_raised = false;
   if (!lds_raised) {
-    e = hipFuncSetAttribute((const void*)topk_final_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)budget);
+    const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             150 * 1024);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kFinalThreads), lds, st, n,
-                     n_valid, nv_add, slot_pos, k, nblk, idx_out, count_out, w.hist, w.hist_stride,
-                     w, lds_cand);
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(kSelThreads),
+                     lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, w,
+                     lds_cand);
   return hipGetLastError();
 }
 
