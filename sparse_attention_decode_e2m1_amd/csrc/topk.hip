@@ -26,9 +26,10 @@
 //  3. The row's last block to arrive finishes it: it turns the counts into
 //     offsets, gathers the lists into LDS, resolves the remaining entries
 //     among the candidates by radix selection over the 64-bit rank values,
-//     keeps the chosen ones in position order, merges the two sorted lists
-//     by binary search and writes the output.  It then clears the histogram
-//     copies and the counter for the next call.
+//     and writes the kept slots in slot order -- read back from an LDS
+//     bitmap for rows up to 2^19 slots, else merged from the two sorted
+//     lists by binary search.  It then clears the histogram copies and the
+//     counter for the next call.
 // Every pass over memory issues all of a thread's loads before using them.
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
@@ -121,16 +122,22 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32
 
 // Completion of row r by its last block (all select blocks of the row have
 // written their regions and counts).
+// With bm_words > 0 the kept slots are marked in an LDS bitmap of bm_words
+// words (one bit per slot) and read back in slot order; otherwise they are
+// listed (kept outright, then chosen, each in slot order) and merged.
 __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
                            int32_t k, int nblk, int32_t* __restrict__ idx_out,
                            int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
-                           uint32_t* smem, uint32_t* tmp) {
+                           int32_t bm_words, uint32_t* smem, uint32_t* tmp) {
   constexpr int NT = kSelThreads;
+  const bool use_bm = bm_words > 0;
   uint32_t* rhist = smem;                      // 2048 radix bins
   uint32_t* offA = rhist + 2048;               // nblk + 1
   uint32_t* offE = offA + (nblk + 1);          // nblk + 1
-  uint32_t* list = offE + (nblk + 1);          // k: kept positions (above, then chosen)
-  uint64_t* cl = reinterpret_cast<uint64_t*>(list + ((k + 1) & ~1));  // lds_cand candidates
+  uint32_t* list = offE + (nblk + 1);          // k kept slots, or the bitmap
+  uint32_t* bm = list;
+  const int xwords = use_bm ? bm_words : k;
+  uint64_t* cl = reinterpret_cast<uint64_t*>(list + ((xwords + 1) & ~1));  // lds_cand candidates
   __shared__ int s_dig;
   __shared__ uint32_t s_dig_above;
   const int tid = threadIdx.x;
@@ -142,7 +149,12 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
     if (count_out && tid == 0) count_out[r] = (int32_t)nv;
     return;
   }
-  // ---- per-block counts -> offsets
+  if (use_bm) {
+    uint4* b4 = reinterpret_cast<uint4*>(bm);  // bm_words is a multiple of 4
+    for (int j = tid; j < bm_words / 4; j += NT) b4[j] = make_uint4(0, 0, 0, 0);
+  }
+  // ---- per-block counts -> offsets (the scans' barriers also order the
+  // bitmap clearing before its first use)
   const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
   constexpr int kMaxPer = (int)(kMaxTopkN / kTopkChunk / NT);  // blocks per thread
   static_assert(kMaxPer >= 1 && kMaxPer <= 8, "counts held in registers");
@@ -227,7 +239,10 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const uint32_t i = i0 + u * tpb;
-          if (i < na) list[a_lo + i] = ta[u];
+          if (i < na) {
+            if (use_bm) atomicOr(&bm[ta[u] >> 5], 1u << (ta[u] & 31));
+            else list[a_lo + i] = ta[u];
+          }
           if (i < ne) cl[e_lo + i] = tc[u];
         }
       }
@@ -297,9 +312,39 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
     }
     thr = prefix;
   }
+  const uint64_t low52 = (1ull << 52) - 1;
+  if (use_bm) {
+    // ---- chosen candidates into the bitmap, then every marked slot in
+    // slot order
+    if (need > 0) for_each([&](uint64_t x) {
+      if ((x & low52) >= thr) {
+        const uint32_t sl = rank_slot(x);
+        atomicOr(&bm[sl >> 5], 1u << (sl & 31));
+      }
+    });
+    __syncthreads();
+    const int wpt = (bm_words + NT - 1) / NT;
+    const int w0 = min(tid * wpt, bm_words), w1 = min(w0 + wpt, bm_words);
+    uint32_t cnt = 0;
+    for (int j = w0; j < w1; ++j) cnt += (uint32_t)__popc(bm[j]);
+    uint32_t tot;
+    uint32_t o = block_scan<NT>(cnt, tmp, &tot);
+    const uint32_t kept = min(tot, (uint32_t)k);
+    for (int j = w0; j < w1; ++j) {
+      uint32_t word = bm[j];
+      while (word) {
+        const uint32_t sl = 32u * (uint32_t)j + (uint32_t)(__ffs(word) - 1);
+        word &= word - 1u;
+        if (o < kept) orow[o] = sp ? sp[sl] : (int32_t)sl;
+        ++o;
+      }
+    }
+    for (uint32_t i = kept + tid; i < (uint32_t)k; i += NT) orow[i] = -1;
+    if (count_out && tid == 0) count_out[r] = (int32_t)kept;
+    return;
+  }
   // ---- chosen candidates (rank value within b1 >= thr), kept in slot
   // order: the concatenated candidate regions are slot-ordered.
-  const uint64_t low52 = (1ull << 52) - 1;
   uint32_t kept;  // k unless the histogram disagreed with the scores
   {
     const uint32_t per_c = (C + NT - 1) / NT;
@@ -367,7 +412,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand) {
+    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand, int32_t bm_words) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t tmp[kSelWaves];
   __shared__ uint32_t wtot[2][kSelWaves];  // kept / candidates per wave
@@ -487,7 +532,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, smem, tmp);
+  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, bm_words, smem, tmp);
   // ---- leave the histogram copies zero for the next call (every block of
   // the row has read them)
   uint4* h4p = reinterpret_cast<uint4*>(rh);
@@ -514,13 +559,15 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st) {
   const int32_t nblk = topk_blocks(n_max);
-  // LDS of the completing block: radix bins + 2 offset arrays + k list +
-  // candidates.  A small budget for small k keeps two blocks per CU.
-  const size_t fixed = (size_t)(2048 + 2 * (nblk + 1) + ((k + 1) & ~1)) * 4;
-  const size_t budget = (k <= 2048 && fixed <= 40 * 1024) ? 72 * 1024 : 150 * 1024;
-  int32_t lds_cand = (int32_t)((budget - fixed) / 8);
+  // LDS of the completing block: radix bins, 2 offset arrays, the kept-slot
+  // bitmap (rows up to kBitmapSlots) or list, then as many candidates as fit.
+  constexpr int64_t kBitmapSlots = int64_t(1) << 19;
+  constexpr size_t kBudget = 150 * 1024;
+  const int32_t bm_words = (n <= kBitmapSlots) ? (int32_t)(((n + 31) / 32 + 3) & ~3) : 0;
+  const int32_t xwords = bm_words > 0 ? bm_words : k;
+  const size_t fixed = (size_t)(2048 + 2 * (nblk + 1) + ((xwords + 1) & ~1)) * 4;
+  int32_t lds_cand = fixed < kBudget ? (int32_t)((kBudget - fixed) / 8) : 0;
   if (lds_cand > 16384) lds_cand = 16384;
-  if (lds_cand < 0) lds_cand = 0;
   const size_t lds = fixed + (size_t)lds_cand * 8;
   static bool lds_raised = false;
   if (!lds_raised) {
@@ -532,7 +579,7 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   }
   hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(kSelThreads),
                      lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, w,
-                     lds_cand);
+                     lds_cand, bm_words);
   return hipGetLastError();
 }
 
