@@ -15,6 +15,13 @@
 
 using namespace csa2;
 
+namespace csa2 {
+LaunchTiming& launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace csa2
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -64,20 +71,19 @@ struct Profiler {
 };
 Profiler g_prof;
 
-// Records an event before and after one launch when profiling is on.
+// While profiling is on, hands a start/stop event pair to the launcher of
+// one call; the launcher attaches them to its kernels, so the pair times the
+// kernels themselves.
 struct ProfScope {
   int id;
-  hipStream_t st;
-  hipEvent_t b = nullptr;
-  ProfScope(int id_, hipStream_t st_) : id(id_), st(st_) {
-    if (g_prof.on && (b = g_prof.get())) hipEventRecord(b, st);
+  hipEvent_t b = nullptr, e = nullptr;
+  ProfScope(int id_, hipStream_t) : id(id_) {
+    if (g_prof.on && (b = g_prof.get()) && (e = g_prof.get())) launch_timing() = {b, e, false, false};
   }
   ~ProfScope() {
-    if (!b) return;
-    hipEvent_t e = g_prof.get();
-    if (!e) return;
-    hipEventRecord(e, st);
-    g_prof.ev[id].push_back({b, e});
+    LaunchTiming& t = launch_timing();
+    if (b && e && t.started && t.stopped) g_prof.ev[id].push_back({b, e});
+    t = LaunchTiming{};
   }
 };
 

@@ -2,6 +2,7 @@
 // translation units of libcsa2.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -56,6 +57,27 @@ inline AttnSplit attn_split(int32_t K, int32_t W) {
   s.nsplit = s.nsg + s.nsw;
   return s;
 }
+
+// Launch timing: while the library profiles a call, its launchers attach
+// the call's start and stop events to the first and last kernel they launch
+// (the events then carry the kernels' own start and end times).
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool started = false, stopped = false;
+};
+LaunchTiming& launch_timing();
+#define CSA2_KERNEL(FIRST, LAST, kernel, grid, block, lds, st, ...)                           \
+  do {                                                                                      \
+    LaunchTiming& _lt = launch_timing();                                                    \
+    if (_lt.start) {                                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, (FIRST) ? _lt.start : nullptr,    \
+                            (LAST) ? _lt.stop : nullptr, 0, __VA_ARGS__);                   \
+      _lt.started |= (FIRST);                                                               \
+      _lt.stopped |= (LAST);                                                                \
+    } else {                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                        \
+    }                                                                                       \
+  } while (0)
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
                            const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,

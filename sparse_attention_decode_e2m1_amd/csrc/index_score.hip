@@ -213,7 +213,7 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   if (nchunks == 0 || rows == 0) return hipSuccess;
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
 #define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \
-  hipLaunchKernelGGL((index_score_kernel<NCH, TPA, GT>), grid, block, 0, st, codes, scales, cap, \
+  CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT>), grid, block, 0, st, codes, scales, cap, \
                      q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, hist,             \
                      hist_stride, chunk, row0)
   switch (DI / 128) {

@@ -14,7 +14,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   if (words == 0) return hipSuccess;
   int64_t blocks = (words + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p,
+  CSA2_KERNEL(true, true, fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p,
                      words);
   return hipGetLastError();
 }
@@ -51,7 +51,7 @@ hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* p
                                 const int32_t* count, int32_t rows, float* out, uint32_t* hist,
                                 int64_t hist_stride, hipStream_t st) {
   const dim3 grid((unsigned)((P + 4095) / 4096), (unsigned)rows), block(256);
-  hipLaunchKernelGGL(gather_scores_kernel, grid, block, 0, st, scores, n, pool, P, count, out, hist,
+  CSA2_KERNEL(true, true, gather_scores_kernel, grid, block, 0, st, scores, n, pool, P, count, out, hist,
                      hist_stride);
   return hipGetLastError();
 }

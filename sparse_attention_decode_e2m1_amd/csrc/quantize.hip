@@ -146,11 +146,11 @@ hipError_t launch_quantize_step(const void* x1, const void* x2, bool bf16, int32
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (bf16)
-    hipLaunchKernelGGL(quantize_step_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)x1,
+    CSA2_KERNEL(true, true, quantize_step_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)x1,
                        (const uint16_t*)x2, rows, T, q_pos, dim1, cap1, codes1, scales1, dim2,
                        cap2, codes2, scales2);
   else
-    hipLaunchKernelGGL(quantize_step_kernel<float>, grid, block, 0, st, (const float*)x1,
+    CSA2_KERNEL(true, true, quantize_step_kernel<float>, grid, block, 0, st, (const float*)x1,
                        (const float*)x2, rows, T, q_pos, dim1, cap1, codes1, scales1, dim2, cap2,
                        codes2, scales2);
   return hipGetLastError();
@@ -163,10 +163,10 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, 
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (bf16)
-    hipLaunchKernelGGL(quantize_kernel<uint16_t>, grid, block, 0, st,
+    CSA2_KERNEL(true, true, quantize_kernel<uint16_t>, grid, block, 0, st,
                        (const uint16_t*)x, rows, dim, stride, dst_rows, codes, scales);
   else
-    hipLaunchKernelGGL(quantize_kernel<float>, grid, block, 0, st, (const float*)x, rows, dim,
+    CSA2_KERNEL(true, true, quantize_kernel<float>, grid, block, 0, st, (const float*)x, rows, dim,
                        stride, dst_rows, codes, scales);
   return hipGetLastError();
 }

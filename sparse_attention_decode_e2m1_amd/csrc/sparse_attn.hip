@@ -479,18 +479,18 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   const bool fused = merge_lds_bytes(sp.nsplit) <= lds && w.cnt != nullptr &&
                      (int64_t)sp.nsplit * rows <= resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
   if (fused) {
-    hipLaunchKernelGGL((sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, q, T, codes,
+    CSA2_KERNEL(true, true, (sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, q, T, codes,
                        scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
                        sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, q, T, codes,
+  CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, q, T, codes,
                      scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
                      sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int NU = 16 * DV / 4;
-  hipLaunchKernelGGL((attn_combine_kernel<DV>), dim3((NU + 255) / 256, (unsigned)rows), dim3(256),
+  CSA2_KERNEL(false, true, (attn_combine_kernel<DV>), dim3((NU + 255) / 256, (unsigned)rows), dim3(256),
                      merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, out, lse);
   return hipGetLastError();
 }

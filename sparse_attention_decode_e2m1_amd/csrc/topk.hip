@@ -549,7 +549,7 @@ hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const 
                             hipStream_t st) {
   const int64_t nchunks = (n_max + kTopkChunk - 1) / kTopkChunk;
   if (nchunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(256), 0, st,
+  CSA2_KERNEL(true, true, topk_hist_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(256), 0, st,
                      scores, n, n_valid, nv_add, hist, hist_stride);
   return hipGetLastError();
 }
@@ -577,7 +577,7 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(kSelThreads),
+  CSA2_KERNEL(true, true, topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(kSelThreads),
                      lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, w,
                      lds_cand, bm_words);
   return hipGetLastError();
