@@ -63,6 +63,48 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     for (int k = tid; k < kHistBins; k += 256) lhist[k] = 0u;
   }
 
+  const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
+  const uint8_t* sbase = scales + (int64_t)b * cap * ROWS;
+  const int32_t* prow = pool ? pool + (int64_t)r * P : nullptr;
+  float* srow = scores + (int64_t)r * n_out;
+
+  // Each wave takes groups of GT consecutive tiles (GT KiB of contiguous
+  // codes for 128 channels in flat mode); the four waves of a round cover
+  // 4*GT consecutive tiles.  The next group's loads are issued before the
+  // current group is computed.
+  const int ntiles = (int)((end - start + 15) >> 4);
+  const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
+  auto row_of = [&](int tile) -> int64_t {
+    int64_t s = start + (int64_t)tile * 16 + i;
+    if (s >= end) s = end - 1;  // clamp: keep the load in bounds, masked later
+    return prow ? (int64_t)prow[s] : s;
+  };
+  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
+  // scales; they are fetched as the aligned 32-bit word holding them, so
+  // nothing has to wait for the loads until the group is computed.
+  auto load_group = [&](int rnd, u32x4 (&cw)[GT][NCH], uint32_t (&sw)[GT][NCH]) {
+    int64_t rows[GT];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) rows[t] = row_of((rnd * 4 + wave) * GT + t);
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        cw[t][c2] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(cbase + rows[t] * ROWB + 64 * c2 + 16 * g));
+        sw[t][c2] =
+            *reinterpret_cast<const uint32_t*>(sbase + rows[t] * ROWS + 8 * c2 + 4 * (g >> 1));
+      }
+    }
+  };
+  const int sshift = 16 * (g & 1);
+
+  u32x4 cw[GT][NCH], ncw[GT][NCH];
+  uint32_t sw[GT][NCH], nsw[GT][NCH];
+  // the first group is requested before the query is prepared, so the
+  // scan's first HBM round trip overlaps the query's
+  if (nrounds > 0) load_group(0, cw, sw);
+
   // ---- query fragments: MFMA row i holds head i % HG of tile slot i / HG
   const int hrow = i % HG, srow_slot = i / HG;
   f16x8 qv[TPA][NCH][4];
@@ -113,45 +155,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const bool owner = (g % GPS) == 0;
   if (hist) __syncthreads();
 
-  const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
-  const uint8_t* sbase = scales + (int64_t)b * cap * ROWS;
-  const int32_t* prow = pool ? pool + (int64_t)r * P : nullptr;
-  float* srow = scores + (int64_t)r * n_out;
-
-  // Each wave takes groups of GT consecutive tiles (GT KiB of contiguous
-  // codes for 128 channels in flat mode); the four waves of a round cover
-  // 4*GT consecutive tiles.  The next group's loads are issued before the
-  // current group is computed.
-  const int ntiles = (int)((end - start + 15) >> 4);
-  const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
-  auto row_of = [&](int tile) -> int64_t {
-    int64_t s = start + (int64_t)tile * 16 + i;
-    if (s >= end) s = end - 1;  // clamp: keep the load in bounds, masked later
-    return prow ? (int64_t)prow[s] : s;
-  };
-  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
-  // scales; they are fetched as the aligned 32-bit word holding them, so
-  // nothing has to wait for the loads until the group is computed.
-  auto load_group = [&](int rnd, u32x4 (&cw)[GT][NCH], uint32_t (&sw)[GT][NCH]) {
-    int64_t rows[GT];
-#pragma unroll
-    for (int t = 0; t < GT; ++t) rows[t] = row_of((rnd * 4 + wave) * GT + t);
-#pragma unroll
-    for (int t = 0; t < GT; ++t) {
-#pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        cw[t][c2] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(cbase + rows[t] * ROWB + 64 * c2 + 16 * g));
-        sw[t][c2] =
-            *reinterpret_cast<const uint32_t*>(sbase + rows[t] * ROWS + 8 * c2 + 4 * (g >> 1));
-      }
-    }
-  };
-  const int sshift = 16 * (g & 1);
-
-  u32x4 cw[GT][NCH], ncw[GT][NCH];
-  uint32_t sw[GT][NCH], nsw[GT][NCH];
-  if (nrounds > 0) load_group(0, cw, sw);
   for (int rnd = 0; rnd < nrounds; ++rnd) {
     if (rnd + 1 < nrounds) load_group(rnd + 1, ncw, nsw);
 #pragma unroll

@@ -39,40 +39,52 @@ constexpr int kSpinLimit = 1 << 20;
 // Partials that another block of the same launch reads go through the
 // device-coherent path (agent-scope accesses: written through to, and read
 // from, the level all XCDs share) instead of full L2 write-back and
-// invalidate fences.
+// invalidate fences.  Values travel in pairs (64-bit accesses).
 template <bool COH>
-__device__ __forceinline__ void st_part(float* p, float v) {
-  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
+__device__ __forceinline__ void st_pair(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  if constexpr (COH)
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *reinterpret_cast<uint64_t*>(p) = v;
 }
 template <bool COH>
-__device__ __forceinline__ float ld_part(const float* p) {
+__device__ __forceinline__ float2 ld_pair(const float* p) {
+  uint64_t v;
   if constexpr (COH)
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
   else
-    return *p;
-}
-template <bool COH>
-__device__ __forceinline__ float4 ld_part4(const float* p) {
-  if constexpr (COH)
-    return make_float4(ld_part<true>(p), ld_part<true>(p + 1), ld_part<true>(p + 2),
-                       ld_part<true>(p + 3));
-  else
-    return *reinterpret_cast<const float4*>(p);
+    v = *reinterpret_cast<const uint64_t*>(p);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
-// Merge of the splits of one query row into output units [u0, u1) (a unit
-// is four channels of one head); `ml` is LDS for nsplit x 32 floats plus 256
-// float4.  All threads of the block call it.  The partial outputs a thread
-// needs are requested before the split maxima are reduced, so the merge
-// costs about two memory round trips.
+// Layout of a split's partial output for one head: wave w, lane column i and
+// output tile nt of P.V hold value channel w*dv/4 + 16*nt + i, stored at
+// w*dv/4 + 32*(nt/2) + 2*i + nt%2, so a lane writes tiles nt, nt+1 as one
+// pair and the 16 lanes of a row write 128 contiguous bytes.  Slot p of a
+// head row therefore holds channel:
+template <int DV>
+__device__ __forceinline__ int partial_channel(int p) {
+  constexpr int CPW = DV / 4;
+  const int w = p / CPW, rem = p % CPW;
+  return w * CPW + (2 * (rem / 32) + (rem & 1)) * 16 + (rem % 32) / 2;
+}
+
+// Merge of the splits of one query row into output units [u0, u1): unit u is
+// the slot pair (2(u % (dv/2)), +1) of head u / (dv/2).  `ml` is LDS for
+// nsplit x 32 floats plus 256 float2.  All threads of the block call it.
+// The split maxima/sums and the partial outputs a thread needs are all
+// requested before any is used, so the merge costs about one memory round
+// trip plus the reduction of the maxima.
 template <int DV, bool COH>
 __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, int u1,
                             float* __restrict__ orow, float* __restrict__ lrow, bool write_lse,
                             bool ok, float* ml) {
   constexpr int PSTRIDE = 16 * DV + 32;
-  constexpr int UPH = DV / 4;  // units per head
-  constexpr int KB = 16;       // partial loads in flight per thread
+  constexpr int UPH = DV / 2;  // units per head
+  constexpr int NU = 16 * UPH;
+  constexpr int KB = 20;       // partial loads in flight per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_M[16], s_L[16];
   __shared__ float red[4][16];
@@ -80,40 +92,42 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
   int SUB = 1;  // threads per unit
   while (SUB < 64 && SUB * 2 * nu <= 256) SUB *= 2;
   const int per_pass = 256 / SUB;
-  float4* racc = reinterpret_cast<float4*>(ml + nsplit * 32);
-  constexpr int NU = 16 * DV / 4;
+  float2* racc = reinterpret_cast<float2*>(ml + nsplit * 32);
   const int nml = nsplit * 32;
   for (int ub = 0; ub == 0 || ub < nu; ub += per_pass) {
     const int uu = ub + tid / SUB, sub = tid % SUB;
     const bool live = uu < nu;
     const int u = min(u0 + uu, NU - 1);  // clamped: every load below stays in bounds
-    const int h = u / UPH, c4 = u % UPH;
-    const float* col = prow + h * DV + 4 * c4;
-    // Split maxima and sums first (ml[s][0..15] = m, ml[s][16..31] = l), then
-    // this thread's partial outputs; indices are clamped rather than
-    // branched on, so every load is requested before any is used.
-    float mlv[8];
+    const int h = u / UPH, pp = 2 * (u % UPH);
+    const float* col = prow + h * DV + pp;
+    // Split maxima and sums (ml[s][0..15] = m, ml[s][16..31] = l) and this
+    // thread's partial outputs; indices are clamped rather than branched on.
+    const int nmp = nml / 2;  // pairs
+    float2 mlv[4];
     if (ub == 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = min(k * 256 + tid, nml - 1);
-        mlv[k] = ld_part<COH>(prow + (int64_t)(j >> 5) * PSTRIDE + 16 * DV + (j & 31));
+      for (int k = 0; k < 4; ++k) {
+        const int jp = min(k * 256 + tid, nmp - 1);
+        mlv[k] = ld_pair<COH>(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
       }
     }
-    float4 v[KB];
+    float2 v[KB];
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int s = min(sub + k * SUB, nsplit - 1);
-      v[k] = ld_part4<COH>(col + (int64_t)s * PSTRIDE);
-    }
+    for (int k = 0; k < KB; ++k) v[k] = ld_pair<COH>(col + (int64_t)min(sub + k * SUB, nsplit - 1) * PSTRIDE);
     if (ub == 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = k * 256 + tid;
-        if (j < nml) ml[j] = mlv[k];
+      for (int k = 0; k < 4; ++k) {
+        const int jp = k * 256 + tid;
+        if (jp < nmp) {
+          ml[2 * jp] = mlv[k].x;
+          ml[2 * jp + 1] = mlv[k].y;
+        }
       }
-      for (int j = 8 * 256 + tid; j < nml; j += 256)  // beyond 64 splits
-        ml[j] = ld_part<COH>(prow + (int64_t)(j >> 5) * PSTRIDE + 16 * DV + (j & 31));
+      for (int jp = 4 * 256 + tid; jp < nmp; jp += 256) {  // beyond 64 splits
+        const float2 t = ld_pair<COH>(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
+        ml[2 * jp] = t.x;
+        ml[2 * jp + 1] = t.y;
+      }
       __syncthreads();
       // per head hh: max and weighted sum over splits; lanes hh of the four
       // 16-lane rows of the four waves take every 16th split
@@ -147,46 +161,40 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
         lrow[tid] = !ok ? __int_as_float(0x7FC00000) : (Lt > 0.0f) ? s_M[tid] + logf(Lt) : -INFINITY;
       }
     }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int s = sub + k * SUB;
       const float wv = (live && s < nsplit) ? ml[s * 32 + h] : 0.0f;
       acc.x += wv * v[k].x;
       acc.y += wv * v[k].y;
-      acc.z += wv * v[k].z;
-      acc.w += wv * v[k].w;
     }
     // splits beyond the first KB per thread
     for (int s0 = sub + KB * SUB; live && s0 < nsplit; s0 += KB * SUB) {
 #pragma unroll
-      for (int k = 0; k < KB; ++k) v[k] = ld_part4<COH>(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
+      for (int k = 0; k < KB; ++k) v[k] = ld_pair<COH>(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
         const int s = s0 + k * SUB;
         const float wv = (s < nsplit) ? ml[s * 32 + h] : 0.0f;
         acc.x += wv * v[k].x;
         acc.y += wv * v[k].y;
-        acc.z += wv * v[k].z;
-        acc.w += wv * v[k].w;
       }
     }
     racc[tid] = acc;
     __syncthreads();
     if (live && sub == 0) {
-      float4 t = acc;
+      float2 t = acc;
       for (int k = 1; k < SUB; ++k) {
-        const float4 o = racc[tid + k];
+        const float2 o = racc[tid + k];
         t.x += o.x;
         t.y += o.y;
-        t.z += o.z;
-        t.w += o.w;
       }
       const float L = s_L[h];
       const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-      float4 res = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-      if (!ok) res = make_float4(NAN, NAN, NAN, NAN);
-      *reinterpret_cast<float4*>(orow + h * DV + 4 * c4) = res;
+      const int ch = partial_channel<DV>(pp);  // slot pp + 1 holds channel ch + 16
+      orow[h * DV + ch] = ok ? t.x * inv : NAN;
+      orow[h * DV + ch + 16] = ok ? t.y * inv : NAN;
     }
     __syncthreads();
   }
@@ -362,18 +370,26 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   // ---- partial result of this split: o[16][DV], m[16], l[16]
   float* prow = part + (int64_t)r * nsplit * PSTRIDE;
   float* pb = prow + (int64_t)sidx * PSTRIDE;
+  static_assert(NT % 2 == 0, "tiles stored in pairs");
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NT; nt += 2)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      st_part<FUSED>(pb + (4 * g + rr) * DV + wave * CPW + nt * 16 + i, o[nt][rr] * wscale);
-  if (wave == 0 && i == 0) {
+      st_pair<FUSED>(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
+                     o[nt + 1][rr] * wscale);
+  if (wave == 0 && i < 8) {
+    // m of heads 2i, 2i+1 and l of heads 2i, 2i+1 (lanes i < 8 of each g
+    // hold the four heads 4g + rr; lanes with g == 0 write for all)
+    if (g == 0) {
+      float mm[2], ll[2];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      st_part<FUSED>(pb + 16 * DV + h, mh[rr]);
-      st_part<FUSED>(pb + 16 * DV + 16 + h,
-                     red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
+      for (int k = 0; k < 2; ++k) {
+        const int h = 2 * i + k;
+        mm[k] = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
+        ll[k] = red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h];
+      }
+      st_pair<FUSED>(pb + 16 * DV + 2 * i, mm[0], mm[1]);
+      st_pair<FUSED>(pb + 16 * DV + 16 + 2 * i, ll[0], ll[1]);
     }
   }
   if constexpr (FUSED) {
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     __syncthreads();
     const bool ok = s_ok != 0;
     // this block's slice of the row's output units
-    constexpr int NU = 16 * DV / 4;
+    constexpr int NU = 16 * DV / 2;
     const int per = (NU + nsplit - 1) / nsplit;
     const int u0 = min(sidx * per, NU), u1 = min(u0 + per, NU);
     merge_slice<DV, true>(prow, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            float* __restrict__ lse) {
   extern __shared__ float ml[];
   constexpr int PSTRIDE = 16 * DV + 32;
-  constexpr int NU = 16 * DV / 4;
+  constexpr int NU = 16 * DV / 2;
   const int r = blockIdx.y;
   const int u0 = blockIdx.x * 256, u1 = min(u0 + 256, NU);
   merge_slice<DV, false>(part + (int64_t)r * nsplit * PSTRIDE, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
@@ -434,7 +450,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 size_t attn_lds_bytes(int32_t dv) { return (size_t)64 * (dv + 8) * sizeof(_Float16); }
 
 static size_t merge_lds_bytes(int32_t nsplit) {
-  return (size_t)nsplit * 32 * sizeof(float) + 256 * sizeof(float4);
+  return (size_t)nsplit * 32 * sizeof(float) + 256 * sizeof(float2);
 }
 
 // Blocks of the fused kernel that fit on the device at once.
@@ -489,7 +505,7 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
                      sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NU = 16 * DV / 4;
+  constexpr int NU = 16 * DV / 2;
   CSA2_KERNEL(false, true, (attn_combine_kernel<DV>), dim3((NU + 255) / 256, (unsigned)rows), dim3(256),
                      merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, out, lse);
   return hipGetLastError();
