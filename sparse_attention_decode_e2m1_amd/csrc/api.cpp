@@ -125,6 +125,10 @@ void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
     tw->hist_stride = kCtlWordsPerRow;
     tw->ctr = ctl ? ctl + kHistWords + 2 : nullptr;
     tw->ctr_stride = kCtlWordsPerRow;
+    tw->cut = ctl ? ctl + kHistWords + 3 : nullptr;
+    // Copies spread the histogram atomics of a row's many scoring blocks;
+    // with many rows per pass one copy keeps the select pass's reads small.
+    tw->hist_copies = rows <= 32 ? kMaxHistCopies : 1;
   }
   if (aw) {
     aw->cnt = ctl ? ctl + kHistWords : nullptr;
@@ -270,7 +274,7 @@ csa2_status csa2_index_score(const csa2_fp4_cache* icache, int32_t B, int32_t T,
   const int64_t n_max = pool ? std::min<int64_t>(P, n_out) : std::min<int64_t>(icache->cap, n_out);
   CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(icache->codes, icache->scales, icache->dim, icache->cap, B * T, T,
                               q_idx, w, H_I, n_valid, 0, pool, pool ? P : 0, n_max, scores, n_out,
-                              nullptr, 0, as_stream(stream)),
+                              nullptr, 0, 1, as_stream(stream)),
            "index score launch");
   return CSA2_OK;
 }
@@ -308,7 +312,7 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
     const float* sc = scores + (size_t)r0 * n;
     const int32_t* nv = n_valid + r0;
     const int32_t* sp = slot_pos ? slot_pos + (size_t)r0 * n : nullptr;
-    CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(sc, nr, n, nv, 0, n, tw.hist, tw.hist_stride, st),
+    CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(sc, nr, n, nv, 0, n, tw.hist, tw.hist_stride, tw.hist_copies, st),
                 "top-k histogram launch");
     CSA2_LAUNCH(2, PROF_STREAM,
                 launch_topk_select(sc, nr, n, nv, 0, n, sp, k, idx_out + (size_t)r0 * k,
@@ -498,7 +502,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       const int64_t n_max = pooled_in ? a->P_in : a->icache.cap;
       CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
                                   qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
-                                  L.scores, L.n_out, L.tw.hist, L.tw.hist_stride, st, r0),
+                                  L.scores, L.n_out, L.tw.hist, L.tw.hist_stride, L.tw.hist_copies,
+                                  st, r0),
                "index score launch");
       int32_t* idx = a->idx_out + (size_t)r0 * a->K;
       if (mode == CSA2_MODE_FULL && a->P > 0) {
@@ -508,7 +513,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
                                     pcount, L.tw, st),
                  "pool select launch");
         CSA2_LAUNCH(4, PROF_STREAM, launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
-                                      L.tw.hist, L.tw.hist_stride, st),
+                                      L.tw.hist, L.tw.hist_stride, L.tw.hist_copies, st),
                  "pool gather launch");
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
                                     nullptr, L.tw, st),

@@ -18,7 +18,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kHistBins = 4096;       // top 12 bits of the ordered score key
 constexpr int kHistShift = 20;
-// Copies of each row's histogram; block b adds into copy b % kHistCopies.
+// Most copies of each row's histogram; block b adds into copy b % copies.
 // Device-scope atomics on one address serialise (about 11 ns each on
 // MI355X), so the merge of many blocks is spread over the copies.
 constexpr int kHistCopies = 8;

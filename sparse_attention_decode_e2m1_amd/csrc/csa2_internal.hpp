@@ -20,8 +20,10 @@ constexpr int64_t kMaxTopkN = int64_t(1) << 25;  // longest score row Top-K acce
 // copies, then the attention merge counters -- in one fixed-size block at the start of the workspace.  They are
 // zero between calls, so any workspace left by a previous call (of any kind
 // or shape) is ready for the next.
-constexpr int64_t kHistWords = int64_t(8) * 4096;  // kHistCopies x kHistBins
-// + attention arrival / leave counters (words 0, 1) and the Top-K arrival counter (word 2)
+constexpr int kMaxHistCopies = 8;
+constexpr int64_t kHistWords = int64_t(kMaxHistCopies) * 4096;  // copies x 4096 bins
+// + attention arrival / leave counters (words 0, 1), the Top-K arrival counter (word 2) and
+// the Top-K cut bin (word 3)
 constexpr int64_t kCtlWordsPerRow = kHistWords + 64;
 
 struct TopkWs {
@@ -38,6 +40,8 @@ struct TopkWs {
   int64_t counts_stride;
   uint32_t* ctr;         // row r at ctr + r * ctr_stride: select blocks arrived (zero between calls)
   int64_t ctr_stride;
+  uint32_t* cut;         // row r at cut + r * ctr_stride: the cut bin, when precomputed
+  int32_t hist_copies;   // histogram copies in use (1 .. kHistCopies)
 };
 
 struct AttnWs {
@@ -49,11 +53,12 @@ struct AttnWs {
 struct AttnSplit {
   int32_t nsg, nsw, nsplit;  // splits of global entries, of window entries, total
 };
-inline AttnSplit attn_split(int32_t K, int32_t W) {
+inline AttnSplit attn_split(int32_t K, int32_t W, int32_t rounds = 1) {
   AttnSplit s;
-  s.nsg = (K + kAttnSplit - 1) / kAttnSplit;
+  const int32_t span = kAttnSplit * rounds;  // entries per split
+  s.nsg = (K + span - 1) / span;
   if (s.nsg < 1) s.nsg = 1;  // one split still writes the empty result
-  s.nsw = (W + kAttnSplit - 1) / kAttnSplit;
+  s.nsw = (W + span - 1) / span;
   s.nsplit = s.nsg + s.nsw;
   return s;
 }
@@ -87,10 +92,10 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
                               const float* w, int32_t HI, const int32_t* n_valid,
                               int32_t nv_add, const int32_t* pool, int32_t P, int64_t n_max,
                               float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
-                              hipStream_t st, int32_t row0 = 0);
+                              int32_t hist_copies, hipStream_t st, int32_t row0 = 0);
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
-                            hipStream_t st);
+                            int32_t hist_copies, hipStream_t st, bool first = true);
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
@@ -106,7 +111,8 @@ size_t attn_lds_bytes(int32_t dv);
 // those scores into hist (row stride hist_stride).
 hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* pool, int32_t P,
                                 const int32_t* count, int32_t rows, float* out,
-                                uint32_t* hist, int64_t hist_stride, hipStream_t st);
+                                uint32_t* hist, int64_t hist_stride, int32_t hist_copies,
+                                hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // Quantize-on-write of one decode/prefill step: rows r of x1 (dim1) and x2
 // (dim2) go to cache row (r / T) * cap + q_pos[r] of their planes.

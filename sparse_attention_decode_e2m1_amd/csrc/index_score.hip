@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
     const int32_t* __restrict__ n_valid, const int32_t* __restrict__ pool, int32_t P,
     int32_t nv_add, float* __restrict__ scores, int64_t n_out, uint32_t* __restrict__ hist,
-    int64_t hist_stride, int32_t chunk, int32_t row0) {
+    int64_t hist_stride, int32_t hist_copies, int32_t chunk, int32_t row0) {
   constexpr int DI = 128 * NCH;
   constexpr int ROWB = DI / 2;    // code bytes per row
   constexpr int ROWS = DI / 16;   // scale bytes per row
@@ -197,10 +197,156 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   }
   if (hist) {
     __syncthreads();
-    uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
+    uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
     for (int k = tid; k < kHistBins; k += 256) {
       const uint32_t c = lhist[k];
       if (c) atomicAdd(gh + k, c);
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------- prefill
+// Many query tokens of one sequence score the same positions, so the scan
+// becomes a tokens x positions contraction: MFMA rows = 4 tokens x 4 heads,
+// columns = 16 positions, k = channels.  A wave holds the query fragments of
+// 32 tokens (8 row groups) in registers and dequantizes each key tile once
+// for all of them: 32 MFMAs per 16-position tile.  Lane (i, g) of row group
+// j then holds the four heads of token 4j + g at position i, so the score
+// needs no cross-lane sum.  Token t sees positions below n_valid[t] + nv_add.
+template <int NCH>
+__global__ __launch_bounds__(256) void index_score_tokens_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
+    const int32_t* __restrict__ n_valid, int32_t nv_add, int32_t rows, float* __restrict__ scores,
+    int64_t n_out, int32_t chunk, int32_t row0) {
+  constexpr int DI = 128 * NCH;
+  constexpr int ROWB = DI / 2;
+  constexpr int ROWS = DI / 16;
+  constexpr int NG = 8;  // row groups of 4 tokens per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int rbase = blockIdx.y * 128 + wave * 32;  // first token row of this wave
+  if (rbase >= rows) return;                       // no block-wide barrier below
+  const int b = (row0 + rbase) / T;                // all 32 tokens share the sequence
+  // visible lengths: nvt[j] for token 4j + g (the epilogue's token), and the
+  // wave's longest
+  int64_t nvt[NG];
+  int64_t nvmax;
+  {
+    const int tr = min(rbase + (lane & 31), rows - 1);
+    int64_t v = min(min((int64_t)n_valid[tr] + nv_add, n_out), cap);
+    int64_t m = v;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) m = max(m, (int64_t)__shfl_xor(m, d, kWave));
+    nvmax = m;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int t = rbase + 4 * j + g;
+      nvt[j] = (t < rows) ? (int64_t)__shfl(v, 4 * j + g, kWave) : 0;
+    }
+  }
+  const int64_t start = (int64_t)blockIdx.x * chunk;
+  if (start >= nvmax) return;
+  const int64_t end = min(nvmax, start + chunk);
+
+  // query fragments: row i of group j = token 4j + i/4, head i%4
+  f16x8 qv[NG][NCH][4];
+  float wq[NG][4];
+  {
+    const int h = i & 3;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int t = min(rbase + 4 * j + (i >> 2), rows - 1);
+      const bool live = h < HI;
+      const uint16_t* qr = q_idx + ((int64_t)t * HI + (live ? h : 0)) * DI;
+      float vals[NCH][4][8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(qr + 128 * c2 + 32 * g + 8 * kk);
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            vals[c2][kk][2 * x] = bf16_to_f32(wd[x] & 0xFFFFu);
+            vals[c2][kk][2 * x + 1] = bf16_to_f32(wd[x] >> 16);
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(vals[c2][kk][x]));
+        }
+      amax = fmaxf(amax, shfl_xor(amax, 16));
+      amax = fmaxf(amax, shfl_xor(amax, 32));
+      const int qexp = fp16_exponent_for(amax);
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            qv[j][c2][kk][x] = live ? (_Float16)ldexpf(vals[c2][kk][x], qexp) : (_Float16)0.0f;
+      // epilogue weights of token 4j + g, heads rr (exponent from lane 4g + rr)
+      const int te = min(rbase + 4 * j + g, rows - 1);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int e = __shfl(qexp, 4 * g + rr, kWave);
+        wq[j][rr] = (rr < HI) ? ldexpf(w[(int64_t)te * HI + rr], -e) : 0.0f;
+      }
+    }
+  }
+
+  const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
+  const uint8_t* sbase = scales + (int64_t)b * cap * ROWS;
+  const int sshift = 16 * (g & 1);
+  const int ntiles = (int)((end - start + 15) >> 4);
+  auto load_tile = [&](int tile, u32x4 (&cw)[NCH], uint32_t (&sw)[NCH]) {
+    int64_t s = start + (int64_t)tile * 16 + i;
+    if (s >= end) s = end - 1;
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; ++c2) {
+      cw[c2] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(cbase + s * ROWB + 64 * c2 + 16 * g));
+      sw[c2] = *reinterpret_cast<const uint32_t*>(sbase + s * ROWS + 8 * c2 + 4 * (g >> 1));
+    }
+  };
+  // a ring of PF tiles in flight ahead of the one being computed
+  constexpr int PF = 4;
+  u32x4 cw[PF][NCH];
+  uint32_t sw[PF][NCH];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_tile(min(p, max(ntiles - 1, 0)), cw[p], sw[p]);
+  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int tile = t0 + p;
+      if (tile >= ntiles) break;
+      f16x8 kb[NCH][4];
+#pragma unroll
+      for (int c2 = 0; c2 < NCH; ++c2) {
+        const uint32_t s2b = sw[p][c2] >> sshift;
+        const f16x2 s_lo = scale_pair(s2b & 0xFFu);
+        const f16x2 s_hi = scale_pair((s2b >> 8) & 0xFFu);
+        kb[c2][0] = fp4x8_to_f16(cw[p][c2].x, s_lo);
+        kb[c2][1] = fp4x8_to_f16(cw[p][c2].y, s_lo);
+        kb[c2][2] = fp4x8_to_f16(cw[p][c2].z, s_hi);
+        kb[c2][3] = fp4x8_to_f16(cw[p][c2].w, s_hi);
+      }
+      // refill this ring slot with the tile PF ahead (clamped in range)
+      load_tile(min(tile + PF, ntiles - 1), cw[p], sw[p]);
+      const int64_t s = start + (int64_t)tile * 16 + i;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(qv[j][c2][kk], kb[c2][kk], acc);
+        float part = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) part += wq[j][rr] * fmaxf(acc[rr], 0.0f);
+        if (s < nvt[j]) scores[(int64_t)(rbase + 4 * j + g) * n_out + s] = part;
+      }
     }
   }
 }
@@ -210,15 +356,28 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
                               const float* w, int32_t HI, const int32_t* n_valid,
                               int32_t nv_add, const int32_t* pool, int32_t P, int64_t n_max,
                               float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
-                              hipStream_t st, int32_t row0) {
+                              int32_t hist_copies, hipStream_t st, int32_t row0) {
+  if (n_max <= 0 || rows == 0) return hipSuccess;
+  // Prefill chunks (32 or more tokens per sequence, whole waves of one
+  // sequence, 128-channel keys) take the tokens x positions kernel; the Top-K histogram is then
+  // built from the written scores.
+  if (!pool && HI <= 4 && T >= 32 && T % 32 == 0 && row0 % 32 == 0 && DI == 128) {
+    const int32_t pchunk = 1024;
+    const dim3 g2((unsigned)((n_max + pchunk - 1) / pchunk), (unsigned)((rows + 127) / 128));
+    CSA2_KERNEL(true, !hist, (index_score_tokens_kernel<1>), g2, dim3(256), 0, st, codes, scales,
+                cap, q_idx, w, HI, T, n_valid, nv_add, rows, scores, n_out, pchunk, row0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !hist) return e;
+    return launch_topk_hist(scores, rows, n_out, n_valid, nv_add, n_max, hist, hist_stride,
+                            hist_copies, st, false);
+  }
   const int32_t chunk = kScoreChunk;
   const int64_t nchunks = (n_max + chunk - 1) / chunk;
-  if (nchunks == 0 || rows == 0) return hipSuccess;
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
 #define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \
   CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT>), grid, block, 0, st, codes, scales, cap, \
                      q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, hist,             \
-                     hist_stride, chunk, row0)
+                     hist_stride, hist_copies, chunk, row0)
   switch (DI / 128) {
     case 1:
       if (HI <= 4) CSA2_IS_LAUNCH(1, 4, 8);

@@ -24,7 +24,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 __global__ __launch_bounds__(256) void gather_scores_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ pool, int32_t P,
     const int32_t* __restrict__ count, float* __restrict__ out, uint32_t* __restrict__ hist,
-    int64_t hist_stride) {
+    int64_t hist_stride, int32_t hist_copies) {
   __shared__ uint32_t lhist[kHistBins];
   const int r = blockIdx.y;
   const int32_t c = min(count[r], P);
@@ -36,23 +36,33 @@ __global__ __launch_bounds__(256) void gather_scores_kernel(
   const float* srow = scores + (int64_t)r * n;
   const int32_t* prow = pool + (int64_t)r * P;
   float* orow = out + (int64_t)r * P;
-  for (int32_t s = start + threadIdx.x; s < end; s += 256) {
-    const float v = srow[prow[s]];
-    orow[s] = v;
-    atomicAdd(&lhist[score_key(v) >> kHistShift], 1u);
+  // 16 slots per thread, indices then scores all requested before use
+  int32_t sl[16];
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) sl[u] = prow[min(start + u * 256 + (int32_t)threadIdx.x, end - 1)];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) v[u] = srow[sl[u]];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int32_t s = start + u * 256 + threadIdx.x;
+    if (s < end) {
+      orow[s] = v[u];
+      atomicAdd(&lhist[score_key(v[u]) >> kHistShift], 1u);
+    }
   }
   __syncthreads();
-  uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
+  uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
   for (int k = threadIdx.x; k < kHistBins; k += 256)
     if (lhist[k]) atomicAdd(gh + k, lhist[k]);
 }
 
 hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* pool, int32_t P,
                                 const int32_t* count, int32_t rows, float* out, uint32_t* hist,
-                                int64_t hist_stride, hipStream_t st) {
+                                int64_t hist_stride, int32_t hist_copies, hipStream_t st) {
   const dim3 grid((unsigned)((P + 4095) / 4096), (unsigned)rows), block(256);
   CSA2_KERNEL(true, true, gather_scores_kernel, grid, block, 0, st, scores, n, pool, P, count, out, hist,
-                     hist_stride);
+              hist_stride, hist_copies);
   return hipGetLastError();
 }
 

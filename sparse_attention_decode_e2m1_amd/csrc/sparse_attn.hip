@@ -206,8 +206,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     const uint8_t* __restrict__ scales, int64_t cap, const int32_t* __restrict__ idx, int32_t K,
     const uint8_t* __restrict__ swa, const float* __restrict__ swa_scale,
     const int32_t* __restrict__ swa_pos0, int32_t S, int32_t W, const int32_t* __restrict__ q_pos,
-    float sm_scale, float* __restrict__ part, int32_t nsg, int32_t nsplit, int32_t row0,
-    float* __restrict__ out, float* __restrict__ lse, uint32_t* __restrict__ cnt,
+    float sm_scale, float* __restrict__ part, int32_t nsg, int32_t nsplit, int32_t rounds,
+    int32_t row0, float* __restrict__ out, float* __restrict__ lse, uint32_t* __restrict__ cnt,
     int64_t cnt_stride) {
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   constexpr int NT = CPW / 16;      // P.V output tiles per wave
   constexpr int PSTRIDE = 16 * DV + 32;
   extern __shared__ _Float16 Vs[];  // [64 entries][VST]; the merge reuses it
-  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the split]
+  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
   __shared__ float red_max[4][16];
   __shared__ float red_sum[4][16];
 
@@ -224,11 +224,19 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const bool is_win = sidx >= nsg;
-  const int e = (is_win ? sidx - nsg : sidx) * 64 + wave * 16 + i;  // entry of this lane
+  // entry of this lane in round rnd: e0 + 64 * rnd
+  const int e0 = (is_win ? sidx - nsg : sidx) * 64 * rounds + wave * 16 + i;
+  int nw = 0, wlo = 0, pos0 = 0;
+  if (is_win) {
+    const int p = q_pos[r];
+    pos0 = swa_pos0[b];
+    wlo = max(p - W + 1, pos0);
+    nw = max(0, min(p, pos0 + S - 1) - wlo + 1);
+  }
 
   // ---- loads, in dependency order: the index, then the query, then the row
-  int ix = -1;
-  if (!is_win && e < K) ix = idx[(int64_t)r * K + e];
+  auto load_ix = [&](int e) -> int { return (!is_win && e < K) ? idx[(int64_t)r * K + e] : -1; };
+  int ix = load_ix(e0);
   uint32_t rq[NM][8];
   {
     const uint16_t* qr = q + ((int64_t)r * 16 + i) * D;
@@ -242,36 +250,34 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   }
   uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
   bool valid;
-  if (!is_win) {
-    valid = ix >= 0 && ix < cap;
-    const int64_t row = (int64_t)b * cap + (valid ? ix : 0);
-    const uint8_t* cr = codes + row * (D / 2);
-    const uint8_t* sr = scales + row * (D / 16);
+  auto load_row = [&](int e) {
+    if (!is_win) {
+      valid = ix >= 0 && ix < cap;
+      const int64_t row = (int64_t)b * cap + (valid ? ix : 0);
+      const uint8_t* cr = codes + row * (D / 2);
+      const uint8_t* sr = scales + row * (D / 16);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
-      w0[m] = cw.x;
-      w1[m] = cw.y;
-      sc[m] = sr[4 * m + g];
-    }
-  } else {
-    const int p = q_pos[r];
-    const int pos0 = swa_pos0[b];
-    const int wlo = max(p - W + 1, pos0);
-    const int whi = min(p, pos0 + S - 1);
-    const int nw = max(0, whi - wlo + 1);
-    valid = e < nw;
-    const int64_t row = (int64_t)b * S + (valid ? (wlo - pos0 + e) : 0);
-    const uint8_t* wr = swa + row * D;
+      for (int m = 0; m < NM; ++m) {
+        const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
+        w0[m] = cw.x;
+        w1[m] = cw.y;
+        sc[m] = sr[4 * m + g];
+      }
+    } else {
+      valid = e < nw;
+      const int64_t row = (int64_t)b * S + (valid ? (wlo - pos0 + e) : 0);
+      const uint8_t* wr = swa + row * D;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
-      w0[m] = v.x;
-      w1[m] = v.y;
-      w2[m] = v.z;
-      w3[m] = v.w;
+      for (int m = 0; m < NM; ++m) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
+        w0[m] = v.x;
+        w1[m] = v.y;
+        w2[m] = v.z;
+        w3[m] = v.w;
+      }
     }
-  }
+  };
+  load_row(e0);
 
   // ---- query fragments (head i), scaled per head into fp16 range
   f16x8 qa[NM][2];
@@ -305,65 +311,91 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   const float wscale = is_win ? swa_scale[b] : 1.0f;
   const float lscale = sm_scale * wscale;
 
-  // ---- dequantize this wave's tile, logits (rows = heads 4g + rr, column = entry i)
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  {
-    _Float16* vrow = Vs + (wave * 16 + i) * VST;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      f16x8 k0, k1;
-      if (!is_win) {
-        const f16x2 s2 = scale_pair(sc[m]);
-        k0 = fp4x8_to_f16(w0[m], s2);
-        k1 = fp4x8_to_f16(w1[m], s2);
-      } else {
-        uint4 v;
-        v.x = w0[m];
-        v.y = w1[m];
-        v.z = w2[m];
-        v.w = w3[m];
-        e4m3x16_to_f16(v, k0, k1);
-      }
-      acc = mfma16x16x32(qa[m][0], k0, acc);
-      acc = mfma16x16x32(qa[m][1], k1, acc);
-      if (m < NMV) {
-        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0;
-        *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
-      }
-    }
-  }
-  // ---- softmax statistics of the split, per head
-  float lg[4], mh[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    lg[rr] = valid ? ldexpf(acc[rr], -er[rr]) * lscale : -INFINITY;
-    const float mx = row16_max(lg[rr]);
-    if (i == 0) red_max[wave][4 * g + rr] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int h = 4 * g + rr;
-    mh[rr] = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-    const float pr = (mh[rr] == -INFINITY) ? 0.0f : __expf(lg[rr] - mh[rr]);
-    Ps[h * 64 + wave * 16 + i] = (_Float16)pr;
-    const float ps = row16_sum(pr);  // the sum uses the unrounded probabilities
-    if (i == 0) red_sum[wave][h] = ps;
-  }
-  __syncthreads();
-  // ---- P.V for this wave's channels
+  // running softmax state of heads 4g + rr, and this wave's P.V tiles
+  float mh[4], lh[4];
   f32x4 o[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int ch = wave * CPW + nt * 16 + i;
+  for (int rr = 0; rr < 4; ++rr) {
+    mh[rr] = -INFINITY;
+    lh[rr] = 0.0f;
+  }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
-      f16x8 vb;
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int rnd = 0; rnd < rounds; ++rnd) {
+    if (rnd > 0) {
+      __syncthreads();  // the previous round's reads of Vs and Ps are done
+      load_row(e0 + 64 * rnd);
+    }
+    if (rnd + 1 < rounds) ix = load_ix(e0 + 64 * (rnd + 1));  // next round's index, in flight
+    // ---- dequantize this wave's tile, logits (rows = heads 4g + rr, column = entry i)
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      _Float16* vrow = Vs + (wave * 16 + i) * VST;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vb[j] = Vs[(32 * ks + 8 * g + j) * VST + ch];
-      o[nt] = mfma16x16x32(pa, vb, o[nt]);
+      for (int m = 0; m < NM; ++m) {
+        f16x8 k0, k1;
+        if (!is_win) {
+          const f16x2 s2 = scale_pair(sc[m]);
+          k0 = fp4x8_to_f16(w0[m], s2);
+          k1 = fp4x8_to_f16(w1[m], s2);
+        } else {
+          uint4 v;
+          v.x = w0[m];
+          v.y = w1[m];
+          v.z = w2[m];
+          v.w = w3[m];
+          e4m3x16_to_f16(v, k0, k1);
+        }
+        acc = mfma16x16x32(qa[m][0], k0, acc);
+        acc = mfma16x16x32(qa[m][1], k1, acc);
+        if (m < NMV) {
+          *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0;
+          *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
+        }
+      }
+    }
+    // ---- softmax statistics, folded into the running state
+    float lg[4], alpha[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      lg[rr] = valid ? ldexpf(acc[rr], -er[rr]) * lscale : -INFINITY;
+      const float mx = row16_max(lg[rr]);
+      if (i == 0) red_max[wave][4 * g + rr] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 4 * g + rr;
+      const float mr = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
+      const float mnew = fmaxf(mh[rr], mr);
+      alpha[rr] = (mnew == -INFINITY) ? 1.0f : __expf(mh[rr] - mnew);
+      const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lg[rr] - mnew);
+      Ps[h * 64 + wave * 16 + i] = (_Float16)pr;
+      const float ps = row16_sum(pr);  // the sum uses the unrounded probabilities
+      if (i == 0) red_sum[wave][h] = ps;
+      mh[rr] = mnew;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 4 * g + rr;
+      lh[rr] = lh[rr] * alpha[rr] + (red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
+    }
+    // ---- P.V for this wave's channels
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) o[nt][rr] *= alpha[rr];
+      const int ch = wave * CPW + nt * 16 + i;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
+        f16x8 vb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vb[j] = Vs[(32 * ks + 8 * g + j) * VST + ch];
+        o[nt] = mfma16x16x32(pa, vb, o[nt]);
+      }
     }
   }
 
@@ -377,20 +409,12 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     for (int rr = 0; rr < 4; ++rr)
       st_pair<FUSED>(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
                      o[nt + 1][rr] * wscale);
-  if (wave == 0 && i < 8) {
-    // m of heads 2i, 2i+1 and l of heads 2i, 2i+1 (lanes i < 8 of each g
-    // hold the four heads 4g + rr; lanes with g == 0 write for all)
-    if (g == 0) {
-      float mm[2], ll[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int h = 2 * i + k;
-        mm[k] = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-        ll[k] = red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h];
-      }
-      st_pair<FUSED>(pb + 16 * DV + 2 * i, mm[0], mm[1]);
-      st_pair<FUSED>(pb + 16 * DV + 16 + 2 * i, ll[0], ll[1]);
-    }
+  // running max and sum of heads 4g + rr, written by lanes i == 0 as pairs
+  if (wave == 0 && i == 0) {
+    st_pair<FUSED>(pb + 16 * DV + 4 * g, mh[0], mh[1]);
+    st_pair<FUSED>(pb + 16 * DV + 4 * g + 2, mh[2], mh[3]);
+    st_pair<FUSED>(pb + 16 * DV + 16 + 4 * g, lh[0], lh[1]);
+    st_pair<FUSED>(pb + 16 * DV + 16 + 4 * g + 2, lh[2], lh[3]);
   }
   if constexpr (FUSED) {
     // publish the partial, then wait for the row's other splits
@@ -490,19 +514,28 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  const AttnSplit sp = attn_split(K, W);
+  // One round (64 entries) per split when the whole grid fits on the device
+  // and the splits merge in the same launch; with many query rows, splits of
+  // several rounds keep the partials few.
+  const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
+  int32_t rounds = 1;
+  AttnSplit sp = attn_split(K, W, rounds);
+  while ((int64_t)sp.nsplit * rows > 4 * cap_blocks && sp.nsplit > 2 && rounds < 64) {
+    rounds *= 2;
+    sp = attn_split(K, W, rounds);
+  }
   const dim3 grid((unsigned)sp.nsplit, (unsigned)rows);
-  const bool fused = merge_lds_bytes(sp.nsplit) <= lds && w.cnt != nullptr &&
-                     (int64_t)sp.nsplit * rows <= resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
+  const bool fused = rounds == 1 && merge_lds_bytes(sp.nsplit) <= lds && w.cnt != nullptr &&
+                     (int64_t)sp.nsplit * rows <= cap_blocks;
   if (fused) {
     CSA2_KERNEL(true, true, (sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, q, T, codes,
                        scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
-                       sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
+                       sp.nsg, sp.nsplit, rounds, row0, out, lse, w.cnt, w.cnt_stride);
     return hipGetLastError();
   }
   CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, q, T, codes,
                      scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
-                     sp.nsg, sp.nsplit, row0, out, lse, w.cnt, w.cnt_stride);
+                     sp.nsg, sp.nsplit, rounds, row0, out, lse, w.cnt, w.cnt_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int NU = 16 * DV / 2;

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
                                                         const int32_t* __restrict__ n_valid,
                                                         int32_t nv_add,
                                                         uint32_t* __restrict__ hist,
-                                                        int64_t hist_stride) {
+                                                        int64_t hist_stride,
+                                                        int32_t hist_copies) {
   constexpr int PT = kTopkChunk / 256;
   __shared__ uint32_t lhist[kHistBins];
   const int r = blockIdx.y;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
   for (int j = 0; j < PT; ++j)
     if (start + j * 256 + threadIdx.x < nv) atomicAdd(&lhist[score_key(v[j]) >> kHistShift], 1u);
   __syncthreads();
-  uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % kHistCopies) * kHistBins;
+  uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
   for (int k = threadIdx.x; k < kHistBins; k += 256)
     if (lhist[k]) atomicAdd(gh + k, lhist[k]);
 }
@@ -118,6 +119,64 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32
   __syncthreads();
   *total = tot;
   return off + inc - v;
+}
+
+// The row's 12-bit key histogram summed over its `copies` copies, bins
+// [4t, 4t+4) of thread t (1024 threads).
+__device__ __forceinline__ void load_hist4(const uint32_t* rh, int copies, uint32_t (&h4)[4]) {
+  uint4 hc[kHistCopies];
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c)
+    hc[c] = (c < copies) ? *reinterpret_cast<const uint4*>(rh + c * kHistBins + 4 * threadIdx.x)
+                         : make_uint4(0, 0, 0, 0);
+  h4[0] = h4[1] = h4[2] = h4[3] = 0u;
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c) {
+    h4[0] += hc[c].x;
+    h4[1] += hc[c].y;
+    h4[2] += hc[c].z;
+    h4[3] += hc[c].w;
+  }
+}
+
+// The bin holding the k-th largest key: count(bins > b1) < k <= count(bins
+// >= b1).  Written to *b1 by the thread that finds it (left unchanged when
+// the histogram holds fewer than k keys); every thread calls it.
+__device__ __forceinline__ void find_cut(const uint32_t* rh, int copies, int32_t k, uint32_t* tmp,
+                                         int* b1) {
+  uint32_t h4[4];
+  load_hist4(rh, copies, h4);
+  const uint32_t sum = h4[0] + h4[1] + h4[2] + h4[3];
+  uint32_t total;
+  const uint32_t excl = block_scan<kSelThreads>(sum, tmp, &total);
+  const uint32_t above = total - excl - sum;  // keys in bins of higher threads
+  if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
+    uint32_t acc = above;
+    bool found = false;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (!found && acc + h4[j] >= (uint32_t)k) {
+        *b1 = 4 * threadIdx.x + j;
+        found = true;
+      }
+      acc += h4[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Rows with many select blocks find their cut once: one block per row.
+__global__ __launch_bounds__(kSelThreads) void topk_cut_kernel(const int32_t* __restrict__ n_valid,
+                                                               int32_t nv_add, int64_t n, int32_t k,
+                                                               TopkWs w) {
+  __shared__ uint32_t tmp[kSelWaves];
+  __shared__ int s_b1;
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0) s_b1 = 0x7FFFFFFF;
+  __syncthreads();
+  if (min((int64_t)n_valid[r] + nv_add, n) > k)
+    find_cut(w.hist + (int64_t)r * w.hist_stride, w.hist_copies, k, tmp, &s_b1);
+  if (threadIdx.x == 0) w.cut[(int64_t)r * w.ctr_stride] = (uint32_t)s_b1;
 }
 
 // Completion of row r by its last block (all select blocks of the row have
@@ -412,7 +471,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand, int32_t bm_words) {
+    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand, int32_t bm_words, bool use_cut) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t tmp[kSelWaves];
   __shared__ uint32_t wtot[2][kSelWaves];  // kept / candidates per wave
@@ -439,39 +498,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 #pragma unroll
       for (int j = 0; j < kPerLane; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
       // the row's histogram summed over its copies: bins [4t, 4t+4)
-      uint32_t h4[4] = {0u, 0u, 0u, 0u};
-      {
-        uint4 hc[kHistCopies];
-#pragma unroll
-        for (int c = 0; c < kHistCopies; ++c)
-          hc[c] = *reinterpret_cast<const uint4*>(rh + c * kHistBins + 4 * tid);
-#pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) {
-          h4[0] += hc[c].x;
-          h4[1] += hc[c].y;
-          h4[2] += hc[c].z;
-          h4[3] += hc[c].w;
-        }
-      }
       if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
-      {
-        const uint32_t sum = h4[0] + h4[1] + h4[2] + h4[3];
-        uint32_t total;
-        const uint32_t excl = block_scan<kSelThreads>(sum, tmp, &total);
-        const uint32_t above = total - excl - sum;  // elements in bins of higher threads
-        if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
-          uint32_t acc = above;
-          bool found = false;
-#pragma unroll
-          for (int j = 3; j >= 0; --j) {
-            if (!found && acc + h4[j] >= (uint32_t)k) {
-              s_b1 = 4 * tid + j;
-              found = true;
-            }
-            acc += h4[j];
-          }
-        }
+      if (use_cut) {
+        if (tid == 0) s_b1 = (int)w.cut[(int64_t)r * w.ctr_stride];
         __syncthreads();
+      } else {
+        find_cut(rh, w.hist_copies, k, tmp, &s_b1);
       }
       const uint32_t b1 = (uint32_t)s_b1;
       // count pass: this wave's kept and candidate totals
@@ -528,7 +560,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     uint32_t* ctr = w.ctr + (int64_t)r * w.ctr_stride;
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == (uint32_t)nblk - 1u;
-    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s_last) {
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w.cut[(int64_t)r * w.ctr_stride] = 0u;  // every block of the row has read it
+    }
   }
   __syncthreads();
   if (!s_last) return;
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   // ---- leave the histogram copies zero for the next call (every block of
   // the row has read them)
   uint4* h4p = reinterpret_cast<uint4*>(rh);
-  for (int j = tid; j < kHistCopies * kHistBins / 4; j += kSelThreads) h4p[j] = make_uint4(0, 0, 0, 0);
+  for (int j = tid; j < w.hist_copies * kHistBins / 4; j += kSelThreads) h4p[j] = make_uint4(0, 0, 0, 0);
 }
 
 static int32_t topk_blocks(int64_t n_max) {
@@ -546,11 +581,11 @@ static int32_t topk_blocks(int64_t n_max) {
 
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
-                            hipStream_t st) {
+                            int32_t hist_copies, hipStream_t st, bool first) {
   const int64_t nchunks = (n_max + kTopkChunk - 1) / kTopkChunk;
   if (nchunks == 0) return hipSuccess;
-  CSA2_KERNEL(true, true, topk_hist_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(256), 0, st,
-                     scores, n, n_valid, nv_add, hist, hist_stride);
+  CSA2_KERNEL(first, true, topk_hist_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(256), 0, st,
+                     scores, n, n_valid, nv_add, hist, hist_stride, hist_copies);
   return hipGetLastError();
 }
 
@@ -577,9 +612,14 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  CSA2_KERNEL(true, true, topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows), dim3(kSelThreads),
-                     lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, w,
-                     lds_cand, bm_words);
+  // many blocks per row: find each row's cut once instead of in every block
+  const bool use_cut = (int64_t)rows * nblk > 1024;
+  if (use_cut)
+    CSA2_KERNEL(true, false, topk_cut_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, st,
+                n_valid, nv_add, n, k, w);
+  CSA2_KERNEL(!use_cut, true, topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows),
+              dim3(kSelThreads), lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out,
+              count_out, w, lds_cand, bm_words, use_cut);
   return hipGetLastError();
 }
 
