@@ -141,9 +141,11 @@ void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
 void carve_topk(Carve& c, int32_t rows, int64_t n, int32_t k, TopkWs* tw) {
   (void)k;
   const int64_t nblk = std::max<int64_t>(1, (n + kTopkChunk - 1) / kTopkChunk);
-  tw->above_stride = nblk * kTopkChunk;
+  // regions cover whole blocks of either chunk size
+  const int64_t span = std::max<int64_t>(1, (n + kTopkChunkLarge - 1) / kTopkChunkLarge) * kTopkChunkLarge;
+  tw->above_stride = span;
   tw->above = c.take<uint32_t>((size_t)rows * tw->above_stride);
-  tw->cand_stride = nblk * kTopkChunk;
+  tw->cand_stride = span;
   tw->cand = c.take<uint64_t>((size_t)rows * tw->cand_stride);
   tw->counts_stride = 2 * nblk;
   tw->counts = c.take<uint32_t>((size_t)rows * tw->counts_stride);

@@ -11,7 +11,8 @@ namespace csa2 {
 
 constexpr int32_t kScoreChunk = 2048;  // positions per scoring block
 constexpr int kScoreGroup = 4;         // consecutive 16-position tiles per wave load
-constexpr int32_t kTopkChunk = 4096;   // scores per select block (4 per thread)
+constexpr int32_t kTopkChunk = 4096;        // scores per select block (4 per thread)
+constexpr int32_t kTopkChunkLarge = 16384;  // ... when a pass has many rows (16 per thread)
 constexpr int32_t kAttnSplit = 64;      // entries per attention split (one tile per wave)
 constexpr int32_t kMaxSplits = 512;     // (CSA2_MAX_K + CSA2_MAX_W) / kAttnSplit
 constexpr int64_t kMaxTopkN = int64_t(1) << 25;  // longest score row Top-K accepts
@@ -29,8 +30,8 @@ constexpr int64_t kCtlWordsPerRow = kHistWords + 64;
 struct TopkWs {
   uint32_t* hist;        // row r at hist + r * hist_stride (kHistCopies x 4096 bins)
   int64_t hist_stride;   // in words
-  // Per select block b of row r, regions of kTopkChunk entries at offset
-  // r * stride + b * kTopkChunk: the positions kept outright and the
+  // Per select block b of row r, regions of `chunk` entries at offset
+  // r * stride + b * chunk (chunk = kTopkChunk or kTopkChunkLarge): the positions kept outright and the
   // candidates' 64-bit rank values, each in position order.
   uint32_t* above;
   int64_t above_stride;

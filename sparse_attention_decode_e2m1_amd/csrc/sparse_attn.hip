@@ -520,7 +520,7 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
   int32_t rounds = 1;
   AttnSplit sp = attn_split(K, W, rounds);
-  while ((int64_t)sp.nsplit * rows > 4 * cap_blocks && sp.nsplit > 2 && rounds < 64) {
+  while ((int64_t)sp.nsplit * rows > 8 * cap_blocks && sp.nsplit > 2 && rounds < 64) {
     rounds *= 2;
     sp = attn_split(K, W, rounds);
   }

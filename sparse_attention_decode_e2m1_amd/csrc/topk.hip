@@ -15,8 +15,8 @@
 //     (a block adds into copy blockIdx % kHistCopies: device-scope atomics on
 //     one address serialise).  Built by the scoring kernel, or here by
 //     topk_hist_kernel.
-//  2. topk_select_kernel, one 1024-thread block per kTopkChunk (4096) scores
-//     of a row: the block sums the histogram copies and finds the bin b1 holding
+//  2. topk_select_kernel, one 1024-thread block per 4096 scores of a row
+//     (16384 when a pass has many rows): the block sums the histogram copies and finds the bin b1 holding
 //     the K-th key.  Its scores above b1 are kept outright; those in b1 are
 //     candidates.  Wave w takes a contiguous run of slots, so a count pass
 //     and a prefix over the 16 wave totals place both lists in position
@@ -38,8 +38,6 @@ namespace csa2 {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSlotsPerWave = kTopkChunk / kSelWaves;  // 256 consecutive slots
-constexpr int kPerLane = kSlotsPerWave / 64;           // 4 scores per lane
 constexpr int kHistPerThread = kHistBins / kSelThreads;  // 4 bins per thread
 static_assert(kHistPerThread == 4, "one uint4 of each histogram copy per thread");
 
@@ -187,7 +185,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_cut_kernel(const int32_t* __
 __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
                            int32_t k, int nblk, int32_t* __restrict__ idx_out,
                            int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
-                           int32_t bm_words, uint32_t* smem, uint32_t* tmp) {
+                           int32_t bm_words, int32_t chunk, uint32_t* smem, uint32_t* tmp) {
   constexpr int NT = kSelThreads;
   const bool use_bm = bm_words > 0;
   uint32_t* rhist = smem;                      // 2048 radix bins
@@ -264,7 +262,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
   const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
   auto cand_at = [&](uint32_t c) -> uint64_t {
     const int b = block_of(offE, c);
-    return ld_coh(cbase + (int64_t)b * kTopkChunk + (c - offE[b]));
+    return ld_coh(cbase + (int64_t)b * chunk + (c - offE[b]));
   };
   // ---- gather the kept ("above") positions and the candidates
   const uint32_t Ak = min(A, (uint32_t)k);
@@ -283,8 +281,8 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
       const int bb = live ? b : 0;
       const uint32_t a_lo = min(offA[bb], Ak), a_hi = live ? min(offA[bb + 1], Ak) : a_lo;
       const uint32_t e_lo = min(offE[bb], nC), e_hi = live ? min(offE[bb + 1], nC) : e_lo;
-      const uint32_t* ar = abase + (int64_t)bb * kTopkChunk;
-      const uint64_t* cr = cbase + (int64_t)bb * kTopkChunk;
+      const uint32_t* ar = abase + (int64_t)bb * chunk;
+      const uint64_t* cr = cbase + (int64_t)bb * chunk;
       const uint32_t na = a_hi - a_lo, ne = e_hi - e_lo;
       for (uint32_t i0 = j; i0 < max(na, ne); i0 += 8 * tpb) {
         uint32_t ta[8];
@@ -468,6 +466,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
   if (count_out && tid == 0) count_out[r] = (int32_t)kept;
 }
 
+template <int PL>  // scores per lane: a block takes 1024 * PL consecutive slots
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
@@ -480,8 +479,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int r = blockIdx.y, nblk = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
-  const int64_t start = (int64_t)blockIdx.x * kTopkChunk;
-  const int64_t wstart = start + (int64_t)wave * kSlotsPerWave;
+  constexpr int32_t kChunk = kSelThreads * PL;
+  const int64_t start = (int64_t)blockIdx.x * kChunk;
+  const int64_t wstart = start + (int64_t)wave * 64 * PL;
   uint32_t* rh = w.hist + (int64_t)r * w.hist_stride;
 
   if (nv > k) {
@@ -494,9 +494,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     } else {
       // this wave's scores: slots wstart + 64j + lane
       const float* srow = scores + (int64_t)r * n;
-      float v[kPerLane];
+      float v[PL];
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
+      for (int j = 0; j < PL; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
       // the row's histogram summed over its copies: bins [4t, 4t+4)
       if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
       if (use_cut) {
@@ -508,9 +508,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       const uint32_t b1 = (uint32_t)s_b1;
       // count pass: this wave's kept and candidate totals
       uint32_t na = 0, ne = 0;
-      uint32_t keys[kPerLane];
+      uint32_t keys[PL];
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) {
+      for (int j = 0; j < PL; ++j) {
         const int64_t s = wstart + 64 * j + lane;
         keys[j] = score_key(v[j]);
         const uint32_t bin = keys[j] >> kHistShift;
@@ -532,11 +532,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         te += c;
       }
       // write pass, in slot order
-      uint32_t* ra = w.above + (int64_t)r * w.above_stride + (int64_t)blockIdx.x * kTopkChunk;
-      uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kTopkChunk;
+      uint32_t* ra = w.above + (int64_t)r * w.above_stride + (int64_t)blockIdx.x * kChunk;
+      uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kChunk;
       const uint64_t lt = lanemask_lt();
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) {
+      for (int j = 0; j < PL; ++j) {
         const int64_t s = wstart + 64 * j + lane;
         const uint32_t bin = keys[j] >> kHistShift;
         const bool ab = s < nv && bin > b1;
@@ -567,15 +567,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, bm_words, smem, tmp);
+  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, bm_words, kChunk, smem,
+             tmp);
   // ---- leave the histogram copies zero for the next call (every block of
   // the row has read them)
   uint4* h4p = reinterpret_cast<uint4*>(rh);
   for (int j = tid; j < w.hist_copies * kHistBins / 4; j += kSelThreads) h4p[j] = make_uint4(0, 0, 0, 0);
 }
 
-static int32_t topk_blocks(int64_t n_max) {
-  const int64_t b = (n_max + kTopkChunk - 1) / kTopkChunk;
+static int32_t topk_blocks(int64_t n_max, int32_t chunk) {
+  const int64_t b = (n_max + chunk - 1) / chunk;
   return (int32_t)(b < 1 ? 1 : b);
 }
 
@@ -593,7 +594,10 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st) {
-  const int32_t nblk = topk_blocks(n_max);
+  // many rows: bigger blocks (fewer, each with more scores)
+  const bool large = (int64_t)rows * topk_blocks(n_max, kTopkChunk) > 1024;
+  const int32_t chunk = large ? kTopkChunkLarge : kTopkChunk;
+  const int32_t nblk = topk_blocks(n_max, chunk);
   // LDS of the completing block: radix bins, 2 offset arrays, the kept-slot
   // bitmap (rows up to kBitmapSlots) or list, then as many candidates as fit.
   constexpr int64_t kBitmapSlots = int64_t(1) << 19;
@@ -606,9 +610,11 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   const size_t lds = fixed + (size_t)lds_cand * 8;
   static bool lds_raised = false;
   if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             150 * 1024);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<4>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)topk_select_kernel<16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
@@ -617,9 +623,14 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   if (use_cut)
     CSA2_KERNEL(true, false, topk_cut_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, st,
                 n_valid, nv_add, n, k, w);
-  CSA2_KERNEL(!use_cut, true, topk_select_kernel, dim3((unsigned)nblk, (unsigned)rows),
-              dim3(kSelThreads), lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out,
-              count_out, w, lds_cand, bm_words, use_cut);
+  if (large)
+    CSA2_KERNEL(!use_cut, true, topk_select_kernel<16>, dim3((unsigned)nblk, (unsigned)rows),
+                dim3(kSelThreads), lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out,
+                count_out, w, lds_cand, bm_words, use_cut);
+  else
+    CSA2_KERNEL(!use_cut, true, topk_select_kernel<4>, dim3((unsigned)nblk, (unsigned)rows),
+                dim3(kSelThreads), lds, st, scores, n, n_valid, nv_add, slot_pos, k, idx_out,
+                count_out, w, lds_cand, bm_words, use_cut);
   return hipGetLastError();
 }
 
