@@ -180,10 +180,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       if constexpr (GPS >= 2) part += shfl_xor(part, 16);
       if constexpr (GPS >= 4) part += shfl_xor(part, 32);
       const int64_t s = start + (int64_t)((rnd * 4 + wave) * GT + a * TPA + my_slot) * 16 + i;
-      if (owner && s < end) {
-        srow[s] = part;
-        if (hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
-      }
+      // Lanes past the end scored the clamped last position, so storing at the
+      // clamped slot writes the same value; an unconditional store keeps the
+      // count of outstanding memory operations fixed, so waiting for the next
+      // group's loads does not also wait for these stores.
+      if (owner) srow[min(s, end - 1)] = part;
+      if (owner && s < end && hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
     }
     if (rnd + 1 < nrounds) {
 #pragma unroll
@@ -229,22 +231,14 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
   const int rbase = blockIdx.y * 128 + wave * 32;  // first token row of this wave
   if (rbase >= rows) return;                       // no block-wide barrier below
   const int b = (row0 + rbase) / T;                // all 32 tokens share the sequence
-  // visible lengths: nvt[j] for token 4j + g (the epilogue's token), and the
-  // wave's longest
-  int64_t nvt[NG];
+  // the wave's longest visible length
   int64_t nvmax;
   {
     const int tr = min(rbase + (lane & 31), rows - 1);
-    int64_t v = min(min((int64_t)n_valid[tr] + nv_add, n_out), cap);
-    int64_t m = v;
+    int64_t m = min(min((int64_t)n_valid[tr] + nv_add, n_out), cap);
 #pragma unroll
     for (int d = 1; d < 32; d <<= 1) m = max(m, (int64_t)__shfl_xor(m, d, kWave));
     nvmax = m;
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      const int t = rbase + 4 * j + g;
-      nvt[j] = (t < rows) ? (int64_t)__shfl(v, 4 * j + g, kWave) : 0;
-    }
   }
   const int64_t start = (int64_t)blockIdx.x * chunk;
   if (start >= nvmax) return;
@@ -291,7 +285,8 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int e = __shfl(qexp, 4 * g + rr, kWave);
-        wq[j][rr] = (rr < HI) ? ldexpf(w[(int64_t)te * HI + rr], -e) : 0.0f;
+        const float wv = w[(int64_t)te * HI + min(rr, HI - 1)];  // unconditional load
+        wq[j][rr] = (rr < HI) ? ldexpf(wv, -e) : 0.0f;
       }
     }
   }
@@ -317,10 +312,12 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
 #pragma unroll
   for (int p = 0; p < PF; ++p) load_tile(min(p, max(ntiles - 1, 0)), cw[p], sw[p]);
   for (int t0 = 0; t0 < ntiles; t0 += PF) {
+    // Tiles past the end recompute the clamped last position and store the
+    // same value there, so the body is straight-line code (no early exit)
+    // and the waits for each ring slot count only its own loads.
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int tile = t0 + p;
-      if (tile >= ntiles) break;
       f16x8 kb[NCH][4];
 #pragma unroll
       for (int c2 = 0; c2 < NCH; ++c2) {
@@ -345,7 +342,10 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
         float part = 0.0f;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) part += wq[j][rr] * fmaxf(acc[rr], 0.0f);
-        if (s < nvt[j]) scores[(int64_t)(rbase + 4 * j + g) * n_out + s] = part;
+        // Unconditional (clamped) store, as in index_score_kernel: tokens past
+      // the last row computed that row's score (clamped query and weights),
+      // and slots past a token's visible range are never read for it.
+      scores[(int64_t)min(rbase + 4 * j + g, rows - 1) * n_out + min(s, end - 1)] = part;
       }
     }
   }

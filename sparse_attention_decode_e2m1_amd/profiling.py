@@ -9,7 +9,12 @@
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N
         HBM bytes per dispatch of a kernel from two ``--pmc FETCH_SIZE`` /
         ``--pmc WRITE_SIZE`` runs, each scaled by the factor that makes the
-        same counter read N bytes for a plain copy of N bytes.
+        same counter read N bytes for a plain copy of N bytes;
+
+    python -m sparse_attention_decode_e2m1_amd.profiling mfma \
+        --kernel index_score_tokens_kernel --counters C.csv
+        MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x
+        SIMDs) and f16 MFMA flops per dispatch from one --pmc run.
 
 The traffic summary also records a digest of the sources the kernel is built
 from, so a reader can tell whether the counters still describe the kernel.
@@ -104,6 +109,24 @@ def cmd_traffic(a):
     print(f"traffic_bytes_per_dispatch: {fetch_b + write_b:.0f}")
 
 
+def cmd_mfma(a):
+    """MFMA utilisation of a kernel from one --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16 and GRBM_GUI_ACTIVE."""
+    c = counter_means(a.counters, a.kernel)
+    busy, mops, active = (c["SQ_VALU_MFMA_BUSY_CYCLES"], c["SQ_INSTS_VALU_MFMA_MOPS_F16"],
+                          c["GRBM_GUI_ACTIVE"])
+    util = busy / (active * a.simds)
+    flops = mops * 512
+    print(f"kernel: {a.kernel}")
+    print(f"dispatches_averaged: yes")
+    print(f"SQ_VALU_MFMA_BUSY_CYCLES_per_dispatch: {busy:.0f}")
+    print(f"SQ_INSTS_VALU_MFMA_MOPS_F16_per_dispatch: {mops:.0f}")
+    print(f"GRBM_GUI_ACTIVE_per_dispatch: {active:.0f}")
+    print(f"simds: {a.simds}")
+    print(f"mfma_busy_fraction: {util:.4f}")
+    print(f"mfma_f16_flop_per_dispatch: {flops:.4g}")
+
+
 def read_traffic(path: str, kernel: str):
     """HBM bytes per dispatch recorded in a traffic summary, or None when the
     file is absent or the kernel's sources changed since it was taken."""
@@ -133,8 +156,12 @@ def main(argv=None):
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument("--" + k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--counters", required=True)
+    m.add_argument("--simds", type=int, default=1024)  # 256 CUs x 4 SIMDs
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
