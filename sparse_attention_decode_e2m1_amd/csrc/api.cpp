@@ -116,23 +116,19 @@ struct Carve {
   }
 };
 
-// Control block of row r: the kHistWords histogram copies, then the
-// attention merge counters.
-void carve_ctl(Carve& c, int32_t rows, TopkWs* tw, AttnWs* aw) {
+// Control block of row r: the kHistWords histogram copies, then the Top-K
+// counters.
+void carve_ctl(Carve& c, int32_t rows, TopkWs* tw) {
   uint32_t* ctl = c.take<uint32_t>((size_t)rows * kCtlWordsPerRow);
   if (tw) {
     tw->hist = ctl;
     tw->hist_stride = kCtlWordsPerRow;
-    tw->ctr = ctl ? ctl + kHistWords + 2 : nullptr;
+    tw->ctr = ctl ? ctl + kHistWords : nullptr;
     tw->ctr_stride = kCtlWordsPerRow;
-    tw->cut = ctl ? ctl + kHistWords + 3 : nullptr;
+    tw->cut = ctl ? ctl + kHistWords + 1 : nullptr;
     // Copies spread the histogram atomics of a row's many scoring blocks;
     // with many rows per pass one copy keeps the select pass's reads small.
     tw->hist_copies = rows <= 32 ? kMaxHistCopies : 1;
-  }
-  if (aw) {
-    aw->cnt = ctl ? ctl + kHistWords : nullptr;
-    aw->cnt_stride = kCtlWordsPerRow;
   }
 }
 
@@ -287,7 +283,7 @@ size_t csa2_topk_workspace_bytes(int32_t rows, int64_t n, int32_t k) {
   const int32_t rc = std::min(rows, kRowChunk);
   Carve c(nullptr);
   TopkWs tw;
-  carve_ctl(c, rc, &tw, nullptr);
+  carve_ctl(c, rc, &tw);
   carve_topk(c, rc, n, k, &tw);
   return c.off;
 }
@@ -306,7 +302,7 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
   const int32_t rc = std::min(rows, kRowChunk);
   Carve c(ws);
   TopkWs tw;
-  carve_ctl(c, rc, &tw, nullptr);
+  carve_ctl(c, rc, &tw);
   carve_topk(c, rc, n, k, &tw);
   const hipStream_t st = as_stream(stream);
   for (int32_t r0 = 0; r0 < rows; r0 += rc) {
@@ -330,7 +326,7 @@ size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int3
   const int32_t rc = std::min(rows, kRowChunk);
   Carve c(nullptr);
   AttnWs aw;
-  carve_ctl(c, rc, nullptr, &aw);
+  carve_ctl(c, rc, nullptr);
   carve_attn(c, rc, K, W, dv, &aw);
   return c.off;
 }
@@ -374,7 +370,7 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
   const int32_t rc = std::min(rows, kRowChunk);
   Carve c(ws);
   AttnWs aw;
-  carve_ctl(c, rc, nullptr, &aw);
+  carve_ctl(c, rc, nullptr);
   carve_attn(c, rc, K, Weff, dv, &aw);
   const int32_t D = kv->dim;
   for (int32_t r0 = 0; r0 < rows; r0 += rc) {
@@ -411,7 +407,7 @@ StepLayout step_layout(csa2_mode mode, const csa2_layer_args* a, void* ws) {
   L.n_out = (mode == CSA2_MODE_REUSE) ? 1 : (pooled_in ? a->P_in : a->icache.cap);
   const int32_t Weff = (a->S > 0) ? a->W : 0;
   Carve c(ws);
-  carve_ctl(c, L.rc, &L.tw, &L.aw);
+  carve_ctl(c, L.rc, &L.tw);
   if (mode != CSA2_MODE_REUSE) {
     L.scores = c.take<float>((size_t)L.rc * L.n_out);
     const int32_t kmax = (mode == CSA2_MODE_FULL && a->P > 0) ? std::max(a->P, a->K) : a->K;

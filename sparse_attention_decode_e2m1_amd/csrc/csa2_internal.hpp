@@ -18,13 +18,12 @@ constexpr int32_t kMaxSplits = 512;     // (CSA2_MAX_K + CSA2_MAX_W) / kAttnSpli
 constexpr int64_t kMaxTopkN = int64_t(1) << 25;  // longest score row Top-K accepts
 
 // Every call keeps the control words of query row r -- the Top-K histogram
-// copies, then the attention merge counters -- in one fixed-size block at the start of the workspace.  They are
-// zero between calls, so any workspace left by a previous call (of any kind
-// or shape) is ready for the next.
+// copies and counters -- in one fixed-size block at the start of the
+// workspace.  They are zero between calls, so any workspace left by a
+// previous call (of any kind or shape) is ready for the next.
 constexpr int kMaxHistCopies = 8;
 constexpr int64_t kHistWords = int64_t(kMaxHistCopies) * 4096;  // copies x 4096 bins
-// + attention arrival / leave counters (words 0, 1), the Top-K arrival counter (word 2) and
-// the Top-K cut bin (word 3)
+// + the Top-K arrival counter (word 0) and the Top-K cut bin (word 1)
 constexpr int64_t kCtlWordsPerRow = kHistWords + 64;
 
 struct TopkWs {
@@ -47,8 +46,6 @@ struct TopkWs {
 
 struct AttnWs {
   float* part;        // [rows][nsplit][16*dv + 32]
-  uint32_t* cnt;      // row r at cnt + r * cnt_stride: arrivals, departures
-  int64_t cnt_stride;
 };
 
 struct AttnSplit {

@@ -19,44 +19,23 @@
 // [w*dv/4, (w+1)*dv/4).  Window entries enter as raw E4M3 values and their
 // scale multiplies the split's logits and partial output.
 //
-// Each split writes its partial (o, max, sum) per head.  The merge
-//   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L
-// runs in the same launch when every block of the grid can be resident at
-// once: a block writes its partial with device-coherent stores, waits for
-// them to complete, counts itself in the row's arrival counter and waits for
-// the row's other splits (bounded wait), then merges one slice of the row's
-// output with device-coherent loads.  Otherwise a second kernel merges.
+// Each split writes its partial (o, max, sum) per head, and a second kernel
+// merges them:
+//   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L.
+// (Merging in the same launch, with the splits exchanging partials through
+// device-coherent memory, measured slower on MI355X than the kernel boundary:
+// partials written by one XCD and read by another make a slow round trip.)
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-// Longest wait of the merging blocks for the other splits of their row, in
-// polls of about 100 cycles (far beyond any real wait, a guard against a
-// grid that is not co-resident): the row's output is then set to NaN.
-constexpr int kSpinLimit = 1 << 20;
-
-// Partials that another block of the same launch reads go through the
-// device-coherent path (agent-scope accesses: written through to, and read
-// from, the level all XCDs share) instead of full L2 write-back and
-// invalidate fences.  Values travel in pairs (64-bit accesses).
-template <bool COH>
+// Partial values travel in pairs (64-bit accesses).
 __device__ __forceinline__ void st_pair(float* p, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  if constexpr (COH)
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    *reinterpret_cast<uint64_t*>(p) = v;
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
-template <bool COH>
 __device__ __forceinline__ float2 ld_pair(const float* p) {
-  uint64_t v;
-  if constexpr (COH)
-    v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_AGENT);
-  else
-    v = *reinterpret_cast<const uint64_t*>(p);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+  return *reinterpret_cast<const float2*>(p);
 }
 
 // Layout of a split's partial output for one head: wave w, lane column i and
@@ -77,10 +56,10 @@ __device__ __forceinline__ int partial_channel(int p) {
 // The split maxima/sums and the partial outputs a thread needs are all
 // requested before any is used, so the merge costs about one memory round
 // trip plus the reduction of the maxima.
-template <int DV, bool COH>
+template <int DV>
 __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, int u1,
                             float* __restrict__ orow, float* __restrict__ lrow, bool write_lse,
-                            bool ok, float* ml) {
+                            float* ml) {
   constexpr int PSTRIDE = 16 * DV + 32;
   constexpr int UPH = DV / 2;  // units per head
   constexpr int NU = 16 * UPH;
@@ -108,12 +87,12 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int jp = min(k * 256 + tid, nmp - 1);
-        mlv[k] = ld_pair<COH>(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
+        mlv[k] = ld_pair(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
       }
     }
     float2 v[KB];
 #pragma unroll
-    for (int k = 0; k < KB; ++k) v[k] = ld_pair<COH>(col + (int64_t)min(sub + k * SUB, nsplit - 1) * PSTRIDE);
+    for (int k = 0; k < KB; ++k) v[k] = ld_pair(col + (int64_t)min(sub + k * SUB, nsplit - 1) * PSTRIDE);
     if (ub == 0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -124,7 +103,7 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
         }
       }
       for (int jp = 4 * 256 + tid; jp < nmp; jp += 256) {  // beyond 64 splits
-        const float2 t = ld_pair<COH>(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
+        const float2 t = ld_pair(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
         ml[2 * jp] = t.x;
         ml[2 * jp + 1] = t.y;
       }
@@ -158,7 +137,7 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
       __syncthreads();
       if (write_lse && tid < 16) {
         const float Lt = s_L[tid];
-        lrow[tid] = !ok ? __int_as_float(0x7FC00000) : (Lt > 0.0f) ? s_M[tid] + logf(Lt) : -INFINITY;
+        lrow[tid] = (Lt > 0.0f) ? s_M[tid] + logf(Lt) : -INFINITY;
       }
     }
     float2 acc = make_float2(0.f, 0.f);
@@ -172,7 +151,7 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
     // splits beyond the first KB per thread
     for (int s0 = sub + KB * SUB; live && s0 < nsplit; s0 += KB * SUB) {
 #pragma unroll
-      for (int k = 0; k < KB; ++k) v[k] = ld_pair<COH>(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
+      for (int k = 0; k < KB; ++k) v[k] = ld_pair(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
         const int s = s0 + k * SUB;
@@ -193,69 +172,107 @@ __device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, 
       const float L = s_L[h];
       const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
       const int ch = partial_channel<DV>(pp);  // slot pp + 1 holds channel ch + 16
-      orow[h * DV + ch] = ok ? t.x * inv : NAN;
-      orow[h * DV + ch + 16] = ok ? t.y * inv : NAN;
+      orow[h * DV + ch] = t.x * inv;
+      orow[h * DV + ch + 16] = t.y * inv;
     }
     __syncthreads();
   }
 }
 
-template <int D, int DV, bool FUSED>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(
-    const uint16_t* __restrict__ q, int32_t T, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, int64_t cap, const int32_t* __restrict__ idx, int32_t K,
-    const uint8_t* __restrict__ swa, const float* __restrict__ swa_scale,
-    const int32_t* __restrict__ swa_pos0, int32_t S, int32_t W, const int32_t* __restrict__ q_pos,
-    float sm_scale, float* __restrict__ part, int32_t nsg, int32_t nsplit, int32_t rounds,
-    int32_t row0, float* __restrict__ out, float* __restrict__ lse, uint32_t* __restrict__ cnt,
-    int64_t cnt_stride) {
+// B operand of P.V straight from the row-major V tile: ds_read_b64_tr_b16
+// hands lane t of each 16-lane group element t % 4 of the 64-bit word
+// addressed by lane 4j + t / 4, as its element j.  With lane s addressing
+// V[e0 + s / 4][c0 + 4 (s % 4)], lane t receives V[e0 + j][c0 + t], j < 4.
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+__device__ __forceinline__ f16x8 v_operand(const _Float16* lo, const _Float16* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(hi));
+  return __builtin_bit_cast(f16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int DV>
+constexpr int vs_stride() {
+  // halves; a row stride of 8 banks mod 64 keeps the four rows of a
+  // transposed read on distinct banks
+  return DV + 16;
+}
+
+struct AttnArgs {
+  const uint16_t* q;
+  int32_t T;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t cap;
+  const int32_t* idx;
+  int32_t K;
+  const uint8_t* swa;
+  const float* swa_scale;
+  const int32_t* swa_pos0;
+  int32_t S, W;
+  const int32_t* q_pos;
+  float sm_scale;
+  float* part;
+  int32_t nsg, nsplit, rounds, row0;
+};
+
+// One split of one query row.  WIN: the split holds window entries (raw
+// E4M3 rows); MULTI: the split runs several rounds of 64 entries.  Each
+// instantiation is straight-line code from the index load to the row loads,
+// so the row loads issue as soon as the index arrives.
+template <int D, int DV, bool WIN, bool MULTI>
+__device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _Float16* Vs,
+                                           _Float16* Ps, float (*red_max)[16],
+                                           float (*red_sum)[16]) {
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
-  constexpr int VST = DV + 8;       // LDS row stride of V (halves), padded
+  constexpr int VST = vs_stride<DV>();
   constexpr int CPW = DV / 4;       // value channels per wave
   constexpr int NT = CPW / 16;      // P.V output tiles per wave
   constexpr int PSTRIDE = 16 * DV + 32;
-  extern __shared__ _Float16 Vs[];  // [64 entries][VST]; the merge reuses it
-  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
-  __shared__ float red_max[4][16];
-  __shared__ float red_sum[4][16];
-
-  const int r = blockIdx.y, b = (row0 + r) / T, sidx = blockIdx.x;
+  const int b = (a.row0 + r) / a.T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const bool is_win = sidx >= nsg;
+  const int rounds = MULTI ? a.rounds : 1;
   // entry of this lane in round rnd: e0 + 64 * rnd
-  const int e0 = (is_win ? sidx - nsg : sidx) * 64 * rounds + wave * 16 + i;
+  const int e0 = (WIN ? sidx - a.nsg : sidx) * 64 * rounds + wave * 16 + i;
   int nw = 0, wlo = 0, pos0 = 0;
-  if (is_win) {
-    const int p = q_pos[r];
-    pos0 = swa_pos0[b];
-    wlo = max(p - W + 1, pos0);
-    nw = max(0, min(p, pos0 + S - 1) - wlo + 1);
+  float wscale = 1.0f;
+  if constexpr (WIN) {
+    const int p = a.q_pos[r];
+    pos0 = a.swa_pos0[b];
+    wscale = a.swa_scale[b];
+    wlo = max(p - a.W + 1, pos0);
+    nw = max(0, min(p, pos0 + a.S - 1) - wlo + 1);
   }
 
   // ---- loads, in dependency order: the index, then the query, then the row
-  auto load_ix = [&](int e) -> int { return (!is_win && e < K) ? idx[(int64_t)r * K + e] : -1; };
+  // (a row with K == 0 still has one global split, and idx may be null)
+  auto load_ix = [&](int e) -> int {
+    return (WIN || a.K == 0) ? 0 : a.idx[(int64_t)r * a.K + min(e, a.K - 1)];
+  };
   int ix = load_ix(e0);
   uint32_t rq[NM][8];
   {
-    const uint16_t* qr = q + ((int64_t)r * 16 + i) * D;
+    const uint16_t* qr = a.q + ((int64_t)r * 16 + i) * D;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const uint4 a = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g);
+      const uint4 u = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g);
       const uint4 c = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g + 8);
-      rq[m][0] = a.x; rq[m][1] = a.y; rq[m][2] = a.z; rq[m][3] = a.w;
+      rq[m][0] = u.x; rq[m][1] = u.y; rq[m][2] = u.z; rq[m][3] = u.w;
       rq[m][4] = c.x; rq[m][5] = c.y; rq[m][6] = c.z; rq[m][7] = c.w;
     }
   }
   uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
   bool valid;
   auto load_row = [&](int e) {
-    if (!is_win) {
-      valid = ix >= 0 && ix < cap;
-      const int64_t row = (int64_t)b * cap + (valid ? ix : 0);
-      const uint8_t* cr = codes + row * (D / 2);
-      const uint8_t* sr = scales + row * (D / 16);
+    if constexpr (!WIN) {
+      valid = e < a.K && ix >= 0 && ix < a.cap;
+      const int64_t row = (int64_t)b * a.cap + (valid ? ix : 0);
+      const uint8_t* cr = a.codes + row * (D / 2);
+      const uint8_t* sr = a.scales + row * (D / 16);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
@@ -265,8 +282,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
       }
     } else {
       valid = e < nw;
-      const int64_t row = (int64_t)b * S + (valid ? (wlo - pos0 + e) : 0);
-      const uint8_t* wr = swa + row * D;
+      const int64_t row = (int64_t)b * a.S + (valid ? (wlo - pos0 + e) : 0);
+      const uint8_t* wr = a.swa + row * D;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
@@ -278,6 +295,9 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     }
   };
   load_row(e0);
+  // keep the row loads ahead of the query conversion (the scheduler would
+  // otherwise sink them below it, after the query has arrived)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- query fragments (head i), scaled per head into fp16 range
   f16x8 qa[NM][2];
@@ -308,8 +328,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   int er[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) er[rr] = __shfl(qexp, 4 * g + rr, kWave);
-  const float wscale = is_win ? swa_scale[b] : 1.0f;
-  const float lscale = sm_scale * wscale;
+  const float lscale = a.sm_scale * wscale;
 
   // running softmax state of heads 4g + rr, and this wave's P.V tiles
   float mh[4], lh[4];
@@ -321,21 +340,23 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // this lane's transposed-read address in the V tile (see v_operand)
+  const _Float16* vt = Vs + (8 * g + (i >> 2)) * VST + wave * CPW + 4 * (i & 3);
 
   for (int rnd = 0; rnd < rounds; ++rnd) {
-    if (rnd > 0) {
+    if (MULTI && rnd > 0) {
       __syncthreads();  // the previous round's reads of Vs and Ps are done
       load_row(e0 + 64 * rnd);
     }
-    if (rnd + 1 < rounds) ix = load_ix(e0 + 64 * (rnd + 1));  // next round's index, in flight
+    if (MULTI && rnd + 1 < rounds) ix = load_ix(e0 + 64 * (rnd + 1));  // next round's index
     // ---- dequantize this wave's tile, logits (rows = heads 4g + rr, column = entry i)
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
     {
       _Float16* vrow = Vs + (wave * 16 + i) * VST;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         f16x8 k0, k1;
-        if (!is_win) {
+        if constexpr (!WIN) {
           const f16x2 s2 = scale_pair(sc[m]);
           k0 = fp4x8_to_f16(w0[m], s2);
           k1 = fp4x8_to_f16(w1[m], s2);
@@ -347,8 +368,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
           v.w = w3[m];
           e4m3x16_to_f16(v, k0, k1);
         }
-        acc = mfma16x16x32(qa[m][0], k0, acc);
-        acc = mfma16x16x32(qa[m][1], k1, acc);
+        acc0 = mfma16x16x32(qa[m][0], k0, acc0);
+        acc1 = mfma16x16x32(qa[m][1], k1, acc1);
         if (m < NMV) {
           *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0;
           *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
@@ -359,7 +380,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     float lg[4], alpha[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      lg[rr] = valid ? ldexpf(acc[rr], -er[rr]) * lscale : -INFINITY;
+      lg[rr] = valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * lscale : -INFINITY;
       const float mx = row16_max(lg[rr]);
       if (i == 0) red_max[wave][4 * g + rr] = mx;
     }
@@ -387,97 +408,73 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) o[nt][rr] *= alpha[rr];
-      const int ch = wave * CPW + nt * 16 + i;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
-        f16x8 vb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vb[j] = Vs[(32 * ks + 8 * g + j) * VST + ch];
-        o[nt] = mfma16x16x32(pa, vb, o[nt]);
+        const _Float16* vp = vt + 32 * ks * VST + 16 * nt;
+        o[nt] = mfma16x16x32(pa, v_operand(vp, vp + 4 * VST), o[nt]);
       }
     }
   }
 
   // ---- partial result of this split: o[16][DV], m[16], l[16]
-  float* prow = part + (int64_t)r * nsplit * PSTRIDE;
-  float* pb = prow + (int64_t)sidx * PSTRIDE;
+  float* pb = a.part + ((int64_t)r * a.nsplit + sidx) * PSTRIDE;
   static_assert(NT % 2 == 0, "tiles stored in pairs");
 #pragma unroll
   for (int nt = 0; nt < NT; nt += 2)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      st_pair<FUSED>(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
-                     o[nt + 1][rr] * wscale);
+      st_pair(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
+              o[nt + 1][rr] * wscale);
   // running max and sum of heads 4g + rr, written by lanes i == 0 as pairs
   if (wave == 0 && i == 0) {
-    st_pair<FUSED>(pb + 16 * DV + 4 * g, mh[0], mh[1]);
-    st_pair<FUSED>(pb + 16 * DV + 4 * g + 2, mh[2], mh[3]);
-    st_pair<FUSED>(pb + 16 * DV + 16 + 4 * g, lh[0], lh[1]);
-    st_pair<FUSED>(pb + 16 * DV + 16 + 4 * g + 2, lh[2], lh[3]);
-  }
-  if constexpr (FUSED) {
-    // publish the partial, then wait for the row's other splits
-    __shared__ int s_ok;
-    uint32_t* arrive = cnt + (int64_t)r * cnt_stride;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
-    __syncthreads();
-    if (tid == 0) {
-      __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int ok = 0;
-      for (int it = 0; it < kSpinLimit; ++it) {
-        if (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-            (uint32_t)nsplit) {
-          ok = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      s_ok = ok;
-    }
-    __syncthreads();
-    const bool ok = s_ok != 0;
-    // this block's slice of the row's output units
-    constexpr int NU = 16 * DV / 2;
-    const int per = (NU + nsplit - 1) / nsplit;
-    const int u0 = min(sidx * per, NU), u1 = min(u0 + per, NU);
-    merge_slice<DV, true>(prow, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
-                    lse ? lse + (int64_t)r * 16 : nullptr, lse && sidx == 0, ok,
-                    reinterpret_cast<float*>(Vs));
-    // the last block to leave clears the row's counters for the next call
-    if (tid == 0) {
-      uint32_t* leave = arrive + 1;
-      if (__hip_atomic_fetch_add(leave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          (uint32_t)nsplit - 1u) {
-        __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(leave, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    st_pair(pb + 16 * DV + 4 * g, mh[0], mh[1]);
+    st_pair(pb + 16 * DV + 4 * g + 2, mh[2], mh[3]);
+    st_pair(pb + 16 * DV + 16 + 4 * g, lh[0], lh[1]);
+    st_pair(pb + 16 * DV + 16 + 4 * g + 2, lh[2], lh[3]);
   }
 }
 
-// Merge kernel for grids that cannot all be resident: block (x, r) merges
-// units [256x, 256x + 256) of row r.
+// Block (s, r): split s of query row r (global entries for s < nsg, window
+// entries after).
+template <int D, int DV, bool MULTI>
+__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
+  extern __shared__ _Float16 Vs[];  // [64 entries][vs_stride]
+  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
+  __shared__ float red_max[4][16];
+  __shared__ float red_sum[4][16];
+  const int r = blockIdx.y, sidx = blockIdx.x;
+  if (sidx >= a.nsg)
+    split_body<D, DV, true, MULTI>(a, r, sidx, Vs, Ps, red_max, red_sum);
+  else
+    split_body<D, DV, false, MULTI>(a, r, sidx, Vs, Ps, red_max, red_sum);
+}
+
+// Merge kernel: block (x, r) merges output units [x ublk, (x + 1) ublk) of
+// row r.
 template <int DV>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
-                                                           int32_t nsplit, float* __restrict__ out,
+                                                           int32_t nsplit, int32_t ublk,
+                                                           float* __restrict__ out,
                                                            float* __restrict__ lse) {
   extern __shared__ float ml[];
   constexpr int PSTRIDE = 16 * DV + 32;
   constexpr int NU = 16 * DV / 2;
   const int r = blockIdx.y;
-  const int u0 = blockIdx.x * 256, u1 = min(u0 + 256, NU);
-  merge_slice<DV, false>(part + (int64_t)r * nsplit * PSTRIDE, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
-                  lse ? lse + (int64_t)r * 16 : nullptr, lse && blockIdx.x == 0, true, ml);
+  const int u0 = blockIdx.x * ublk, u1 = min(u0 + ublk, NU);
+  merge_slice<DV>(part + (int64_t)r * nsplit * PSTRIDE, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
+                  lse ? lse + (int64_t)r * 16 : nullptr, lse && blockIdx.x == 0, ml);
 }
 
-size_t attn_lds_bytes(int32_t dv) { return (size_t)64 * (dv + 8) * sizeof(_Float16); }
+size_t attn_lds_bytes(int32_t dv) {
+  return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
+}
 
 static size_t merge_lds_bytes(int32_t nsplit) {
   return (size_t)nsplit * 32 * sizeof(float) + 256 * sizeof(float2);
 }
 
-// Blocks of the fused kernel that fit on the device at once.
+// Blocks of the split kernel that fit on the device at once.
 template <typename F>
 static int64_t resident_blocks(F kernel, size_t lds) {
   static int64_t cached = -1;
@@ -502,10 +499,10 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   const size_t lds = attn_lds_bytes(DV);
   static bool lds_raised = false;
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, false>,
+      e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)attn_combine_kernel<DV>,
@@ -514,9 +511,10 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  // One round (64 entries) per split when the whole grid fits on the device
-  // and the splits merge in the same launch; with many query rows, splits of
-  // several rounds keep the partials few.
+  // An empty window array contributes no entries (its pointers may be null).
+  if (S == 0) W = 0;
+  // One round (64 entries) per split unless the grid would be many times the
+  // device: then splits of several rounds keep the partials few.
   const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
   int32_t rounds = 1;
   AttnSplit sp = attn_split(K, W, rounds);
@@ -524,23 +522,21 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
     rounds *= 2;
     sp = attn_split(K, W, rounds);
   }
+  const AttnArgs args{q, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos,
+                      sm_scale, w.part, sp.nsg, sp.nsplit, rounds, row0};
   const dim3 grid((unsigned)sp.nsplit, (unsigned)rows);
-  const bool fused = rounds == 1 && merge_lds_bytes(sp.nsplit) <= lds && w.cnt != nullptr &&
-                     (int64_t)sp.nsplit * rows <= cap_blocks;
-  if (fused) {
-    CSA2_KERNEL(true, true, (sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, q, T, codes,
-                       scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
-                       sp.nsg, sp.nsplit, rounds, row0, out, lse, w.cnt, w.cnt_stride);
-    return hipGetLastError();
-  }
-  CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, q, T, codes,
-                     scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale, w.part,
-                     sp.nsg, sp.nsplit, rounds, row0, out, lse, w.cnt, w.cnt_stride);
+  if (rounds > 1)
+    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, args);
+  else
+    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Merge: slices of 64 units (4 threads per unit) while the grid is small,
+  // of 256 units once the rows alone fill the device.
   constexpr int NU = 16 * DV / 2;
-  CSA2_KERNEL(false, true, (attn_combine_kernel<DV>), dim3((NU + 255) / 256, (unsigned)rows), dim3(256),
-                     merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, out, lse);
+  const int32_t ublk = (int64_t)rows * (NU / 256) >= 512 ? 256 : 64;
+  CSA2_KERNEL(false, true, (attn_combine_kernel<DV>), dim3((NU + ublk - 1) / ublk, (unsigned)rows),
+              dim3(256), merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, ublk, out, lse);
   return hipGetLastError();
 }
 

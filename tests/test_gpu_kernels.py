@@ -293,6 +293,27 @@ def test_sparse_attn_no_entries():
     assert (host(out) == 0).all() and np.isneginf(host(lse)).all()
 
 
+def test_sparse_attn_window_without_rows():
+    """W > 0 over an empty window array (S = 0, no window pointers): only the
+    Top-K entries are attended."""
+    N, K = 3000, 200
+    codes, scales, _, _ = _attn_case(5, N)
+    rng = np.random.default_rng(5)
+    idx = np.sort(rng.choice(N, K, replace=False)).astype(np.int32)[None]
+    q = torch.randn(1, 16, 576, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    out = torch.full((1, 16, 512), np.nan, device="cuda")
+    lse = torch.full((1, 16), np.nan, device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(1, K, 128, 512))
+    sm = float(np.float32(0.05))
+    api.sparse_attn(q.cuda(), 1, 1, api.cache(dev(codes), dev(scales), 576, N), dev(idx), K,
+                    None, None, None, 0, 128, dev(np.array([N - 1], np.int32)), sm, 512, out, lse, ws)
+    torch.cuda.synchronize()
+    o, l = oracle.sparse_attn(q[0].float().numpy(), codes, scales, idx[0],
+                              np.zeros((0, 576), np.uint8), 1.0, sm, 512)
+    assert_attention_close(host(out)[0], o, what="S=0")
+    assert np.allclose(host(lse)[0], l, atol=1e-4, rtol=1e-5)
+
+
 def test_sparse_attn_small_dims_and_batch():
     """D = dv = 128 kernel variant, several sequences."""
     B, N, K = 3, 2000, 300
