@@ -27,12 +27,21 @@
 // The block also builds a histogram of the top 12 bits of each score's
 // ordered key and adds it to one of the row's global histogram copies, which
 // the Top-K select pass then uses to find the bin holding the K-th score.
+#include <type_traits>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
 
-template <int NCH, int TPA, int GT>  // 128-channel chunks, tiles per accumulator, tiles per group
+// Two scale bytes (low half of `word`) as fp16 (exact: E4M3 lies inside
+// fp16's normal range).
+__device__ __forceinline__ f16x2 scale_pair2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+}
+
+template <int NCH, int TPA, int GT, bool POOL>  // 128-channel chunks, tiles per accumulator,
+                                                // tiles per group, positions from a pool list
 __global__ __launch_bounds__(256) void index_score_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
@@ -51,12 +60,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int r = blockIdx.y;
   const int b = (row0 + r) / T;
   // visible entries, clamped to what the score row and the key list hold
-  const int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), pool ? (int64_t)P : cap);
+  const int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), POOL ? (int64_t)P : cap);
   const int64_t start = (int64_t)blockIdx.x * chunk;
   if (start >= nv) return;  // uniform for the whole block
   const int64_t end = min(nv, start + chunk);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: kept in a scalar register, the whole-group
+  // test below is a scalar branch
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
 
   if (hist) {
@@ -65,45 +77,64 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 
   const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
   const uint8_t* sbase = scales + (int64_t)b * cap * ROWS;
-  const int32_t* prow = pool ? pool + (int64_t)r * P : nullptr;
+  const int32_t* prow = POOL ? pool + (int64_t)r * P : nullptr;
   float* srow = scores + (int64_t)r * n_out;
 
   // Each wave takes groups of GT consecutive tiles (GT KiB of contiguous
   // codes for 128 channels in flat mode); the four waves of a round cover
   // 4*GT consecutive tiles.  The next group's loads are issued before the
-  // current group is computed.
+  // current group is computed, into the other of two register buffers.
+  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
+  // scales; they are fetched as the aligned 32-bit word holding them.
   const int ntiles = (int)((end - start + 15) >> 4);
   const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
-  auto row_of = [&](int tile) -> int64_t {
-    int64_t s = start + (int64_t)tile * 16 + i;
-    if (s >= end) s = end - 1;  // clamp: keep the load in bounds, masked later
-    return prow ? (int64_t)prow[s] : s;
-  };
-  // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
-  // scales; they are fetched as the aligned 32-bit word holding them, so
-  // nothing has to wait for the loads until the group is computed.
-  auto load_group = [&](int rnd, u32x4 (&cw)[GT][NCH], uint32_t (&sw)[GT][NCH]) {
-    int64_t rows[GT];
+  // Whole chunks of a flat scan read every group at fixed offsets from one
+  // address; the last chunk of a row (and pool lists) compute each tile's
+  // rows, clamped to the range (lanes past the end reload the last position;
+  // their scores are masked).  Each variant is straight-line code.
+  auto load_group = [&](auto per_tile, int rnd, u32x4 (&cw)[GT][NCH], uint32_t (&sw)[GT][NCH]) {
+    const int tile0 = (rnd * 4 + wave) * GT;
+    if constexpr (!decltype(per_tile)::value) {
+      const int64_t p0 = start + (int64_t)tile0 * 16;
+      const uint8_t* cp = cbase + (p0 + i) * ROWB + 16 * g;
+      const uint8_t* sp = sbase + (p0 + i) * ROWS + 4 * (g >> 1);
 #pragma unroll
-    for (int t = 0; t < GT; ++t) rows[t] = row_of((rnd * 4 + wave) * GT + t);
+      for (int t = 0; t < GT; ++t)
 #pragma unroll
-    for (int t = 0; t < GT; ++t) {
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          cw[t][c2] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(cp + t * 16 * ROWB + 64 * c2));
+          sw[t][c2] = *reinterpret_cast<const uint32_t*>(sp + t * 16 * ROWS + 8 * c2);
+        }
+    } else {
+      int64_t rows[GT];
 #pragma unroll
-      for (int c2 = 0; c2 < NCH; ++c2) {
-        cw[t][c2] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(cbase + rows[t] * ROWB + 64 * c2 + 16 * g));
-        sw[t][c2] =
-            *reinterpret_cast<const uint32_t*>(sbase + rows[t] * ROWS + 8 * c2 + 4 * (g >> 1));
+      for (int t = 0; t < GT; ++t) {
+        const int64_t s = min(start + (int64_t)(tile0 + t) * 16 + i, end - 1);
+        rows[t] = POOL ? (int64_t)prow[s] : s;
       }
+#pragma unroll
+      for (int t = 0; t < GT; ++t)
+#pragma unroll
+        for (int c2 = 0; c2 < NCH; ++c2) {
+          cw[t][c2] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(cbase + rows[t] * ROWB + 64 * c2 + 16 * g));
+          sw[t][c2] =
+              *reinterpret_cast<const uint32_t*>(sbase + rows[t] * ROWS + 8 * c2 + 4 * (g >> 1));
+        }
     }
   };
   const int sshift = 16 * (g & 1);
 
-  u32x4 cw[GT][NCH], ncw[GT][NCH];
-  uint32_t sw[GT][NCH], nsw[GT][NCH];
+  const bool whole = !POOL && chunk == kScoreChunk && end - start == chunk;  // block-uniform
+  u32x4 cwA[GT][NCH], cwB[GT][NCH];
+  uint32_t swA[GT][NCH], swB[GT][NCH];
   // the first group is requested before the query is prepared, so the
   // scan's first HBM round trip overlaps the query's
-  if (nrounds > 0) load_group(0, cw, sw);
+  if (nrounds > 0) {
+    if (whole) load_group(std::false_type{}, 0, cwA, swA);
+    else load_group(std::true_type{}, 0, cwA, swA);
+  }
 
   // ---- query fragments: MFMA row i holds head i % HG of tile slot i / HG
   const int hrow = i % HG, srow_slot = i / HG;
@@ -155,8 +186,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const bool owner = (g % GPS) == 0;
   if (hist) __syncthreads();
 
-  for (int rnd = 0; rnd < nrounds; ++rnd) {
-    if (rnd + 1 < nrounds) load_group(rnd + 1, ncw, nsw);
+  auto compute_group = [&](int rnd, const u32x4 (&cw)[GT][NCH], const uint32_t (&sw)[GT][NCH]) {
 #pragma unroll
     for (int a = 0; a < NACC; ++a) {
       f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -165,9 +195,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
         const int t = a * TPA + sl;
 #pragma unroll
         for (int c2 = 0; c2 < NCH; ++c2) {
-          const uint32_t s2b = sw[t][c2] >> sshift;
-          const f16x2 s_lo = scale_pair(s2b & 0xFFu);
-          const f16x2 s_hi = scale_pair((s2b >> 8) & 0xFFu);
+          const f16x2 sp = scale_pair2(sw[t][c2] >> sshift);
+          const f16x2 s_lo = {sp[0], sp[0]}, s_hi = {sp[1], sp[1]};
           acc = mfma16x16x32(qv[sl][c2][0], fp4x8_to_f16(cw[t][c2].x, s_lo), acc);
           acc = mfma16x16x32(qv[sl][c2][1], fp4x8_to_f16(cw[t][c2].y, s_lo), acc);
           acc = mfma16x16x32(qv[sl][c2][2], fp4x8_to_f16(cw[t][c2].z, s_hi), acc);
@@ -187,14 +216,27 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       if (owner) srow[min(s, end - 1)] = part;
       if (owner && s < end && hist) atomicAdd(&lhist[score_key(part) >> kHistShift], 1u);
     }
-    if (rnd + 1 < nrounds) {
+  };
+  // Rounds in pairs, alternating the two buffers.  A whole chunk has a fixed
+  // number of rounds and is unrolled completely, so every load and wait is
+  // placed at compile time.
+  if (whole) {
+    constexpr int NR = kScoreChunk / (64 * GT);
+    static_assert(NR % 2 == 0 && NR * 64 * GT == kScoreChunk, "whole chunks");
 #pragma unroll
-      for (int t = 0; t < GT; ++t)
-#pragma unroll
-        for (int c2 = 0; c2 < NCH; ++c2) {
-          cw[t][c2] = ncw[t][c2];
-          sw[t][c2] = nsw[t][c2];
-        }
+    for (int rnd = 0; rnd < NR; rnd += 2) {
+      load_group(std::false_type{}, rnd + 1, cwB, swB);
+      compute_group(rnd, cwA, swA);
+      if (rnd + 2 < NR) load_group(std::false_type{}, rnd + 2, cwA, swA);
+      compute_group(rnd + 1, cwB, swB);
+    }
+  } else {
+    for (int rnd = 0; rnd < nrounds; rnd += 2) {
+      if (rnd + 1 < nrounds) load_group(std::true_type{}, rnd + 1, cwB, swB);
+      compute_group(rnd, cwA, swA);
+      if (rnd + 1 >= nrounds) break;
+      if (rnd + 2 < nrounds) load_group(std::true_type{}, rnd + 2, cwA, swA);
+      compute_group(rnd + 1, cwB, swB);
     }
   }
   if (hist) {
@@ -375,9 +417,16 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   const int64_t nchunks = (n_max + chunk - 1) / chunk;
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
 #define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \
-  CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT>), grid, block, 0, st, codes, scales, cap, \
-                     q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, hist,             \
-                     hist_stride, hist_copies, chunk, row0)
+  do {                                                                                         \
+    if (pool)                                                                                  \
+      CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT, true>), grid, block, 0, st,    \
+                  codes, scales, cap, q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, \
+                  hist, hist_stride, hist_copies, chunk, row0);                                \
+    else                                                                                       \
+      CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT, false>), grid, block, 0, st,   \
+                  codes, scales, cap, q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, \
+                  hist, hist_stride, hist_copies, chunk, row0);                                \
+  } while (0)
   switch (DI / 128) {
     case 1:
       if (HI <= 4) CSA2_IS_LAUNCH(1, 4, 8);
