@@ -177,26 +177,73 @@ __global__ __launch_bounds__(kSelThreads) void topk_cut_kernel(const int32_t* __
   if (threadIdx.x == 0) w.cut[(int64_t)r * w.ctr_stride] = (uint32_t)s_b1;
 }
 
+// Radix selection of the need-th largest rank value among C candidates
+// (all sharing the top 12 key bits): 11-bit digits at shifts 41, 30, 19, 8,
+// then 8 bits at 0; stops once a whole bucket is taken.  for_each(f) calls f
+// on every candidate (each once, spread over the block's threads).  Returns
+// the threshold: the candidates >= it (low 52 bits compared) are the need
+// largest.  All NT threads call it.
+template <int NT, typename ForEach>
+__device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tmp,
+                                    ForEach&& for_each) {
+  __shared__ int s_dig;
+  __shared__ uint32_t s_dig_above;
+  const int tid = threadIdx.x;
+  if (need == 0) return ~0ull;
+  uint64_t prefix = 0;
+  uint32_t rem = need;
+  for (int p = 0; p < 5; ++p) {
+    const int sh = p < 4 ? 41 - 11 * p : 0, wd = p < 4 ? 11 : 8;
+    const int nb = 1 << wd;
+    for (int j = tid; j < 2048; j += NT) rhist[j] = 0u;
+    if (tid == 0) {
+      s_dig = 0;
+      s_dig_above = 0;
+    }
+    __syncthreads();
+    const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
+    for_each([&](uint64_t x) {
+      if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
+    });
+    __syncthreads();
+    // digit d with count(> d) < rem <= count(>= d); 2 bins per thread
+    const int b0 = 2 * tid;
+    const uint32_t c0v = (b0 < nb) ? rhist[b0] : 0u, c1v = (b0 + 1 < nb) ? rhist[b0 + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(c0v + c1v, tmp, &tot);
+    const uint32_t above = tot - ex - c0v - c1v;
+    if (above < rem && above + c1v >= rem) {
+      s_dig = b0 + 1;
+      s_dig_above = above;
+    } else if (above + c1v < rem && above + c1v + c0v >= rem) {
+      s_dig = b0;
+      s_dig_above = above + c1v;
+    }
+    __syncthreads();
+    const uint32_t d = (uint32_t)s_dig;
+    rem -= s_dig_above;
+    prefix |= (uint64_t)d << sh;
+    const bool whole_bucket = rhist[d] == rem;
+    __syncthreads();
+    if (whole_bucket) break;
+  }
+  return prefix;
+}
+
 // Completion of row r by its last block (all select blocks of the row have
-// written their regions and counts).
-// With bm_words > 0 the kept slots are marked in an LDS bitmap of bm_words
-// words (one bit per slot) and read back in slot order; otherwise they are
-// listed (kept outright, then chosen, each in slot order) and merged.
+// written their regions and counts), for rows too long for the bitmap: the
+// kept slots are listed (kept outright, then chosen, each in slot order) and
+// merged.
 __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
                            int32_t k, int nblk, int32_t* __restrict__ idx_out,
                            int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
-                           int32_t bm_words, int32_t chunk, uint32_t* smem, uint32_t* tmp) {
+                           int32_t chunk, uint32_t* smem, uint32_t* tmp) {
   constexpr int NT = kSelThreads;
-  const bool use_bm = bm_words > 0;
   uint32_t* rhist = smem;                      // 2048 radix bins
   uint32_t* offA = rhist + 2048;               // nblk + 1
   uint32_t* offE = offA + (nblk + 1);          // nblk + 1
-  uint32_t* list = offE + (nblk + 1);          // k kept slots, or the bitmap
-  uint32_t* bm = list;
-  const int xwords = use_bm ? bm_words : k;
-  uint64_t* cl = reinterpret_cast<uint64_t*>(list + ((xwords + 1) & ~1));  // lds_cand candidates
-  __shared__ int s_dig;
-  __shared__ uint32_t s_dig_above;
+  uint32_t* list = offE + (nblk + 1);          // k kept slots
+  uint64_t* cl = reinterpret_cast<uint64_t*>(list + ((k + 1) & ~1));  // lds_cand candidates
   const int tid = threadIdx.x;
   int32_t* orow = idx_out + (int64_t)r * k;
   const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
@@ -206,12 +253,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
     if (count_out && tid == 0) count_out[r] = (int32_t)nv;
     return;
   }
-  if (use_bm) {
-    uint4* b4 = reinterpret_cast<uint4*>(bm);  // bm_words is a multiple of 4
-    for (int j = tid; j < bm_words / 4; j += NT) b4[j] = make_uint4(0, 0, 0, 0);
-  }
-  // ---- per-block counts -> offsets (the scans' barriers also order the
-  // bitmap clearing before its first use)
+  // ---- per-block counts -> offsets
   const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
   constexpr int kMaxPer = (int)(kMaxTopkN / kTopkChunk / NT);  // blocks per thread
   static_assert(kMaxPer >= 1 && kMaxPer <= 8, "counts held in registers");
@@ -297,8 +339,7 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
         for (int u = 0; u < 8; ++u) {
           const uint32_t i = i0 + u * tpb;
           if (i < na) {
-            if (use_bm) atomicOr(&bm[ta[u] >> 5], 1u << (ta[u] & 31));
-            else list[a_lo + i] = ta[u];
+            list[a_lo + i] = ta[u];
           }
           if (i < ne) cl[e_lo + i] = tc[u];
         }
@@ -323,83 +364,8 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
       }
     }
   };
-  // ---- radix selection of the need-th largest rank value among the
-  // candidates (all share the 12 top bits b1): 11-bit digits at shifts 41,
-  // 30, 19, 8, then 8 bits at 0; stop once a whole bucket is taken.
-  uint64_t thr = ~0ull;
-  if (need > 0) {
-    uint64_t prefix = 0;
-    uint32_t rem = need;
-    const int shifts[5] = {41, 30, 19, 8, 0};
-    const int widths[5] = {11, 11, 11, 11, 8};
-    for (int p = 0; p < 5; ++p) {
-      const int sh = shifts[p], wd = widths[p];
-      const int nb = 1 << wd;
-      for (int j = tid; j < 2048; j += NT) rhist[j] = 0u;
-      if (tid == 0) {
-        s_dig = 0;
-        s_dig_above = 0;
-      }
-      __syncthreads();
-      const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
-      for_each([&](uint64_t x) {
-        if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
-      });
-      __syncthreads();
-      // digit d with count(> d) < rem <= count(>= d); 2 bins per thread
-      const int b0 = 2 * tid;
-      const uint32_t c0v = (b0 < nb) ? rhist[b0] : 0u, c1v = (b0 + 1 < nb) ? rhist[b0 + 1] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_scan<NT>(c0v + c1v, tmp, &tot);
-      const uint32_t above = tot - ex - c0v - c1v;
-      if (above < rem && above + c1v >= rem) {
-        s_dig = b0 + 1;
-        s_dig_above = above;
-      } else if (above + c1v < rem && above + c1v + c0v >= rem) {
-        s_dig = b0;
-        s_dig_above = above + c1v;
-      }
-      __syncthreads();
-      const uint32_t d = (uint32_t)s_dig;
-      rem -= s_dig_above;
-      prefix |= (uint64_t)d << sh;
-      const bool whole_bucket = rhist[d] == rem;
-      __syncthreads();
-      if (whole_bucket) break;
-    }
-    thr = prefix;
-  }
+  const uint64_t thr = radix_threshold<NT>(need, rhist, tmp, for_each);
   const uint64_t low52 = (1ull << 52) - 1;
-  if (use_bm) {
-    // ---- chosen candidates into the bitmap, then every marked slot in
-    // slot order
-    if (need > 0) for_each([&](uint64_t x) {
-      if ((x & low52) >= thr) {
-        const uint32_t sl = rank_slot(x);
-        atomicOr(&bm[sl >> 5], 1u << (sl & 31));
-      }
-    });
-    __syncthreads();
-    const int wpt = (bm_words + NT - 1) / NT;
-    const int w0 = min(tid * wpt, bm_words), w1 = min(w0 + wpt, bm_words);
-    uint32_t cnt = 0;
-    for (int j = w0; j < w1; ++j) cnt += (uint32_t)__popc(bm[j]);
-    uint32_t tot;
-    uint32_t o = block_scan<NT>(cnt, tmp, &tot);
-    const uint32_t kept = min(tot, (uint32_t)k);
-    for (int j = w0; j < w1; ++j) {
-      uint32_t word = bm[j];
-      while (word) {
-        const uint32_t sl = 32u * (uint32_t)j + (uint32_t)(__ffs(word) - 1);
-        word &= word - 1u;
-        if (o < kept) orow[o] = sp ? sp[sl] : (int32_t)sl;
-        ++o;
-      }
-    }
-    for (uint32_t i = kept + tid; i < (uint32_t)k; i += NT) orow[i] = -1;
-    if (count_out && tid == 0) count_out[r] = (int32_t)kept;
-    return;
-  }
   // ---- chosen candidates (rank value within b1 >= thr), kept in slot
   // order: the concatenated candidate regions are slot-ordered.
   uint32_t kept;  // k unless the histogram disagreed with the scores
@@ -466,12 +432,190 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
   if (count_out && tid == 0) count_out[r] = (int32_t)kept;
 }
 
+// Rows of up to kBitmapSlots slots: the select blocks publish their kept
+// slots as a bitmap (one bit per slot, in the row's `above` region), so the
+// row's last block fetches, in one round trip, the per-block counts, the
+// bitmap and the first kSpec candidates of every block.  The chosen
+// candidates are marked in the same (LDS) bitmap, which is then read back in
+// slot order: wave w takes a contiguous run of words, 64 at a time, and
+// lane offsets come from wave prefix sums.  The output is staged in LDS and
+// written with whole-row coalesced stores.
+constexpr int64_t kBitmapSlots = int64_t(1) << 19;
+constexpr int kSpec = 64;
+
+__device__ void finish_row_bm(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
+                              int32_t k, int nblk, int32_t* __restrict__ idx_out,
+                              int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
+                              int32_t bm_words, int32_t chunk, uint32_t* smem, uint32_t* tmp) {
+  constexpr int NT = kSelThreads, NW = kSelWaves;
+  constexpr int kBW = (int)(kBitmapSlots / 64 / NT);                 // bitmap u64 words per thread
+  constexpr int kCP = (int)(kBitmapSlots / kTopkChunk) * kSpec / NT;  // early candidates per thread
+  static_assert(kBitmapSlots / kTopkChunk <= NT, "one block's counts per thread");
+  uint32_t* rhist = smem;                          // 2048 radix bins
+  uint32_t* offE = rhist + 2048;                   // nblk + 1
+  uint32_t* bm = offE + 2 * (nblk + 1);            // bm_words (8-byte aligned)
+  uint64_t* cl = reinterpret_cast<uint64_t*>(bm + bm_words);  // lds_cand candidates
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* orow = idx_out + (int64_t)r * k;
+  const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
+
+  if (nv <= k) {
+    for (int j = tid; j < k; j += NT) orow[j] = (j < nv) ? (sp ? sp[j] : j) : -1;
+    if (count_out && tid == 0) count_out[r] = (int32_t)nv;
+    return;
+  }
+  // ---- one round trip: counts, bitmap, early candidates (each thread
+  // issues all of its loads before using any; out-of-range ones are skipped
+  // rather than clamped, since many loads of one address serialise)
+  const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
+  const uint64_t* gbm = reinterpret_cast<const uint64_t*>(w.above + (int64_t)r * w.above_stride);
+  const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
+  const int nw64 = bm_words / 2;
+  const int vw64 = (int)((nv + 63) >> 6);  // words holding valid slots
+  uint32_t ca = 0u, ce = 0u;
+  if (tid < nblk) {
+    ca = ld_coh(crow + 2 * tid);
+    ce = ld_coh(crow + 2 * tid + 1);
+  }
+  uint64_t bw[kBW];
+#pragma unroll
+  for (int m = 0; m < kBW; ++m) bw[m] = (tid + m * NT < vw64) ? ld_coh(gbm + tid + m * NT) : 0ull;
+  uint64_t cv[kCP];
+#pragma unroll
+  for (int m = 0; m < kCP; ++m) {
+    const int f = tid + m * NT;
+    cv[m] = (f < nblk * kSpec) ? ld_coh(cbase + (int64_t)(f / kSpec) * chunk + f % kSpec) : 0ull;
+  }
+  uint64_t* bm64 = reinterpret_cast<uint64_t*>(bm);
+#pragma unroll
+  for (int m = 0; m < kBW; ++m) {
+    const int j = tid + m * NT;
+    if (j < nw64) bm64[j] = (j < vw64) ? bw[m] : 0ull;
+  }
+  // counts -> candidate offsets: thread b holds block b's counts, so the
+  // waves' own prefix sums and one exchange of wave totals suffice (the
+  // radix bins serve as scratch)
+  const uint32_t ie = wave_incl_scan(ce), ia = wave_incl_scan(ca);
+  if (lane == 63) {
+    rhist[wave] = ie;
+    rhist[NW + wave] = ia;
+  }
+  __syncthreads();
+  uint32_t A = 0, C = 0, eb0 = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const uint32_t te = rhist[x];
+    eb0 += (x < wave) ? te : 0u;
+    C += te;
+    A += rhist[NW + x];
+  }
+  if (tid < nblk) offE[tid] = eb0 + ie - ce;
+  if (tid == 0) offE[nblk] = C;
+  __syncthreads();
+  const uint32_t need = (uint32_t)k - min(A, (uint32_t)k);
+  const bool in_lds = C <= (uint32_t)lds_cand;
+  if (in_lds) {
+#pragma unroll
+    for (int m = 0; m < kCP; ++m) {
+      const int f = tid + m * NT, b = f / kSpec, i = f % kSpec;
+      if (b < nblk && (uint32_t)i < offE[b + 1] - offE[b]) cl[offE[b] + i] = cv[m];
+    }
+    // blocks with more than kSpec candidates: the rest, TPB threads per
+    // block, each with up to 8 loads in flight
+    constexpr int TPB = NT / (int)(kBitmapSlots / kTopkChunk);
+    for (int b0 = 0; b0 < nblk; b0 += NT / TPB) {
+      const int b = b0 + tid / TPB, j = tid % TPB;
+      const uint32_t eb = (b < nblk) ? offE[b + 1] - offE[b] : 0u;
+      for (uint32_t i0 = kSpec + j; i0 < eb; i0 += 8 * TPB) {
+        uint64_t t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = i0 + u * TPB;
+          t[u] = (i < eb) ? ld_coh(cbase + (int64_t)b * chunk + i) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * TPB < eb) cl[offE[b] + i0 + u * TPB] = t[u];
+      }
+    }
+  }
+  __syncthreads();
+  auto cand_at = [&](uint32_t c) -> uint64_t {
+    int lo = 0, hi = nblk - 1;  // block = last b with offE[b] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offE[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return ld_coh(cbase + (int64_t)lo * chunk + (c - offE[lo]));
+  };
+  auto for_each = [&](auto&& f) {
+    if (in_lds) {
+      for (uint32_t c = tid; c < C; c += NT) f(cl[c]);
+    } else {
+      for (uint32_t c = tid; c < C; c += NT) f(cand_at(c));
+    }
+  };
+  const uint64_t thr = radix_threshold<NT>(need, rhist, tmp, for_each);
+  const uint64_t low52 = (1ull << 52) - 1;
+  if (need > 0) for_each([&](uint64_t x) {
+    if ((x & low52) >= thr) {
+      const uint32_t sl = rank_slot(x);
+      atomicOr(&bm[sl >> 5], 1u << (sl & 31));
+    }
+  });
+  __syncthreads();
+  // ---- marked slots in slot order, over 64-bit words
+  const int WPW = ((nw64 + NW - 1) / NW + 63) & ~63;
+  const int wb = min(wave * WPW, nw64), we = min(wb + WPW, nw64);
+  uint32_t cnt = 0;
+  for (int j = wb + lane; j < we; j += 64) cnt += (uint32_t)__popcll(bm64[j]);
+  const uint32_t wtotal = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), 63);
+  if (lane == 0) tmp[wave] = wtotal;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const uint32_t t = tmp[x];
+    base += (x < wave) ? t : 0u;
+    tot += t;
+  }
+  const uint32_t kept = min(tot, (uint32_t)k);
+  // staged in the candidate area (no longer read) when it holds k slots
+  uint32_t* ob = (2 * (int64_t)lds_cand >= k) ? reinterpret_cast<uint32_t*>(cl) : nullptr;
+  uint32_t o = base;
+  for (int j0 = wb; j0 < we; j0 += 64) {
+    const int j = j0 + lane;
+    uint64_t word = (j < we) ? bm64[j] : 0ull;
+    const uint32_t c = (uint32_t)__popcll(word);
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t pos = o + incl - c;
+    o += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    while (word) {
+      const uint32_t sl = 64u * (uint32_t)j + (uint32_t)(__ffsll((unsigned long long)word) - 1);
+      word &= word - 1ull;
+      if (pos < kept) {
+        if (ob) ob[pos] = sl;
+        else orow[pos] = sp ? sp[sl] : (int32_t)sl;
+      }
+      ++pos;
+    }
+  }
+  if (ob) {
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) orow[j] = (j < (int)kept) ? (sp ? sp[ob[j]] : (int32_t)ob[j]) : -1;
+  } else {
+    for (uint32_t i = kept + tid; i < (uint32_t)k; i += NT) orow[i] = -1;
+  }
+  if (count_out && tid == 0) count_out[r] = (int32_t)kept;
+}
+
 template <int PL>  // scores per lane: a block takes 1024 * PL consecutive slots
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_select_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand, int32_t bm_words, bool use_cut) {
-  extern __shared__ uint32_t smem[];
+  extern __shared__ uint64_t smem64[];
+  uint32_t* smem = reinterpret_cast<uint32_t*>(smem64);
   __shared__ uint32_t tmp[kSelWaves];
   __shared__ uint32_t wtot[2][kSelWaves];  // kept / candidates per wave
   __shared__ int s_b1, s_last;
@@ -531,8 +675,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         ta += a;
         te += c;
       }
-      // write pass, in slot order
+      // write pass, in slot order: candidates listed; kept slots listed, or
+      // (bitmap rows) published as this wave's bitmap words
       uint32_t* ra = w.above + (int64_t)r * w.above_stride + (int64_t)blockIdx.x * kChunk;
+      uint64_t* gbm = reinterpret_cast<uint64_t*>(w.above + (int64_t)r * w.above_stride);
       uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kChunk;
       const uint64_t lt = lanemask_lt();
 #pragma unroll
@@ -542,7 +688,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         const bool ab = s < nv && bin > b1;
         const bool eq = s < nv && bin == b1;
         const uint64_t ma = __ballot(ab), me = __ballot(eq);
-        if (ab) st_coh(ra + oa + (uint32_t)__popcll(ma & lt), (uint32_t)s);
+        if (bm_words > 0) {
+          if (lane == 0) st_coh(gbm + ((wstart + 64 * j) >> 6), ma);
+        } else if (ab) {
+          st_coh(ra + oa + (uint32_t)__popcll(ma & lt), (uint32_t)s);
+        }
         if (eq) st_coh(rc + oe + (uint32_t)__popcll(me & lt), rank_value(keys[j], (uint32_t)s));
         oa += (uint32_t)__popcll(ma);
         oe += (uint32_t)__popcll(me);
@@ -567,8 +717,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, bm_words, kChunk, smem,
-             tmp);
+  if (bm_words > 0)
+    finish_row_bm(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, bm_words, kChunk,
+                  smem, tmp);
+  else
+    finish_row(r, nv, n, slot_pos, k, nblk, idx_out, count_out, w, lds_cand, kChunk, smem, tmp);
   // ---- leave the histogram copies zero for the next call (every block of
   // the row has read them)
   uint4* h4p = reinterpret_cast<uint4*>(rh);
@@ -600,7 +753,6 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   const int32_t nblk = topk_blocks(n_max, chunk);
   // LDS of the completing block: radix bins, 2 offset arrays, the kept-slot
   // bitmap (rows up to kBitmapSlots) or list, then as many candidates as fit.
-  constexpr int64_t kBitmapSlots = int64_t(1) << 19;
   constexpr size_t kBudget = 150 * 1024;
   const int32_t bm_words = (n <= kBitmapSlots) ? (int32_t)(((n + 31) / 32 + 3) & ~3) : 0;
   const int32_t xwords = bm_words > 0 ? bm_words : k;
