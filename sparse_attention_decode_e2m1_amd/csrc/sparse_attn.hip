@@ -50,135 +50,6 @@ __device__ __forceinline__ int partial_channel(int p) {
   return w * CPW + (2 * (rem / 32) + (rem & 1)) * 16 + (rem % 32) / 2;
 }
 
-// Merge of the splits of one query row into output units [u0, u1): unit u is
-// the slot pair (2(u % (dv/2)), +1) of head u / (dv/2).  `ml` is LDS for
-// nsplit x 32 floats plus 256 float2.  All threads of the block call it.
-// The split maxima/sums and the partial outputs a thread needs are all
-// requested before any is used, so the merge costs about one memory round
-// trip plus the reduction of the maxima.
-template <int DV>
-__device__ void merge_slice(const float* __restrict__ prow, int nsplit, int u0, int u1,
-                            float* __restrict__ orow, float* __restrict__ lrow, bool write_lse,
-                            float* ml) {
-  constexpr int PSTRIDE = 16 * DV + 32;
-  constexpr int UPH = DV / 2;  // units per head
-  constexpr int NU = 16 * UPH;
-  constexpr int KB = 20;       // partial loads in flight per thread
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ float s_M[16], s_L[16];
-  __shared__ float red[4][16];
-  const int nu = max(u1 - u0, 0);
-  int SUB = 1;  // threads per unit
-  while (SUB < 64 && SUB * 2 * nu <= 256) SUB *= 2;
-  const int per_pass = 256 / SUB;
-  float2* racc = reinterpret_cast<float2*>(ml + nsplit * 32);
-  const int nml = nsplit * 32;
-  for (int ub = 0; ub == 0 || ub < nu; ub += per_pass) {
-    const int uu = ub + tid / SUB, sub = tid % SUB;
-    const bool live = uu < nu;
-    const int u = min(u0 + uu, NU - 1);  // clamped: every load below stays in bounds
-    const int h = u / UPH, pp = 2 * (u % UPH);
-    const float* col = prow + h * DV + pp;
-    // Split maxima and sums (ml[s][0..15] = m, ml[s][16..31] = l) and this
-    // thread's partial outputs; indices are clamped rather than branched on.
-    const int nmp = nml / 2;  // pairs
-    float2 mlv[4];
-    if (ub == 0) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jp = min(k * 256 + tid, nmp - 1);
-        mlv[k] = ld_pair(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
-      }
-    }
-    float2 v[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) v[k] = ld_pair(col + (int64_t)min(sub + k * SUB, nsplit - 1) * PSTRIDE);
-    if (ub == 0) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jp = k * 256 + tid;
-        if (jp < nmp) {
-          ml[2 * jp] = mlv[k].x;
-          ml[2 * jp + 1] = mlv[k].y;
-        }
-      }
-      for (int jp = 4 * 256 + tid; jp < nmp; jp += 256) {  // beyond 64 splits
-        const float2 t = ld_pair(prow + (int64_t)(jp >> 4) * PSTRIDE + 16 * DV + 2 * (jp & 15));
-        ml[2 * jp] = t.x;
-        ml[2 * jp + 1] = t.y;
-      }
-      __syncthreads();
-      // per head hh: max and weighted sum over splits; lanes hh of the four
-      // 16-lane rows of the four waves take every 16th split
-      const int hh = lane & 15, qq = lane >> 4;
-      float mx = -INFINITY;
-      for (int s = wave * 4 + qq; s < nsplit; s += 16) mx = fmaxf(mx, ml[s * 32 + hh]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      if (qq == 0) red[wave][hh] = mx;
-      __syncthreads();
-      const float M = fmaxf(fmaxf(red[0][hh], red[1][hh]), fmaxf(red[2][hh], red[3][hh]));
-      float L = 0.0f;
-      for (int s = wave * 4 + qq; s < nsplit; s += 16) {
-        const float ms = ml[s * 32 + hh];
-        const float wv = (ms == -INFINITY) ? 0.0f : __expf(ms - M);
-        ml[s * 32 + hh] = wv;  // the max slot now holds the split's weight
-        L += wv * ml[s * 32 + 16 + hh];
-      }
-      L += shfl_xor(L, 16);
-      L += shfl_xor(L, 32);
-      __syncthreads();
-      if (qq == 0) red[wave][hh] = L;
-      __syncthreads();
-      if (tid < 16) {
-        s_M[tid] = M;
-        s_L[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      }
-      __syncthreads();
-      if (write_lse && tid < 16) {
-        const float Lt = s_L[tid];
-        lrow[tid] = (Lt > 0.0f) ? s_M[tid] + logf(Lt) : -INFINITY;
-      }
-    }
-    float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int s = sub + k * SUB;
-      const float wv = (live && s < nsplit) ? ml[s * 32 + h] : 0.0f;
-      acc.x += wv * v[k].x;
-      acc.y += wv * v[k].y;
-    }
-    // splits beyond the first KB per thread
-    for (int s0 = sub + KB * SUB; live && s0 < nsplit; s0 += KB * SUB) {
-#pragma unroll
-      for (int k = 0; k < KB; ++k) v[k] = ld_pair(col + (int64_t)min(s0 + k * SUB, nsplit - 1) * PSTRIDE);
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int s = s0 + k * SUB;
-        const float wv = (s < nsplit) ? ml[s * 32 + h] : 0.0f;
-        acc.x += wv * v[k].x;
-        acc.y += wv * v[k].y;
-      }
-    }
-    racc[tid] = acc;
-    __syncthreads();
-    if (live && sub == 0) {
-      float2 t = acc;
-      for (int k = 1; k < SUB; ++k) {
-        const float2 o = racc[tid + k];
-        t.x += o.x;
-        t.y += o.y;
-      }
-      const float L = s_L[h];
-      const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-      const int ch = partial_channel<DV>(pp);  // slot pp + 1 holds channel ch + 16
-      orow[h * DV + ch] = t.x * inv;
-      orow[h * DV + ch + 16] = t.y * inv;
-    }
-    __syncthreads();
-  }
-}
-
 // B operand of P.V straight from the row-major V tile: ds_read_b64_tr_b16
 // hands lane t of each 16-lane group element t % 4 of the 64-bit word
 // addressed by lane 4j + t / 4, as its element j.  With lane s addressing
@@ -450,28 +321,78 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
     split_body<D, DV, false, MULTI>(a, r, sidx, Vs, Ps, red_max, red_sum);
 }
 
-// Merge kernel: block (x, r) merges output units [x ublk, (x + 1) ublk) of
-// row r.
-template <int DV>
+// Merge kernel.  Unit u of row r is the value-slot pair (2(u % (dv/2)), +1)
+// of head u / (dv/2); SUB consecutive threads merge one unit, thread `sub`
+// taking splits sub, sub + SUB, ...  Each thread loads, per split, its pair
+// of the partial output and the split's max and sum for the unit's head,
+// all requested before any is used; the SUB threads agree on the running
+// maximum and add their shares with lane moves, so the merge needs no LDS
+// and no barrier:
+//   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L.
+template <int DV, int SUB, int KB>  // KB: splits per thread per pass
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
-                                                           int32_t nsplit, int32_t ublk,
-                                                           float* __restrict__ out,
+                                                           int32_t nsplit, float* __restrict__ out,
                                                            float* __restrict__ lse) {
-  extern __shared__ float ml[];
+  static_assert(SUB == 4, "lane moves below cover groups of four lanes");
   constexpr int PSTRIDE = 16 * DV + 32;
-  constexpr int NU = 16 * DV / 2;
-  const int r = blockIdx.y;
-  const int u0 = blockIdx.x * ublk, u1 = min(u0 + ublk, NU);
-  merge_slice<DV>(part + (int64_t)r * nsplit * PSTRIDE, nsplit, u0, u1, out + (int64_t)r * 16 * DV,
-                  lse ? lse + (int64_t)r * 16 : nullptr, lse && blockIdx.x == 0, ml);
+  constexpr int UPH = DV / 2;          // units per head
+  constexpr int UPB = 256 / SUB;       // units per block
+  const int r = blockIdx.y, tid = threadIdx.x, sub = tid % SUB;
+  const int u = blockIdx.x * UPB + tid / SUB;  // the grid covers the units exactly
+  const int h = u / UPH, pp = 2 * (u % UPH);
+  const float* prow = part + (int64_t)r * nsplit * PSTRIDE;
+  float Mrun = -INFINITY, L = 0.0f, nx = 0.0f, ny = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += SUB * KB) {
+    float2 ov[KB];
+    float mv[KB], lv[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int sc = min(s0 + sub + SUB * k, nsplit - 1);  // clamped: every load in bounds
+      const float* ps = prow + (int64_t)sc * PSTRIDE;
+      ov[k] = ld_pair(ps + h * DV + pp);
+      mv[k] = ps[16 * DV + h];
+      lv[k] = ps[16 * DV + 16 + h];
+    }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if (s0 + sub + SUB * k >= nsplit) mv[k] = -INFINITY;
+      cm = fmaxf(cm, mv[k]);
+    }
+    cm = fmaxf(cm, dpp_move<kDppXor1>(cm));
+    cm = fmaxf(cm, dpp_move<kDppXor2>(cm));
+    const float Mnew = fmaxf(Mrun, cm);
+    const float a = (Mnew == -INFINITY) ? 1.0f : __expf(Mrun - Mnew);
+    L *= a;
+    nx *= a;
+    ny *= a;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const float wv = (mv[k] == -INFINITY) ? 0.0f : __expf(mv[k] - Mnew);
+      L += wv * lv[k];
+      nx += wv * ov[k].x;
+      ny += wv * ov[k].y;
+    }
+    Mrun = Mnew;
+  }
+  L += dpp_move<kDppXor1>(L);
+  L += dpp_move<kDppXor2>(L);
+  nx += dpp_move<kDppXor1>(nx);
+  nx += dpp_move<kDppXor2>(nx);
+  ny += dpp_move<kDppXor1>(ny);
+  ny += dpp_move<kDppXor2>(ny);
+  if (sub == 0) {
+    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    const int ch = partial_channel<DV>(pp);  // slot pp + 1 holds channel ch + 16
+    float* orow = out + (int64_t)r * 16 * DV + h * DV;
+    orow[ch] = nx * inv;
+    orow[ch + 16] = ny * inv;
+    if (lse && pp == 0) lse[(int64_t)r * 16 + h] = (L > 0.0f) ? Mrun + logf(L) : -INFINITY;
+  }
 }
 
 size_t attn_lds_bytes(int32_t dv) {
   return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
-}
-
-static size_t merge_lds_bytes(int32_t nsplit) {
-  return (size_t)nsplit * 32 * sizeof(float) + 256 * sizeof(float2);
 }
 
 // Blocks of the split kernel that fit on the device at once.
@@ -504,10 +425,6 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)attn_combine_kernel<DV>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)merge_lds_bytes(kMaxSplits));
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
@@ -531,12 +448,18 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
     CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Merge: slices of 64 units (4 threads per unit) while the grid is small,
-  // of 256 units once the rows alone fill the device.
+  // four threads per output unit; each pass takes 4 KB splits
   constexpr int NU = 16 * DV / 2;
-  const int32_t ublk = (int64_t)rows * (NU / 256) >= 512 ? 256 : 64;
-  CSA2_KERNEL(false, true, (attn_combine_kernel<DV>), dim3((NU + ublk - 1) / ublk, (unsigned)rows),
-              dim3(256), merge_lds_bytes(sp.nsplit), st, w.part, sp.nsplit, ublk, out, lse);
+  const dim3 cgrid(NU / 64, (unsigned)rows);
+  if (sp.nsplit <= 16)
+    CSA2_KERNEL(false, true, (attn_combine_kernel<DV, 4, 4>), cgrid, dim3(256), 0, st, w.part,
+                sp.nsplit, out, lse);
+  else if (sp.nsplit <= 40)
+    CSA2_KERNEL(false, true, (attn_combine_kernel<DV, 4, 10>), cgrid, dim3(256), 0, st, w.part,
+                sp.nsplit, out, lse);
+  else
+    CSA2_KERNEL(false, true, (attn_combine_kernel<DV, 4, 16>), cgrid, dim3(256), 0, st, w.part,
+                sp.nsplit, out, lse);
   return hipGetLastError();
 }
 
