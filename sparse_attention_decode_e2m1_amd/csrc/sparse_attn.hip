@@ -310,7 +310,9 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
 // entries after).
 template <int D, int DV, bool MULTI>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
-  extern __shared__ _Float16 Vs[];  // [64 entries][vs_stride]
+  // 16-byte aligned: the V tile is written and read with 16- and 8-byte LDS
+  // accesses, so its base must not follow the static arrays unaligned
+  extern __shared__ __attribute__((aligned(16))) _Float16 Vs[];  // [64 entries][vs_stride]
   __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
   __shared__ float red_max[4][16];
   __shared__ float red_sum[4][16];
