@@ -126,9 +126,10 @@ void carve_ctl(Carve& c, int32_t rows, TopkWs* tw) {
     tw->ctr = ctl ? ctl + kHistWords : nullptr;
     tw->ctr_stride = kCtlWordsPerRow;
     tw->cut = ctl ? ctl + kHistWords + 1 : nullptr;
-    // Copies spread the histogram atomics of a row's many scoring blocks;
-    // with many rows per pass one copy keeps the select pass's reads small.
-    tw->hist_copies = rows <= 32 ? kMaxHistCopies : 1;
+    // Copies spread the histogram atomics of a row's many scoring blocks,
+    // but every select block reads all of them: two balance the two (measured
+    // at 256K positions x 4 rows); with many rows per pass, one.
+    tw->hist_copies = rows <= 32 ? 2 : 1;
   }
 }
 

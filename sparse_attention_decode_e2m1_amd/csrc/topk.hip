@@ -435,13 +435,14 @@ __device__ void finish_row(int r, int64_t nv, int64_t n, const int32_t* __restri
 // Rows of up to kBitmapSlots slots: the select blocks publish their kept
 // slots as a bitmap (one bit per slot, in the row's `above` region), so the
 // row's last block fetches, in one round trip, the per-block counts, the
-// bitmap and the first kSpec candidates of every block.  The chosen
+// bitmap and the first `spec` candidates of every block (as many as kCP
+// loads per thread allow, a power of two).  The chosen
 // candidates are marked in the same (LDS) bitmap, which is then read back in
 // slot order: wave w takes a contiguous run of words, 64 at a time, and
 // lane offsets come from wave prefix sums.  The output is staged in LDS and
 // written with whole-row coalesced stores.
 constexpr int64_t kBitmapSlots = int64_t(1) << 19;
-constexpr int kSpec = 64;
+constexpr int kCP = 8;  // early candidate loads per thread
 
 __device__ void finish_row_bm(int r, int64_t nv, int64_t n, const int32_t* __restrict__ slot_pos,
                               int32_t k, int nblk, int32_t* __restrict__ idx_out,
@@ -449,7 +450,6 @@ __device__ void finish_row_bm(int r, int64_t nv, int64_t n, const int32_t* __res
                               int32_t bm_words, int32_t chunk, uint32_t* smem, uint32_t* tmp) {
   constexpr int NT = kSelThreads, NW = kSelWaves;
   constexpr int kBW = (int)(kBitmapSlots / 64 / NT);                 // bitmap u64 words per thread
-  constexpr int kCP = (int)(kBitmapSlots / kTopkChunk) * kSpec / NT;  // early candidates per thread
   static_assert(kBitmapSlots / kTopkChunk <= NT, "one block's counts per thread");
   uint32_t* rhist = smem;                          // 2048 radix bins
   uint32_t* offE = rhist + 2048;                   // nblk + 1
@@ -480,11 +480,14 @@ __device__ void finish_row_bm(int r, int64_t nv, int64_t n, const int32_t* __res
   uint64_t bw[kBW];
 #pragma unroll
   for (int m = 0; m < kBW; ++m) bw[m] = (tid + m * NT < vw64) ? ld_coh(gbm + tid + m * NT) : 0ull;
+  int lspec = 0;  // log2 of candidates fetched early per block
+  while ((2 << lspec) * nblk <= NT * kCP && (2 << lspec) <= chunk) ++lspec;
+  const int spec = 1 << lspec;
   uint64_t cv[kCP];
 #pragma unroll
   for (int m = 0; m < kCP; ++m) {
     const int f = tid + m * NT;
-    cv[m] = (f < nblk * kSpec) ? ld_coh(cbase + (int64_t)(f / kSpec) * chunk + f % kSpec) : 0ull;
+    cv[m] = (f < nblk * spec) ? ld_coh(cbase + (int64_t)(f >> lspec) * chunk + (f & (spec - 1))) : 0ull;
   }
   uint64_t* bm64 = reinterpret_cast<uint64_t*>(bm);
 #pragma unroll
@@ -517,16 +520,16 @@ __device__ void finish_row_bm(int r, int64_t nv, int64_t n, const int32_t* __res
   if (in_lds) {
 #pragma unroll
     for (int m = 0; m < kCP; ++m) {
-      const int f = tid + m * NT, b = f / kSpec, i = f % kSpec;
+      const int f = tid + m * NT, b = f >> lspec, i = f & (spec - 1);
       if (b < nblk && (uint32_t)i < offE[b + 1] - offE[b]) cl[offE[b] + i] = cv[m];
     }
-    // blocks with more than kSpec candidates: the rest, TPB threads per
+    // blocks with more than spec candidates: the rest, TPB threads per
     // block, each with up to 8 loads in flight
     constexpr int TPB = NT / (int)(kBitmapSlots / kTopkChunk);
     for (int b0 = 0; b0 < nblk; b0 += NT / TPB) {
       const int b = b0 + tid / TPB, j = tid % TPB;
       const uint32_t eb = (b < nblk) ? offE[b + 1] - offE[b] : 0u;
-      for (uint32_t i0 = kSpec + j; i0 < eb; i0 += 8 * TPB) {
+      for (uint32_t i0 = spec + j; i0 < eb; i0 += 8 * TPB) {
         uint64_t t[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
