@@ -38,8 +38,6 @@ namespace csa2 {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kHistPerThread = kHistBins / kSelThreads;  // 4 bins per thread
-static_assert(kHistPerThread == 4, "one uint4 of each histogram copy per thread");
 
 // Device-coherent accesses for data one block writes and another block of
 // the same launch reads (agent scope: no full-cache write-back or invalidate).
@@ -119,45 +117,48 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32
   return off + inc - v;
 }
 
-// The row's 12-bit key histogram summed over its `copies` copies, bins
-// [4t, 4t+4) of thread t (1024 threads).
-__device__ __forceinline__ void load_hist4(const uint32_t* rh, int copies, uint32_t (&h4)[4]) {
-  uint4 hc[kHistCopies];
-#pragma unroll
-  for (int c = 0; c < kHistCopies; ++c)
-    hc[c] = (c < copies) ? *reinterpret_cast<const uint4*>(rh + c * kHistBins + 4 * threadIdx.x)
-                         : make_uint4(0, 0, 0, 0);
-  h4[0] = h4[1] = h4[2] = h4[3] = 0u;
-#pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) {
-    h4[0] += hc[c].x;
-    h4[1] += hc[c].y;
-    h4[2] += hc[c].z;
-    h4[3] += hc[c].w;
-  }
-}
-
 // The bin holding the k-th largest key: count(bins > b1) < k <= count(bins
-// >= b1).  Written to *b1 by the thread that finds it (left unchanged when
-// the histogram holds fewer than k keys); every thread calls it.
+// >= b1), from the row's 12-bit key histogram summed over its `copies`
+// copies (thread t of NT takes bins [t*BPT, (t+1)*BPT)).  Written to *b1 by
+// the thread that finds it (left unchanged when the histogram holds fewer
+// than k keys); every thread calls it.
+template <int NT>
 __device__ __forceinline__ void find_cut(const uint32_t* rh, int copies, int32_t k, uint32_t* tmp,
                                          int* b1) {
-  uint32_t h4[4];
-  load_hist4(rh, copies, h4);
-  const uint32_t sum = h4[0] + h4[1] + h4[2] + h4[3];
+  constexpr int BPT = kHistBins / NT, NV = BPT / 4;
+  static_assert(BPT % 4 == 0, "whole uint4 per thread");
+  uint4 hc[kHistCopies][NV];
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c)
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      hc[c][v] = (c < copies)
+                     ? *reinterpret_cast<const uint4*>(rh + c * kHistBins + BPT * threadIdx.x + 4 * v)
+                     : make_uint4(0, 0, 0, 0);
+  uint32_t h[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) h[j] = 0u;
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      h[4 * v] += hc[c][v].x;
+      h[4 * v + 1] += hc[c][v].y;
+      h[4 * v + 2] += hc[c][v].z;
+      h[4 * v + 3] += hc[c][v].w;
+    }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) sum += h[j];
   uint32_t total;
-  const uint32_t excl = block_scan<kSelThreads>(sum, tmp, &total);
+  const uint32_t excl = block_scan<NT>(sum, tmp, &total);
   const uint32_t above = total - excl - sum;  // keys in bins of higher threads
   if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
     uint32_t acc = above;
-    bool found = false;
 #pragma unroll
-    for (int j = 3; j >= 0; --j) {
-      if (!found && acc + h4[j] >= (uint32_t)k) {
-        *b1 = 4 * threadIdx.x + j;
-        found = true;
-      }
-      acc += h4[j];
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (acc < (uint32_t)k && acc + h[j] >= (uint32_t)k) *b1 = BPT * threadIdx.x + j;
+      acc += h[j];
     }
   }
   __syncthreads();
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_cut_kernel(const int32_t* __
   if (threadIdx.x == 0) s_b1 = 0x7FFFFFFF;
   __syncthreads();
   if (min((int64_t)n_valid[r] + nv_add, n) > k)
-    find_cut(w.hist + (int64_t)r * w.hist_stride, w.hist_copies, k, tmp, &s_b1);
+    find_cut<kSelThreads>(w.hist + (int64_t)r * w.hist_stride, w.hist_copies, k, tmp, &s_b1);
   if (threadIdx.x == 0) w.cut[(int64_t)r * w.ctr_stride] = (uint32_t)s_b1;
 }
 
@@ -206,18 +207,28 @@ __device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tm
       if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
     });
     __syncthreads();
-    // digit d with count(> d) < rem <= count(>= d); 2 bins per thread
-    const int b0 = 2 * tid;
-    const uint32_t c0v = (b0 < nb) ? rhist[b0] : 0u, c1v = (b0 + 1 < nb) ? rhist[b0 + 1] : 0u;
+    // digit d with count(> d) < rem <= count(>= d); BPT bins per thread
+    // (bins past nb were cleared, so they count zero)
+    constexpr int BPT = 2048 / NT;
+    const int b0 = BPT * tid;
+    uint32_t cv[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      cv[j] = rhist[b0 + j];
+      sum += cv[j];
+    }
     uint32_t tot;
-    const uint32_t ex = block_scan<NT>(c0v + c1v, tmp, &tot);
-    const uint32_t above = tot - ex - c0v - c1v;
-    if (above < rem && above + c1v >= rem) {
-      s_dig = b0 + 1;
-      s_dig_above = above;
-    } else if (above + c1v < rem && above + c1v + c0v >= rem) {
-      s_dig = b0;
-      s_dig_above = above + c1v;
+    const uint32_t ex = block_scan<NT>(sum, tmp, &tot);
+    uint32_t acc = tot - ex - sum;  // keys in the bins of higher threads
+    if (acc < rem && acc + sum >= rem) {
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (acc < rem && acc + cv[j] >= rem) {
+          s_dig = b0 + j;
+          s_dig_above = acc;
+        }
+        acc += cv[j];
+      }
     }
     __syncthreads();
     const uint32_t d = (uint32_t)s_dig;
@@ -650,7 +661,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4, 
         if (tid == 0) s_b1 = (int)w.cut[(int64_t)r * w.ctr_stride];
         __syncthreads();
       } else {
-        find_cut(rh, w.hist_copies, k, tmp, &s_b1);
+        find_cut<kSelThreads>(rh, w.hist_copies, k, tmp, &s_b1);
       }
       const uint32_t b1 = (uint32_t)s_b1;
       // count pass: this wave's kept and candidate totals
@@ -731,9 +742,337 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4, 
   for (int j = tid; j < w.hist_copies * kHistBins / 4; j += kSelThreads) h4p[j] = make_uint4(0, 0, 0, 0);
 }
 
+// ------------------------------------------------------- one-wait variant
+// When every select block of a pass can be resident at once, the row's last
+// block to arrive only finds the threshold among the candidates and sends
+// each block of the row a record: where the block's part of the output
+// starts and which of its candidates are chosen.  Each block waits for its
+// record (its only wait on another block, bounded by kSpinLimit polls) and
+// writes its own kept slots from the scores it still holds.  512 threads and
+// 8 scores per thread, so two blocks fit on a compute unit.
+constexpr int kCoopThreads = 512;
+constexpr int kCoopWaves = kCoopThreads / 64;
+constexpr int kCoopPL = kTopkChunk / kCoopThreads;  // scores per thread
+constexpr int kCoopCP = 16;                          // early candidate loads per thread
+constexpr size_t kCoopLds = 60 * 1024;               // dynamic LDS of a block
+constexpr uint32_t kSpinLimit = 1u << 20;
+// Records live in histogram copies 4..7 of the row's control block (the
+// passes that use this variant keep at most 4 copies); word 2 after the
+// histogram words flags a record that never came.
+constexpr int64_t kRecWordOffset = 4 * int64_t(kHistBins);
+static_assert(kRecWordOffset + 2 * kCoopThreads <= kHistWords, "records fit the control block");
+
+// Record of block b, written by the completing block and cleared by b: bit
+// 63 set; bit 62: no candidate chosen; bits 61..42: kt; bits 41..29: rel;
+// bits 28..0: the output offset of the block's first kept slot.  A candidate
+// of block b (its key's top 12 bits are the cut bin) with low 20 key bits lo
+// at block-relative slot l is chosen iff lo > kt, or lo == kt and l < rel.
+__device__ __forceinline__ uint64_t coop_record(bool none, uint32_t kt, uint32_t rel,
+                                                uint32_t off) {
+  return (1ull << 63) | ((uint64_t)none << 62) | ((uint64_t)(kt & 0xFFFFFu) << 42) |
+         ((uint64_t)(rel & 0x1FFFu) << 29) | (uint64_t)(off & 0x1FFFFFFFu);
+}
+
+// LDS words of the completing block before its candidate array.
+__host__ __device__ constexpr int32_t coop_fixed_words(int32_t nblk) {
+  return (2048 + 2 * nblk + 1 + 1) & ~1;
+}
+
+// The completing block of row r (every block of the row has published its
+// counts and candidates): the candidates' threshold by radix selection,
+// each block's count of chosen candidates, the blocks' output offsets, and
+// one record per block holding visible slots (its own goes to *own).
+__device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* __restrict__ orow,
+                              int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
+                              uint32_t* smem, uint32_t* tmp, uint64_t* recs, uint64_t* own) {
+  constexpr int NT = kCoopThreads, CH = kTopkChunk;
+  uint32_t* rhist = smem;                 // 2048 radix bins
+  uint32_t* offE = rhist + 2048;          // nblk + 1 candidate offsets
+  uint32_t* chosen = offE + (nblk + 1);   // nblk
+  uint64_t* cl = reinterpret_cast<uint64_t*>(smem + coop_fixed_words(nblk));  // lds_cand
+  const int tid = threadIdx.x;
+  const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
+  const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
+  // one round trip: the counts and the first `spec` candidates of each block
+  uint32_t ca = 0u, ce = 0u;
+  if (tid < nblk) {
+    ca = ld_coh(crow + 2 * tid);
+    ce = ld_coh(crow + 2 * tid + 1);
+  }
+  int lspec = 0;
+  while ((2 << lspec) * nblk <= NT * kCoopCP && (2 << lspec) <= CH) ++lspec;
+  const int spec = 1 << lspec;
+  uint64_t cv[kCoopCP];
+#pragma unroll
+  for (int m = 0; m < kCoopCP; ++m) {
+    const int f = tid + m * NT;
+    cv[m] = (f < nblk * spec) ? ld_coh(cbase + (int64_t)(f >> lspec) * CH + (f & (spec - 1))) : 0ull;
+  }
+  uint32_t A, C;
+  const uint32_t exE = block_scan<NT>(ce, tmp, &C);
+  (void)block_scan<NT>(ca, tmp, &A);
+  if (tid < nblk) {
+    offE[tid] = exE;
+    chosen[tid] = 0u;
+  }
+  if (tid == 0) offE[nblk] = C;
+  __syncthreads();
+  const uint32_t need = (uint32_t)k - min(A, (uint32_t)k);
+  const bool in_lds = C <= (uint32_t)lds_cand;
+  if (in_lds) {
+#pragma unroll
+    for (int m = 0; m < kCoopCP; ++m) {
+      const int f = tid + m * NT, b = f >> lspec, i = f & (spec - 1);
+      if (b < nblk && (uint32_t)i < offE[b + 1] - offE[b]) cl[offE[b] + i] = cv[m];
+    }
+    // blocks with more than spec candidates: the rest, TPB threads per block
+    constexpr int TPB = 8;
+    for (int b0 = 0; b0 < nblk; b0 += NT / TPB) {
+      const int b = b0 + tid / TPB, j = tid % TPB;
+      const uint32_t eb = (b < nblk) ? offE[b + 1] - offE[b] : 0u;
+      for (uint32_t i0 = spec + j; i0 < eb; i0 += 8 * TPB) {
+        uint64_t t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t i = i0 + u * TPB;
+          t[u] = (i < eb) ? ld_coh(cbase + (int64_t)b * CH + i) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * TPB < eb) cl[offE[b] + i0 + u * TPB] = t[u];
+      }
+    }
+  }
+  __syncthreads();
+  auto cand_at = [&](uint32_t c) -> uint64_t {
+    int lo = 0, hi = nblk - 1;  // block = last b with offE[b] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offE[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return ld_coh(cbase + (int64_t)lo * CH + (c - offE[lo]));
+  };
+  auto for_each = [&](auto&& f) {
+    if (in_lds) {
+      for (uint32_t c = tid; c < C; c += NT) f(cl[c]);
+    } else {
+      for (uint32_t c = tid; c < C; c += NT) f(cand_at(c));
+    }
+  };
+  const uint64_t thr = radix_threshold<NT>(need, rhist, tmp, for_each);
+  const uint64_t low52 = (1ull << 52) - 1;
+  if (need > 0) for_each([&](uint64_t x) {
+    if ((x & low52) >= thr) atomicAdd(&chosen[rank_slot(x) / CH], 1u);
+  });
+  __syncthreads();
+  // output offsets: kept and chosen slots of the blocks before
+  uint32_t tot;
+  const uint32_t off = block_scan<NT>((tid < nblk) ? ca + chosen[tid] : 0u, tmp, &tot);
+  // the need largest candidates are those with (lo, ~slot) >= thr: with
+  // lo == kt, the slots up to slot_t
+  const bool none = need == 0;
+  const uint32_t kt = (uint32_t)(thr >> 32) & 0xFFFFFu;
+  const int64_t slot_t = (int64_t)(0xFFFFFFFFu - (uint32_t)(thr & 0xFFFFFFFFull));
+  if (tid < nblk && (int64_t)tid * CH < nv) {
+    const int64_t rel = min(max(slot_t - (int64_t)tid * CH + 1, (int64_t)0), (int64_t)CH);
+    const uint64_t rec = coop_record(none, kt, (uint32_t)rel, off);
+    if (tid == (int)blockIdx.x) *own = rec;
+    else st_coh(recs + tid, rec);
+  }
+  const uint32_t kept = min(tot, (uint32_t)k);  // k unless the histogram disagreed with the scores
+  for (uint32_t i = kept + tid; i < (uint32_t)k; i += NT) orow[i] = -1;
+  if (count_out && tid == 0) count_out[r] = (int32_t)kept;
+}
+
+__global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
+    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
+    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand) {
+  constexpr int NT = kCoopThreads, NW = kCoopWaves, PL = kCoopPL;
+  extern __shared__ uint64_t smem64[];
+  uint32_t* smem = reinterpret_cast<uint32_t*>(smem64);
+  __shared__ uint32_t tmp[NW];
+  __shared__ uint32_t wtot[2][NW];  // kept / candidates per wave
+  __shared__ int s_b1, s_last;
+  __shared__ uint64_t s_rec;
+
+  const int r = blockIdx.y, nblk = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
+  const int64_t start = (int64_t)blockIdx.x * kTopkChunk;
+  const int64_t wstart = start + (int64_t)wave * 64 * PL;  // wave's slots: wstart + 64j + lane
+  uint32_t* rh = w.hist + (int64_t)r * w.hist_stride;
+  int32_t* orow = idx_out + (int64_t)r * k;
+  const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
+
+  if (nv <= k) {
+    // every visible slot is kept, in place; block 0 pads and clears the
+    // histogram (no block reads it)
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int64_t s = start + j * NT + tid;
+      if (s < nv) orow[s] = sp ? sp[s] : (int32_t)s;
+    }
+    if (blockIdx.x == 0) {
+      for (int64_t j = nv + tid; j < k; j += NT) orow[j] = -1;
+      if (count_out && tid == 0) count_out[r] = (int32_t)nv;
+      uint4* h4p = reinterpret_cast<uint4*>(rh);
+      for (int j = tid; j < w.hist_copies * kHistBins / 4; j += NT) h4p[j] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+
+  const bool active = start < nv;
+  uint32_t keys[PL];
+  int32_t pos[PL];
+  uint32_t* crow = w.counts + (int64_t)r * w.counts_stride + 2 * blockIdx.x;
+  if (!active) {
+    if (tid == 0) {
+      st_coh(crow, 0u);
+      st_coh(crow + 1, 0u);
+    }
+  } else {
+    const float* srow = scores + (int64_t)r * n;
+    float v[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) pos[j] = sp ? sp[min(wstart + 64 * j + lane, nv - 1)] : 0;
+    if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
+    find_cut<NT>(rh, w.hist_copies, k, tmp, &s_b1);
+    const uint32_t b1 = (uint32_t)s_b1;
+    uint32_t na = 0, ne = 0;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int64_t s = wstart + 64 * j + lane;
+      keys[j] = score_key(v[j]);
+      const uint32_t bin = keys[j] >> kHistShift;
+      na += (uint32_t)__popcll(__ballot(s < nv && bin > b1));
+      ne += (uint32_t)__popcll(__ballot(s < nv && bin == b1));
+    }
+    if (lane == 0) {
+      wtot[0][wave] = na;
+      wtot[1][wave] = ne;
+    }
+    __syncthreads();
+    uint32_t oe = 0, ta = 0, te = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      const uint32_t c = wtot[1][x];
+      oe += (x < wave) ? c : 0u;
+      ta += wtot[0][x];
+      te += c;
+    }
+    // the candidates' rank values, listed in slot order in the block's region
+    uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kTopkChunk;
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int64_t s = wstart + 64 * j + lane;
+      const bool eq = s < nv && (keys[j] >> kHistShift) == b1;
+      const uint64_t me = __ballot(eq);
+      if (eq) st_coh(rc + oe + (uint32_t)__popcll(me & lt), rank_value(keys[j], (uint32_t)s));
+      oe += (uint32_t)__popcll(me);
+    }
+    if (tid == 0) {
+      st_coh(crow, ta);
+      st_coh(crow + 1, te);
+    }
+  }
+  // ---- arrival; the row's last block completes it
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  uint32_t* ctr = w.ctr + (int64_t)r * w.ctr_stride;
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (uint32_t)nblk - 1u;
+    if (s_last) {
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w.cut[(int64_t)r * w.ctr_stride] = 0u;
+    }
+  }
+  __syncthreads();
+  uint64_t* recs = reinterpret_cast<uint64_t*>(rh + kRecWordOffset);
+  if (s_last) {
+    coop_complete(r, nv, k, nblk, orow, count_out, w, lds_cand, smem, tmp, recs, &s_rec);
+    // every block of the row has read the histogram copies: leave them zero
+    uint4* h4p = reinterpret_cast<uint4*>(rh);
+    for (int j = tid; j < w.hist_copies * kHistBins / 4; j += NT) h4p[j] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+  if (!active) return;
+  // ---- this block's record
+  if (tid == 0) {
+    uint64_t rec = 0ull;
+    if (s_last) {
+      rec = s_rec;
+    } else {
+      uint64_t* mine = recs + blockIdx.x;
+      uint32_t it = 0;
+      while (((rec = ld_coh(mine)) >> 63) == 0ull && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
+      if (rec >> 63) st_coh(mine, (uint64_t)0);
+      else st_coh(ctr + 2, 1u);  // no record: the pass failed (flagged in the control words)
+    }
+    s_rec = rec;
+  }
+  __syncthreads();
+  const uint64_t rec = s_rec;
+  if ((rec >> 63) == 0ull) return;
+  const bool none = (rec >> 62) & 1ull;
+  const uint32_t kt = (uint32_t)(rec >> 42) & 0xFFFFFu, rel = (uint32_t)(rec >> 29) & 0x1FFFu;
+  const uint32_t off = (uint32_t)rec & 0x1FFFFFFFu;
+  const uint32_t b1 = (uint32_t)s_b1;
+  // ---- kept slots of this block, in slot order, from offset `off`
+  uint64_t msel[PL];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int64_t s = wstart + 64 * j + lane;
+    const uint32_t bin = keys[j] >> kHistShift, lo = keys[j] & 0xFFFFFu;
+    const bool sel = s < nv && (bin > b1 || (bin == b1 && !none &&
+                                             (lo > kt || (lo == kt && (uint32_t)(s - start) < rel))));
+    msel[j] = __ballot(sel);
+    cnt += (uint32_t)__popcll(msel[j]);
+  }
+  if (lane == 0) wtot[0][wave] = cnt;
+  __syncthreads();
+  uint32_t o = off;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) o += (x < wave) ? wtot[0][x] : 0u;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int64_t s = wstart + 64 * j + lane;
+    const uint32_t p = o + (uint32_t)__popcll(msel[j] & lt);
+    if (((msel[j] >> lane) & 1ull) && p < (uint32_t)k) orow[p] = sp ? pos[j] : (int32_t)s;
+    o += (uint32_t)__popcll(msel[j]);
+  }
+}
+
 static int32_t topk_blocks(int64_t n_max, int32_t chunk) {
   const int64_t b = (n_max + chunk - 1) / chunk;
   return (int32_t)(b < 1 ? 1 : b);
+}
+
+// Blocks of topk_coop_kernel the current device holds at once (0 if the
+// query fails, which disables that variant).
+static int64_t coop_capacity() {
+  static int64_t cap[64];
+  static bool known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!known[dev]) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, topk_coop_kernel, kCoopThreads,
+                                                     kCoopLds) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cap[dev] = (int64_t)cus * per;
+    known[dev] = true;
+  }
+  return cap[dev];
 }
 
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
@@ -750,6 +1089,19 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st) {
+  // Passes whose blocks can all be resident at once take the one-wait variant.
+  {
+    const int32_t nblk = topk_blocks(n_max, kTopkChunk);
+    if (w.hist_copies <= 4 && nblk <= kCoopThreads &&
+        (int64_t)rows * nblk <= coop_capacity()) {
+      const int32_t fixed = coop_fixed_words(nblk) * 4;
+      const int32_t lds_cand = (int32_t)((kCoopLds - (size_t)fixed) / 8);
+      CSA2_KERNEL(true, true, topk_coop_kernel, dim3((unsigned)nblk, (unsigned)rows),
+                  dim3(kCoopThreads), kCoopLds, st, scores, n, n_valid, nv_add, slot_pos, k,
+                  idx_out, count_out, w, lds_cand);
+      return hipGetLastError();
+    }
+  }
   // many rows: bigger blocks (fewer, each with more scores)
   const bool large = (int64_t)rows * topk_blocks(n_max, kTopkChunk) > 1024;
   const int32_t chunk = large ? kTopkChunkLarge : kTopkChunk;

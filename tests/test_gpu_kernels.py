@@ -217,6 +217,16 @@ def test_topk_large_rows():
     _check_topk(s[:1], np.array([n], np.int32), 16384)
 
 
+def test_topk_many_rows():
+    # more select blocks than the device holds at once: the path whose last
+    # block completes each row by itself
+    rng = np.random.default_rng(5)
+    rows, n = 144, 16384 + 100
+    s = rng.standard_normal((rows, n)).astype(np.float32)
+    nv = rng.integers(200, n + 1, rows).astype(np.int32)
+    _check_topk(s, nv, 256)
+
+
 def test_topk_slot_map():
     rng = np.random.default_rng(4)
     P = 16384
