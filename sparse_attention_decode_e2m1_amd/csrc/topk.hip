@@ -181,14 +181,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_cut_kernel(const int32_t* __
 // Radix selection of the need-th largest rank value among C candidates
 // (all sharing the top 12 key bits): 11-bit digits at shifts 41, 30, 19, 8,
 // then 8 bits at 0; stops once a whole bucket is taken.  for_each(f) calls f
-// on every candidate (each once, spread over the block's threads).  Returns
-// the threshold: the candidates >= it (low 52 bits compared) are the need
-// largest.  All NT threads call it.
-template <int NT, typename ForEach>
+// on every candidate (each once, spread over the block's threads).  With
+// GIVEN0, the first digit's histogram is already at hand (thread t holds
+// bins [t*BPT, (t+1)*BPT) in g0) and that pass skips the candidates.
+// Returns the threshold: the candidates >= it (low 52 bits compared) are the
+// need largest.  All NT threads call it.
+template <int N>
+struct Bins {  // a thread's share of a histogram, passed by value (kept in registers)
+  uint32_t v[N];
+};
+template <int NT, bool GIVEN0, typename ForEach>
 __device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tmp,
-                                    ForEach&& for_each) {
+                                    ForEach&& for_each, Bins<2048 / NT> g0) {
+  constexpr int BPT = 2048 / NT;
   __shared__ int s_dig;
-  __shared__ uint32_t s_dig_above;
+  __shared__ uint32_t s_dig_above, s_dig_count;
   const int tid = threadIdx.x;
   if (need == 0) return ~0ull;
   uint64_t prefix = 0;
@@ -196,25 +203,29 @@ __device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tm
   for (int p = 0; p < 5; ++p) {
     const int sh = p < 4 ? 41 - 11 * p : 0, wd = p < 4 ? 11 : 8;
     const int nb = 1 << wd;
-    for (int j = tid; j < 2048; j += NT) rhist[j] = 0u;
+    const bool given = GIVEN0 && p == 0;
+    if (!given)
+      for (int j = tid; j < 2048; j += NT) rhist[j] = 0u;
     if (tid == 0) {
       s_dig = 0;
       s_dig_above = 0;
+      s_dig_count = 0;
     }
     __syncthreads();
-    const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
-    for_each([&](uint64_t x) {
-      if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
-    });
-    __syncthreads();
+    if (!given) {
+      const uint64_t hi_mask = (~0ull << (sh + wd)) & ((1ull << 52) - 1);
+      for_each([&](uint64_t x) {
+        if ((x & hi_mask) == prefix) atomicAdd(&rhist[(uint32_t)(x >> sh) & (uint32_t)(nb - 1)], 1u);
+      });
+      __syncthreads();
+    }
     // digit d with count(> d) < rem <= count(>= d); BPT bins per thread
     // (bins past nb were cleared, so they count zero)
-    constexpr int BPT = 2048 / NT;
     const int b0 = BPT * tid;
     uint32_t cv[BPT], sum = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      cv[j] = rhist[b0 + j];
+      cv[j] = given ? g0.v[j] : rhist[b0 + j];
       sum += cv[j];
     }
     uint32_t tot;
@@ -226,6 +237,7 @@ __device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tm
         if (acc < rem && acc + cv[j] >= rem) {
           s_dig = b0 + j;
           s_dig_above = acc;
+          s_dig_count = cv[j];
         }
         acc += cv[j];
       }
@@ -234,11 +246,16 @@ __device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tm
     const uint32_t d = (uint32_t)s_dig;
     rem -= s_dig_above;
     prefix |= (uint64_t)d << sh;
-    const bool whole_bucket = rhist[d] == rem;
+    const bool whole_bucket = s_dig_count == rem;
     __syncthreads();
     if (whole_bucket) break;
   }
   return prefix;
+}
+template <int NT, typename ForEach>
+__device__ uint64_t radix_threshold(uint32_t need, uint32_t* rhist, uint32_t* tmp,
+                                    ForEach&& for_each) {
+  return radix_threshold<NT, false>(need, rhist, tmp, for_each, Bins<2048 / NT>{});
 }
 
 // Completion of row r by its last block (all select blocks of the row have
@@ -753,14 +770,18 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4, 
 constexpr int kCoopThreads = 512;
 constexpr int kCoopWaves = kCoopThreads / 64;
 constexpr int kCoopPL = kTopkChunk / kCoopThreads;  // scores per thread
-constexpr int kCoopCP = 16;                          // early candidate loads per thread
-constexpr size_t kCoopLds = 60 * 1024;               // dynamic LDS of a block
+constexpr int kCoopCP = 8;                          // early candidate loads per thread
+constexpr size_t kCoopLds = 17 * 1024;               // dynamic LDS of a block
 constexpr uint32_t kSpinLimit = 1u << 20;
 // Records live in histogram copies 4..7 of the row's control block (the
 // passes that use this variant keep at most 4 copies); word 2 after the
 // histogram words flags a record that never came.
 constexpr int64_t kRecWordOffset = 4 * int64_t(kHistBins);
-static_assert(kRecWordOffset + 2 * kCoopThreads <= kHistWords, "records fit the control block");
+// Then the candidates' first radix digit histogram (2048 bins), added to by
+// the select blocks and cleared by the completing block.
+constexpr int64_t kL2WordOffset = kRecWordOffset + 2 * kCoopThreads;
+static_assert(kTopkChunk == 4096, "12-bit block-relative slots in packed candidates");
+static_assert(kL2WordOffset + 2048 <= kHistWords, "records and digit bins fit the control block");
 
 // Record of block b, written by the completing block and cleared by b: bit
 // 63 set; bit 62: no candidate chosen; bits 61..42: kt; bits 41..29: rel;
@@ -773,27 +794,76 @@ __device__ __forceinline__ uint64_t coop_record(bool none, uint32_t kt, uint32_t
          ((uint64_t)(rel & 0x1FFFu) << 29) | (uint64_t)(off & 0x1FFFFFFFu);
 }
 
-// LDS words of the completing block before its candidate array.
-__host__ __device__ constexpr int32_t coop_fixed_words(int32_t nblk) {
-  return (2048 + 2 * nblk + 1 + 1) & ~1;
+constexpr int kBucketMax = kCoopThreads;  // candidates of the cut digit ranked directly
+
+// Digit d of a 2048-bin histogram held BPT bins per thread (thread t: bins
+// [t*BPT, (t+1)*BPT)) with count(> d) < rem <= count(>= d): *above =
+// count(> d), *cnt = count(d).  All NT threads call it.
+template <int NT>
+__device__ __forceinline__ uint32_t pick_digit(Bins<2048 / NT> cv, uint32_t rem, uint32_t* tmp,
+                                               uint32_t* above, uint32_t* cnt) {
+  constexpr int BPT = 2048 / NT;
+  __shared__ uint32_t s_pick[3];
+  if (threadIdx.x == 0) s_pick[0] = s_pick[1] = s_pick[2] = 0u;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) sum += cv.v[j];
+  uint32_t tot;
+  const uint32_t ex = block_scan<NT>(sum, tmp, &tot);
+  uint32_t acc = tot - ex - sum;
+  if (acc < rem && acc + sum >= rem) {
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (acc < rem && acc + cv.v[j] >= rem) {
+        s_pick[0] = BPT * threadIdx.x + j;
+        s_pick[1] = acc;
+        s_pick[2] = cv.v[j];
+      }
+      acc += cv.v[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t d = s_pick[0];
+  *above = s_pick[1];
+  *cnt = s_pick[2];
+  __syncthreads();
+  return d;
 }
 
 // The completing block of row r (every block of the row has published its
-// counts and candidates): the candidates' threshold by radix selection,
-// each block's count of chosen candidates, the blocks' output offsets, and
-// one record per block holding visible slots (its own goes to *own).
+// counts, candidates and first-digit bins): the threshold among the
+// candidates, each block's count of chosen candidates, the blocks' output
+// offsets, and one record per block holding visible slots (its own goes to
+// *own).  The candidates come straight from the first round trip (the first
+// `spec` of each block, in registers; the rest of a block, if any, from
+// memory).  The first radix digit's histogram is complete, so the cut digit
+// d0 is known at once; candidates above it are chosen, and the few sharing
+// it are ranked against each other (a full radix selection only when more
+// than kBucketMax share it).
 __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* __restrict__ orow,
-                              int32_t* __restrict__ count_out, const TopkWs& w, int32_t lds_cand,
-                              uint32_t* smem, uint32_t* tmp, uint64_t* recs, uint64_t* own) {
-  constexpr int NT = kCoopThreads, CH = kTopkChunk;
-  uint32_t* rhist = smem;                 // 2048 radix bins
-  uint32_t* offE = rhist + 2048;          // nblk + 1 candidate offsets
-  uint32_t* chosen = offE + (nblk + 1);   // nblk
-  uint64_t* cl = reinterpret_cast<uint64_t*>(smem + coop_fixed_words(nblk));  // lds_cand
-  const int tid = threadIdx.x;
+                              int32_t* __restrict__ count_out, const TopkWs& w, uint32_t* smem,
+                              uint32_t* tmp, uint32_t* rh, uint64_t* recs, uint64_t* own) {
+  constexpr int NT = kCoopThreads, NW = kCoopWaves, CH = kTopkChunk, BPT = 2048 / NT;
+  uint32_t* cntE = smem;                    // candidates per block
+  uint32_t* chosen = cntE + NT;             // chosen candidates per block
+  uint32_t* rhist = chosen + NT;            // 2048 radix bins (many ties only)
+  uint64_t* bucket = reinterpret_cast<uint64_t*>(rhist + 2048);  // kBucketMax
+  uint32_t* pcs = reinterpret_cast<uint32_t*>(bucket + kBucketMax);  // kCoopCP x NW counts
+  __shared__ uint32_t s_tot[2][NW];
+  __shared__ uint32_t s_nb, s_rest;
+  __shared__ uint64_t s_thr;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t* crow = w.counts + (int64_t)r * w.counts_stride;
-  const uint64_t* cbase = w.cand + (int64_t)r * w.cand_stride;
-  // one round trip: the counts and the first `spec` candidates of each block
+  // candidates are packed 32-bit words (see the select pass); expand() gives
+  // the 64-bit rank value of block b's word (key bits 19..0, ~row slot)
+  const uint32_t* cbase = reinterpret_cast<const uint32_t*>(w.cand + (int64_t)r * w.cand_stride);
+  auto expand = [&](uint32_t p, int b) -> uint64_t {
+    const uint32_t slot = (uint32_t)b * CH + (uint32_t)(CH - 1) - (p & (uint32_t)(CH - 1));
+    return ((uint64_t)(p >> 12) << 32) | (uint64_t)(0xFFFFFFFFu - slot);
+  };
+  uint32_t* l2 = rh + kL2WordOffset;
+  // ---- one round trip: counts, the first spec candidates of each block, the
+  // first-digit bins
   uint32_t ca = 0u, ce = 0u;
   if (tid < nblk) {
     ca = ld_coh(crow + 2 * tid);
@@ -802,75 +872,179 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
   int lspec = 0;
   while ((2 << lspec) * nblk <= NT * kCoopCP && (2 << lspec) <= CH) ++lspec;
   const int spec = 1 << lspec;
-  uint64_t cv[kCoopCP];
+  uint32_t cv[kCoopCP];
 #pragma unroll
   for (int m = 0; m < kCoopCP; ++m) {
     const int f = tid + m * NT;
-    cv[m] = (f < nblk * spec) ? ld_coh(cbase + (int64_t)(f >> lspec) * CH + (f & (spec - 1))) : 0ull;
+    cv[m] = (f < nblk * spec) ? ld_coh(cbase + (int64_t)(f >> lspec) * CH + (f & (spec - 1))) : 0u;
   }
-  uint32_t A, C;
-  const uint32_t exE = block_scan<NT>(ce, tmp, &C);
-  (void)block_scan<NT>(ca, tmp, &A);
+  Bins<BPT> g0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) g0.v[j] = ld_coh(l2 + BPT * tid + j);
+  // ---- totals (kept, candidates); per-block candidate counts to LDS
+  {
+    const uint32_t sa = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ca), 63);
+    const uint32_t se = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ce), 63);
+    if (lane == 0) {
+      s_tot[0][wave] = sa;
+      s_tot[1][wave] = se;
+    }
+  }
   if (tid < nblk) {
-    offE[tid] = exE;
+    cntE[tid] = ce;
     chosen[tid] = 0u;
   }
-  if (tid == 0) offE[nblk] = C;
+  if (tid == 0) {
+    s_nb = 0u;
+    s_thr = ~0ull;
+    s_rest = 0u;
+  }
   __syncthreads();
+  if (ce > (uint32_t)spec) s_rest = 1u;  // some block has candidates beyond the first round trip
+  uint32_t A = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) A += s_tot[0][x];
+  // every select block has added its bins: clear them (a store that depends
+  // on the loaded value cannot overtake the load)
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if (g0.v[j] != 0u) l2[BPT * tid + j] = 0u;
   const uint32_t need = (uint32_t)k - min(A, (uint32_t)k);
-  const bool in_lds = C <= (uint32_t)lds_cand;
-  if (in_lds) {
+
+  // every candidate once: f(x) on the lanes holding one (x = 0 elsewhere is
+  // never passed); the counts of the register-held blocks are read first
+  // (f(x, uni): uni when the wave's lanes calling f hold candidates of one block)
+  auto for_all_u = [&](auto&& f) {
+    bool has[kCoopCP];
 #pragma unroll
     for (int m = 0; m < kCoopCP; ++m) {
-      const int f = tid + m * NT, b = f >> lspec, i = f & (spec - 1);
-      if (b < nblk && (uint32_t)i < offE[b + 1] - offE[b]) cl[offE[b] + i] = cv[m];
+      const int fi = tid + m * NT, b = fi >> lspec;
+      has[m] = b < nblk && (uint32_t)(fi & (spec - 1)) < cntE[min(b, nblk - 1)];
     }
-    // blocks with more than spec candidates: the rest, TPB threads per block
+#pragma unroll
+    for (int m = 0; m < kCoopCP; ++m)
+      if (has[m]) f(expand(cv[m], (tid + m * NT) >> lspec), lspec >= 6);
     constexpr int TPB = 8;
     for (int b0 = 0; b0 < nblk; b0 += NT / TPB) {
-      const int b = b0 + tid / TPB, j = tid % TPB;
-      const uint32_t eb = (b < nblk) ? offE[b + 1] - offE[b] : 0u;
-      for (uint32_t i0 = spec + j; i0 < eb; i0 += 8 * TPB) {
-        uint64_t t[8];
+      const int b = b0 + tid / TPB;
+      const uint32_t eb = (b < nblk) ? cntE[b] : 0u;
+      for (uint32_t i = spec + tid % TPB; i < eb; i += TPB)
+        f(expand(ld_coh(cbase + (int64_t)b * CH + i), b), false);
+    }
+  };
+  auto for_all = [&](auto&& f) { for_all_u([&](uint64_t x, bool) { f(x); }); };
+  // chosen[b] += lanes with ch set whose candidate is in block b (one LDS
+  // add per distinct block of the wave)
+  auto add_chosen = [&](bool ch, uint32_t b, bool uni) {
+    uint64_t pend = __ballot(ch);
+    if (uni) {
+      if (pend && lane == __ffsll((unsigned long long)pend) - 1) atomicAdd(&chosen[b], (uint32_t)__popcll(pend));
+      return;
+    }
+    while (pend) {
+      const int l = __ffsll((unsigned long long)pend) - 1;
+      const uint32_t bl = (uint32_t)__builtin_amdgcn_readlane((int)b, l);
+      const uint64_t mm = __ballot(ch && b == bl);
+      if (lane == l) atomicAdd(&chosen[bl], (uint32_t)__popcll(mm));
+      pend &= ~mm;
+    }
+  };
+  uint64_t thr = ~0ull;  // rank values (low 52 bits) >= thr are chosen; ~0: none
+  if (need > 0) {
+    uint32_t above0, cnt0;
+    const uint32_t d0 = pick_digit<NT>(g0, need, tmp, &above0, &cnt0);
+    const uint32_t rem = need - min(above0, need);
+    const bool whole = cnt0 == rem;
+    // one pass: digits above d0 chosen (d0 too when its bucket is taken
+    // whole); otherwise d0's candidates gathered for ranking
+    if (lspec >= 6 && s_rest == 0u) {
+      // every candidate is in registers, and the lanes of a wave holding
+      // register m all hold candidates of block (tid + m*NT) >> lspec: the
+      // chosen count of each (register, wave) is one ballot, kept in lane m
+      // and stored once per wave; branch-free, so the registers interleave
+      uint32_t cnt[kCoopCP];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t i = i0 + u * TPB;
-          t[u] = (i < eb) ? ld_coh(cbase + (int64_t)b * CH + i) : 0ull;
-        }
+      for (int m = 0; m < kCoopCP; ++m) cnt[m] = cntE[min((tid + m * NT) >> lspec, nblk - 1)];
+      const uint32_t dlo = whole ? d0 : d0 + 1;  // chosen outright: digit >= dlo
+      uint32_t pcv = 0u;
+      uint64_t anyb = 0ull;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u * TPB < eb) cl[offE[b] + i0 + u * TPB] = t[u];
+      for (int m = 0; m < kCoopCP; ++m) {
+        const int fi = tid + m * NT;
+        const bool has = ((fi >> lspec) < nblk) & ((uint32_t)(fi & (spec - 1)) < cnt[m]);
+        const uint32_t dg = cv[m] >> 21;  // key bits 19..9
+        const uint32_t c = (uint32_t)__popcll(__ballot(has & (dg >= dlo)));
+        pcv = (lane == m) ? c : pcv;
+        anyb |= __ballot(has & !whole & (dg == d0));
       }
+      if (lane < kCoopCP) pcs[lane * NW + wave] = pcv;
+      if (anyb) {  // the cut digit's candidates, for ranking
+#pragma unroll
+        for (int m = 0; m < kCoopCP; ++m) {
+          const int fi = tid + m * NT;
+          const bool has = ((fi >> lspec) < nblk) & ((uint32_t)(fi & (spec - 1)) < cnt[m]);
+          const uint64_t mb = __ballot(has & ((cv[m] >> 21) == d0));
+          if (mb) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_nb, (uint32_t)__popcll(mb));
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            const uint32_t p = base + (uint32_t)__popcll(mb & lanemask_lt());
+            if (((mb >> lane) & 1ull) && p < (uint32_t)kBucketMax) bucket[p] = expand(cv[m], fi >> lspec);
+          }
+        }
+      }
+      __syncthreads();
+      // block b's candidates are registers' lanes [b*spec, (b+1)*spec): spec/64 waves' counts
+      if (tid < nblk) {
+        uint32_t c = 0;
+        for (int f0 = tid * spec; f0 < (tid + 1) * spec; f0 += 64) c += pcs[(f0 / NT) * NW + (f0 % NT) / 64];
+        chosen[tid] = c;
+      }
+    } else {
+      for_all_u([&](uint64_t x, bool uni) {
+        const uint32_t dg = (uint32_t)(x >> 41) & 2047u;
+        const bool ch = dg > d0 || (whole && dg == d0);
+        add_chosen(ch, rank_slot(x) / CH, uni);
+        if (!whole && dg == d0) {
+          const uint32_t p = atomicAdd(&s_nb, 1u);
+          if (p < (uint32_t)kBucketMax) bucket[p] = x;
+        }
+      });
+    }
+    __syncthreads();
+    const uint64_t low52 = (1ull << 52) - 1;
+    if (whole) {
+      thr = (uint64_t)d0 << 41;
+    } else if (s_nb <= (uint32_t)kBucketMax) {
+      // rank of each bucket member among the bucket (rank values are unique)
+      const uint32_t nb = s_nb;
+      bool ch = false;
+      uint64_t x = 0;
+      if ((uint32_t)tid < nb) {
+        x = bucket[tid];
+        uint32_t rk = 0;
+        for (uint32_t i = 0; i < nb; ++i) rk += (bucket[i] > x) ? 1u : 0u;
+        ch = rk < rem;
+        if (rk + 1 == rem) s_thr = x & low52;
+      }
+      add_chosen(ch, rank_slot(x) / CH, false);
+      __syncthreads();
+      thr = s_thr;
+    } else {
+      // many equal leading bits (ties): radix selection over all candidates
+      thr = radix_threshold<NT, true>(need, rhist, tmp, for_all, g0);
+      for_all([&](uint64_t x) {
+        add_chosen(((uint32_t)(x >> 41) & 2047u) == d0 && (x & low52) >= thr, rank_slot(x) / CH, false);
+      });
     }
   }
   __syncthreads();
-  auto cand_at = [&](uint32_t c) -> uint64_t {
-    int lo = 0, hi = nblk - 1;  // block = last b with offE[b] <= c
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offE[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    return ld_coh(cbase + (int64_t)lo * CH + (c - offE[lo]));
-  };
-  auto for_each = [&](auto&& f) {
-    if (in_lds) {
-      for (uint32_t c = tid; c < C; c += NT) f(cl[c]);
-    } else {
-      for (uint32_t c = tid; c < C; c += NT) f(cand_at(c));
-    }
-  };
-  const uint64_t thr = radix_threshold<NT>(need, rhist, tmp, for_each);
-  const uint64_t low52 = (1ull << 52) - 1;
-  if (need > 0) for_each([&](uint64_t x) {
-    if ((x & low52) >= thr) atomicAdd(&chosen[rank_slot(x) / CH], 1u);
-  });
-  __syncthreads();
-  // output offsets: kept and chosen slots of the blocks before
+  // ---- output offsets: kept and chosen slots of the blocks before
   uint32_t tot;
   const uint32_t off = block_scan<NT>((tid < nblk) ? ca + chosen[tid] : 0u, tmp, &tot);
-  // the need largest candidates are those with (lo, ~slot) >= thr: with
-  // lo == kt, the slots up to slot_t
-  const bool none = need == 0;
+  // the chosen candidates are those with (lo, ~slot) >= thr: with lo == kt,
+  // the slots up to slot_t
+  const bool none = thr == ~0ull;
   const uint32_t kt = (uint32_t)(thr >> 32) & 0xFFFFFu;
   const int64_t slot_t = (int64_t)(0xFFFFFFFFu - (uint32_t)(thr & 0xFFFFFFFFull));
   if (tid < nblk && (int64_t)tid * CH < nv) {
@@ -884,10 +1058,10 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
   if (count_out && tid == 0) count_out[r] = (int32_t)kept;
 }
 
-__global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
+__global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_coop_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, TopkWs w, int32_t lds_cand) {
+    int32_t* __restrict__ count_out, TopkWs w) {
   constexpr int NT = kCoopThreads, NW = kCoopWaves, PL = kCoopPL;
   extern __shared__ uint64_t smem64[];
   uint32_t* smem = reinterpret_cast<uint32_t*>(smem64);
@@ -895,6 +1069,7 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
   __shared__ uint32_t wtot[2][NW];  // kept / candidates per wave
   __shared__ int s_b1, s_last;
   __shared__ uint64_t s_rec;
+  __shared__ uint32_t s_keys[kTopkChunk];  // the block's score keys, kept across the wait
 
   const int r = blockIdx.y, nblk = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -923,7 +1098,7 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
   }
 
   const bool active = start < nv;
-  uint32_t keys[PL];
+  uint32_t* l2 = rh + kL2WordOffset;
   int32_t pos[PL];
   uint32_t* crow = w.counts + (int64_t)r * w.counts_stride + 2 * blockIdx.x;
   if (!active) {
@@ -942,10 +1117,12 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
     find_cut<NT>(rh, w.hist_copies, k, tmp, &s_b1);
     const uint32_t b1 = (uint32_t)s_b1;
     uint32_t na = 0, ne = 0;
+    uint32_t keys[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       const int64_t s = wstart + 64 * j + lane;
       keys[j] = score_key(v[j]);
+      s_keys[wave * 64 * PL + 64 * j + lane] = keys[j];
       const uint32_t bin = keys[j] >> kHistShift;
       na += (uint32_t)__popcll(__ballot(s < nv && bin > b1));
       ne += (uint32_t)__popcll(__ballot(s < nv && bin == b1));
@@ -964,14 +1141,21 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
       te += c;
     }
     // the candidates' rank values, listed in slot order in the block's region
-    uint64_t* rc = w.cand + (int64_t)r * w.cand_stride + (int64_t)blockIdx.x * kTopkChunk;
+    // each as one word: key bits 19..0 above the block-relative slot's
+    // complement (12 bits), so larger words rank first within the block
+    uint32_t* rc = reinterpret_cast<uint32_t*>(w.cand + (int64_t)r * w.cand_stride) +
+                   (int64_t)blockIdx.x * kTopkChunk;
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       const int64_t s = wstart + 64 * j + lane;
       const bool eq = s < nv && (keys[j] >> kHistShift) == b1;
       const uint64_t me = __ballot(eq);
-      if (eq) st_coh(rc + oe + (uint32_t)__popcll(me & lt), rank_value(keys[j], (uint32_t)s));
+      if (eq) {
+        st_coh(rc + oe + (uint32_t)__popcll(me & lt),
+               ((keys[j] & 0xFFFFFu) << 12) | (uint32_t)(kTopkChunk - 1 - (s - start)));
+        atomicAdd(l2 + ((keys[j] >> 9) & 2047u), 1u);  // first radix digit: key bits 19..9
+      }
       oe += (uint32_t)__popcll(me);
     }
     if (tid == 0) {
@@ -994,7 +1178,7 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
   __syncthreads();
   uint64_t* recs = reinterpret_cast<uint64_t*>(rh + kRecWordOffset);
   if (s_last) {
-    coop_complete(r, nv, k, nblk, orow, count_out, w, lds_cand, smem, tmp, recs, &s_rec);
+    coop_complete(r, nv, k, nblk, orow, count_out, w, smem, tmp, rh, recs, &s_rec);
     // every block of the row has read the histogram copies: leave them zero
     uint4* h4p = reinterpret_cast<uint4*>(rh);
     for (int j = tid; j < w.hist_copies * kHistBins / 4; j += NT) h4p[j] = make_uint4(0, 0, 0, 0);
@@ -1028,7 +1212,8 @@ __global__ __launch_bounds__(kCoopThreads) void topk_coop_kernel(
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
     const int64_t s = wstart + 64 * j + lane;
-    const uint32_t bin = keys[j] >> kHistShift, lo = keys[j] & 0xFFFFFu;
+    const uint32_t key = s_keys[wave * 64 * PL + 64 * j + lane];
+    const uint32_t bin = key >> kHistShift, lo = key & 0xFFFFFu;
     const bool sel = s < nv && (bin > b1 || (bin == b1 && !none &&
                                              (lo > kt || (lo == kt && (uint32_t)(s - start) < rel))));
     msel[j] = __ballot(sel);
@@ -1094,11 +1279,9 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     const int32_t nblk = topk_blocks(n_max, kTopkChunk);
     if (w.hist_copies <= 4 && nblk <= kCoopThreads &&
         (int64_t)rows * nblk <= coop_capacity()) {
-      const int32_t fixed = coop_fixed_words(nblk) * 4;
-      const int32_t lds_cand = (int32_t)((kCoopLds - (size_t)fixed) / 8);
       CSA2_KERNEL(true, true, topk_coop_kernel, dim3((unsigned)nblk, (unsigned)rows),
                   dim3(kCoopThreads), kCoopLds, st, scores, n, n_valid, nv_add, slot_pos, k,
-                  idx_out, count_out, w, lds_cand);
+                  idx_out, count_out, w);
       return hipGetLastError();
     }
   }
