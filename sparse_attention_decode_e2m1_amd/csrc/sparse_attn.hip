@@ -64,6 +64,10 @@ __device__ __forceinline__ f16x8 v_operand(const _Float16* lo, const _Float16* h
   return __builtin_bit_cast(f16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Row stride (floats) of the round's logits: 64 entries + 4, so the 16 head
+// rows of a 16-byte read fall on different banks.
+constexpr int kLgStride = 68;
+
 template <int DV>
 constexpr int vs_stride() {
   // halves; a row stride of 8 banks mod 64 keeps the four rows of a
@@ -95,8 +99,7 @@ struct AttnArgs {
 // so the row loads issue as soon as the index arrives.
 template <int D, int DV, bool WIN, bool MULTI>
 __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _Float16* Vs,
-                                           _Float16* Ps, float (*red_max)[16],
-                                           float (*red_sum)[16]) {
+                                           float* Lg) {
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
   constexpr int VST = vs_stride<DV>();
@@ -201,14 +204,10 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   for (int rr = 0; rr < 4; ++rr) er[rr] = __shfl(qexp, 4 * g + rr, kWave);
   const float lscale = a.sm_scale * wscale;
 
-  // running softmax state of heads 4g + rr, and this wave's P.V tiles
-  float mh[4], lh[4];
+  // running softmax state of head i (every lane of the block holds its
+  // head's), and this wave's P.V tiles
+  float mrun = -INFINITY, lrun = 0.0f;
   f32x4 o[NT];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    mh[rr] = -INFINITY;
-    lh[rr] = 0.0f;
-  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // this lane's transposed-read address in the V tile (see v_operand)
@@ -216,7 +215,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
 
   for (int rnd = 0; rnd < rounds; ++rnd) {
     if (MULTI && rnd > 0) {
-      __syncthreads();  // the previous round's reads of Vs and Ps are done
+      __syncthreads();  // the previous round's reads of Vs and Lg are done
       load_row(e0 + 64 * rnd);
     }
     if (MULTI && rnd + 1 < rounds) ix = load_ix(e0 + 64 * (rnd + 1));  // next round's index
@@ -247,43 +246,59 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
         }
       }
     }
-    // ---- softmax statistics, folded into the running state
-    float lg[4], alpha[4];
+    // ---- softmax: the tile's logits (heads 4g + rr, entry i) go to LDS; after
+    // one barrier, lane (i, g) reads head i's logits at its P.V operand slots
+    // (entries 32ks + 8g + [0, 8)), and the four lanes of head i agree on its
+    // maximum and sum with lane exchanges.  Every wave thus builds P itself.
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      lg[rr] = valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * lscale : -INFINITY;
-      const float mx = row16_max(lg[rr]);
-      if (i == 0) red_max[wave][4 * g + rr] = mx;
-    }
-    __syncthreads();
+    for (int rr = 0; rr < 4; ++rr)
+      Lg[(4 * g + rr) * kLgStride + wave * 16 + i] =
+          valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * lscale : -INFINITY;
+    __syncthreads();  // every wave's logits and value rows are in LDS
+    float lv[2][8];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      const float mr = fmaxf(fmaxf(red_max[0][h], red_max[1][h]), fmaxf(red_max[2][h], red_max[3][h]));
-      const float mnew = fmaxf(mh[rr], mr);
-      alpha[rr] = (mnew == -INFINITY) ? 1.0f : __expf(mh[rr] - mnew);
-      const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lg[rr] - mnew);
-      Ps[h * 64 + wave * 16 + i] = (_Float16)pr;
-      const float ps = row16_sum(pr);  // the sum uses the unrounded probabilities
-      if (i == 0) red_sum[wave][h] = ps;
-      mh[rr] = mnew;
+    for (int ks = 0; ks < 2; ++ks) {
+      const float4 x0 = *reinterpret_cast<const float4*>(Lg + i * kLgStride + 32 * ks + 8 * g);
+      const float4 x1 = *reinterpret_cast<const float4*>(Lg + i * kLgStride + 32 * ks + 8 * g + 4);
+      lv[ks][0] = x0.x; lv[ks][1] = x0.y; lv[ks][2] = x0.z; lv[ks][3] = x0.w;
+      lv[ks][4] = x1.x; lv[ks][5] = x1.y; lv[ks][6] = x1.z; lv[ks][7] = x1.w;
     }
-    __syncthreads();
+    float mr = -INFINITY;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 4 * g + rr;
-      lh[rr] = lh[rr] * alpha[rr] + (red_sum[0][h] + red_sum[1][h] + red_sum[2][h] + red_sum[3][h]);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mr = fmaxf(mr, lv[ks][j]);
+    mr = fmaxf(mr, shfl_xor(mr, 16));
+    mr = fmaxf(mr, shfl_xor(mr, 32));
+    const float mnew = fmaxf(mrun, mr);
+    const float alpha = (mnew == -INFINITY) ? 1.0f : __expf(mrun - mnew);
+    f16x8 pa[2];
+    float ps = 0.0f;  // the sum uses the unrounded probabilities
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lv[ks][j] - mnew);
+        ps += pr;
+        pa[ks][j] = (_Float16)pr;
+      }
+    ps += shfl_xor(ps, 16);
+    ps += shfl_xor(ps, 32);
+    lrun = lrun * alpha + ps;
+    mrun = mnew;
+    // the P.V tiles hold heads 4g + rr: their rescale factors
+    float alh[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) alh[rr] = __shfl(alpha, 4 * g + rr, kWave);
     // ---- P.V for this wave's channels
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) o[nt][rr] *= alpha[rr];
+      for (int rr = 0; rr < 4; ++rr) o[nt][rr] *= alh[rr];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 pa = *reinterpret_cast<const f16x8*>(Ps + i * 64 + 32 * ks + 8 * g);
         const _Float16* vp = vt + 32 * ks * VST + 16 * nt;
-        o[nt] = mfma16x16x32(pa, v_operand(vp, vp + 4 * VST), o[nt]);
+        o[nt] = mfma16x16x32(pa[ks], v_operand(vp, vp + 4 * VST), o[nt]);
       }
     }
   }
@@ -297,12 +312,10 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     for (int rr = 0; rr < 4; ++rr)
       st_pair(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
               o[nt + 1][rr] * wscale);
-  // running max and sum of heads 4g + rr, written by lanes i == 0 as pairs
-  if (wave == 0 && i == 0) {
-    st_pair(pb + 16 * DV + 4 * g, mh[0], mh[1]);
-    st_pair(pb + 16 * DV + 4 * g + 2, mh[2], mh[3]);
-    st_pair(pb + 16 * DV + 16 + 4 * g, lh[0], lh[1]);
-    st_pair(pb + 16 * DV + 16 + 4 * g + 2, lh[2], lh[3]);
+  // running max and sum of head i, written by lanes g == 0 of wave 0
+  if (wave == 0 && g == 0) {
+    pb[16 * DV + i] = mrun;
+    pb[16 * DV + 16 + i] = lrun;
   }
 }
 
@@ -313,14 +326,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
   // 16-byte aligned: the V tile is written and read with 16- and 8-byte LDS
   // accesses, so its base must not follow the static arrays unaligned
   extern __shared__ __attribute__((aligned(16))) _Float16 Vs[];  // [64 entries][vs_stride]
-  __shared__ _Float16 Ps[16 * 64];  // [head][entry of the round]
-  __shared__ float red_max[4][16];
-  __shared__ float red_sum[4][16];
+  __shared__ __attribute__((aligned(16))) float Lg[16 * kLgStride];  // [head][entry of the round]
   const int r = blockIdx.y, sidx = blockIdx.x;
   if (sidx >= a.nsg)
-    split_body<D, DV, true, MULTI>(a, r, sidx, Vs, Ps, red_max, red_sum);
+    split_body<D, DV, true, MULTI>(a, r, sidx, Vs, Lg);
   else
-    split_body<D, DV, false, MULTI>(a, r, sidx, Vs, Ps, red_max, red_sum);
+    split_body<D, DV, false, MULTI>(a, r, sidx, Vs, Lg);
 }
 
 // Merge kernel.  Unit u of row r is the value-slot pair (2(u % (dv/2)), +1)
