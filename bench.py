@@ -39,7 +39,7 @@ def kv_bytes_per_query(w) -> dict:
     scan = 0
     first_full_pool = False
     for m in w.modes:
-        b = w.K * mrow + w.W * w.D
+        b = (0 if m == I.SWA else w.K * mrow) + w.W * w.D
         if m == I.FULL:
             b += w.N * irow
             scan += w.N * irow
@@ -179,7 +179,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "context": w.N, "query_tokens": w.T,
-                   "layers": [["FULL", "REINDEX", "REUSE"][m] for m in w.modes], "top_k": w.K,
+                   "layers": [I.MODE_NAMES[m] for m in w.modes], "top_k": w.K,
                    "pool": w.P, "window": w.W, "heads": w.H, "latent": w.D, "index_heads": w.HI,
                    "index_dim": w.DI, "kv_bytes_per_query": kvb["total"],
                    "kv_GBps": round(kv_gbps, 1), "kv_frac_of_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),

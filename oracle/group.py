@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).  Uses
 the same seeded inputs as the device harness, the oracle's own FP4 caches
 (quantized here from the fp32 source rows) and the same static wiring of
 modes: Reindex searches the Full layer's caches (inside its pool when it kept
-one); Reuse takes the latest Full/Reindex selection.
+one); Reuse takes the latest Full/Reindex selection; a window-only layer
+attends to its window alone.  Every group of the layer plan sees the same
+cache contents (the device keeps one identical copy per group).
 """
 from __future__ import annotations
 
@@ -66,6 +68,10 @@ class SeqGroup:
                     kw = dict(pool_in=pool[0], pool_count_in=pool[1])
                 r = layer_step(REINDEX, ix_codes=self.ixc, ix_scales=self.ixs,
                                q_idx=L["q_idx"], w_idx=L["w_idx"], **kw, **common)
+            elif mode == I.SWA:
+                # window-only layer: a Reuse call with no global entries
+                common["K"] = 0
+                r = layer_step(REUSE, idx_in=np.zeros((len(self.tok), 0), np.int32), **common)
             else:
                 r = layer_step(REUSE, idx_in=last_idx, **common)
             if mode in (FULL, REINDEX):

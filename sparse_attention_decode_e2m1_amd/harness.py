@@ -5,7 +5,9 @@ Builds the caches and per-layer inputs of a ``inputs.Workload`` on the GPU
 order through ``api.layer_step``.  Wiring between layers follows the static
 modes: a Reindex layer reuses the caches of the group's Full layer (and its
 candidate pool when that layer kept one); a Reuse layer takes the Top-K
-indices of the latest Full/Reindex layer.
+indices of the latest Full/Reindex layer; a window-only layer attends to its
+window alone (Top-K 0).  Each Full layer starts a group with its own cache
+set (identical contents: the caches come from the same seeded rows).
 """
 from __future__ import annotations
 
@@ -35,8 +37,9 @@ class LayerBuffers:
 
 
 class DeviceWorkload:
-    """Caches (``copies`` identical sets, so a timed loop can rotate through
-    more bytes than the 256 MB last-level cache holds) and layer buffers."""
+    """Caches (``copies`` identical sets per layer group, so a timed loop can
+    rotate through more bytes than the 256 MB last-level cache holds) and
+    layer buffers."""
 
     def __init__(self, w: I.Workload, copies: int = 1, device: str = "cuda",
                  seqs: Optional[List[int]] = None):
@@ -64,8 +67,11 @@ class DeviceWorkload:
             self.new_ikey[b * T:(b + 1) * T] = c.ikey[ctx0:].to(new_dtype).to(device)
             del kv_b, ik_b, c
         torch.cuda.synchronize()
+        self.group = I.group_of_layers(w.modes)
+        self.ngroups = max(self.group) + 1
+        self.rot = max(1, copies)  # rotation sets; set c, group g uses caches[c * ngroups + g]
         self.caches = [(kvc, kvs, ixc, ixs)]
-        for _ in range(copies - 1):
+        for _ in range(self.rot * self.ngroups - 1):
             self.caches.append(tuple(t.clone() for t in (kvc, kvs, ixc, ixs)))
         self.q_pos = torch.tensor([w.ctx0 + t for b in range(B) for t in range(T)],
                                   dtype=torch.int32, device=device)
@@ -82,6 +88,7 @@ class DeviceWorkload:
                 scs.append(L.swa_scale)
                 p0s.append(L.swa_pos0)
             has_pool = mode == I.FULL and w.P > 0
+            K = 0 if mode == I.SWA else w.K
             self.layers.append(LayerBuffers(
                 mode=mode,
                 q=torch.cat(qs).contiguous().to(device),
@@ -90,7 +97,7 @@ class DeviceWorkload:
                 swa=torch.stack(swas).contiguous().to(device),
                 swa_scale=torch.tensor(scs, dtype=torch.float32, device=device),
                 swa_pos0=torch.tensor(p0s, dtype=torch.int32, device=device),
-                idx_out=torch.full((self.rows, w.K), -1, dtype=torch.int32, device=device),
+                idx_out=torch.full((self.rows, max(K, 1)), -1, dtype=torch.int32, device=device),
                 out=torch.zeros((self.rows, w.H, w.DV), dtype=torch.float32, device=device),
                 lse=torch.zeros((self.rows, w.H), dtype=torch.float32, device=device),
                 pool_out=torch.full((self.rows, w.P), -1, dtype=torch.int32, device=device)
@@ -99,7 +106,7 @@ class DeviceWorkload:
                 if has_pool else None,
             ))
         self.S = self.layers[0].swa.shape[1]
-        self._args = [self._layer_args(li, c) for c in range(len(self.caches))
+        self._args = [self._layer_args(li, c) for c in range(self.rot)
                       for li in range(len(self.layers))]
         nbytes = max(api.workspace_bytes(a[0], a[1]) for a in self._args)
         self.ws = api.workspace(nbytes, device)
@@ -108,19 +115,22 @@ class DeviceWorkload:
     # ------------------------------------------------------------------
     def _layer_args(self, li: int, copy: int):
         w = self.w
-        kvc, kvs, ixc, ixs = self.caches[copy]
+        kvc, kvs, ixc, ixs = self.caches[copy * self.ngroups + self.group[li]]
         L = self.layers[li]
         mode = L.mode
         src_idx = None
         pool_src = None
         for j in range(li - 1, -1, -1):
+            if self.group[j] != self.group[li]:
+                break
             m = self.layers[j].mode
             if src_idx is None and m in (I.FULL, I.REINDEX):
                 src_idx = self.layers[j].idx_out
             if m == I.FULL and self.layers[j].pool_out is not None and pool_src is None:
                 pool_src = self.layers[j]
         kw = dict(
-            B=w.B, T=w.T, H=w.H, D=w.D, dv=w.DV, H_I=w.HI, D_I=w.DI, K=w.K,
+            B=w.B, T=w.T, H=w.H, D=w.D, dv=w.DV, H_I=w.HI, D_I=w.DI,
+            K=0 if mode == I.SWA else w.K,
             P=w.P if (mode == I.FULL) else 0, S=self.S, W=w.W, sm_scale=w.sm_scale,
             kv=api.cache(kvc, kvs, w.D, w.N), icache=api.cache(ixc, ixs, w.DI, w.N),
             q_pos=self.q_pos, q=L.q, swa=L.swa, swa_scale=L.swa_scale, swa_pos0=L.swa_pos0,
@@ -136,19 +146,21 @@ class DeviceWorkload:
             if pool_src is not None:
                 kw.update(pool_in=pool_src.pool_out, pool_count_in=pool_src.pool_count,
                           P_in=w.P)
-        else:
+        elif mode == I.REUSE:
             kw.update(idx_in=src_idx)
-        return mode, api.layer_args(**kw)
+        # a window-only layer is a Reuse call with no global entries
+        return (I.REUSE if mode == I.SWA else mode), api.layer_args(**kw)
 
     def step(self, copy: int = 0, stream=None):
         """One pass of every layer of the group, in order."""
         n = len(self.layers)
+        c = copy % self.rot
         for li in range(n):
-            mode, args = self._args[copy * n + li]
+            mode, args = self._args[c * n + li]
             api.layer_step(mode, args, self.ws, stream=stream)
 
     def run_layer(self, li: int, copy: int = 0, stream=None):
-        mode, args = self._args[copy * len(self.layers) + li]
+        mode, args = self._args[(copy % self.rot) * len(self.layers) + li]
         api.layer_step(mode, args, self.ws, stream=stream)
 
     def cache_bytes(self):

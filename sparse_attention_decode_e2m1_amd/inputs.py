@@ -19,6 +19,8 @@ import torch
 
 T_KV, T_IKEY, T_Q, T_QI, T_W, T_SWA, T_SAL = range(7)
 FULL, REINDEX, REUSE = 0, 1, 2
+SWA = 3  # a layer that attends to its own window only (no global entries)
+MODE_NAMES = ("FULL", "REINDEX", "REUSE", "SWA")
 
 
 @dataclass(frozen=True)
@@ -60,7 +62,37 @@ C4 = Workload("C4_pool_1m", 3, B=1, N=1048576, K=2048,
               modes=(FULL, REINDEX, REINDEX), P=16384, salient=True)
 C5 = Workload("C5_prefill_4k_on_128k", 4, B=1, N=135168, K=2048,
               modes=(FULL,), T=4096)
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
+
+
+def forty_layer_modes() -> tuple:
+    """The static layer plan of the pages' 40-layer model (helmcode.com/
+    deepseek-v41-flash, section "03 · CSA2": 4 Full, 4 Reindex and 30 Reuse
+    attention layers plus 2 window-only layers, the window-only ones first).
+    The pages give the counts, not the order of the rest; read here as four
+    groups of a Full layer, then its Reindex layer, then Reuse layers (8, 8,
+    7, 7), each group over its own caches."""
+    modes = [SWA, SWA]
+    for n in (8, 8, 7, 7):
+        modes += [FULL, REINDEX] + [REUSE] * n
+    return tuple(modes)
+
+
+# The 40-layer decode step at contexts 4K .. 1M (one sequence, Top-K 2048).
+F1 = tuple(Workload(f"F1_40layer_{tag}", 5 + j, B=1, N=n, K=2048, modes=forty_layer_modes())
+           for j, (tag, n) in enumerate((("4k", 4096), ("16k", 16384), ("64k", 65536),
+                                         ("256k", 262144), ("1m", 1048576))))
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5) + F1}
+
+
+def group_of_layers(modes) -> list:
+    """Cache group of each layer: each Full layer starts a group with its
+    own caches; layers before the first Full layer belong to group 0."""
+    g, out = -1, []
+    for m in modes:
+        if m == FULL:
+            g += 1
+        out.append(max(g, 0))
+    return out
 
 
 def seed(c: int, b: int, layer: int, t: int) -> int:

@@ -62,6 +62,9 @@ def compare_group(w, dw, ores, ocaches, seqs=None, tokens=None):
     seqs = list(range(w.B)) if seqs is None else seqs
     tok = list(range(w.T)) if tokens is None else tokens
     kvc, kvs, ixc, ixs = (host(t) for t in dw.caches[0])
+    for extra in dw.caches[1:]:  # every group's copy holds the same rows after the step
+        for a, t in zip((kvc, kvs, ixc, ixs), extra):
+            assert np.array_equal(a, host(t))
     same_sets = 0
     for b in seqs:
         okvc, okvs, oixc, oixs = ocaches[b]
@@ -85,7 +88,7 @@ def compare_group(w, dw, ores, ocaches, seqs=None, tokens=None):
                         continue  # a legitimate near-tie swap: outputs differ by design
                     same_sets += 1
                 if L.mode == I.REUSE:
-                    src = [x for x in range(li) if dw.layers[x].mode != I.REUSE][-1]
+                    src = [x for x in range(li) if dw.layers[x].mode in (I.FULL, I.REINDEX)][-1]
                     if not np.array_equal(host(dw.layers[src].idx_out)[row], ores[b][src].idx[j]):
                         continue
                 assert_attention_close(gout[row], r.out[j], what=what)

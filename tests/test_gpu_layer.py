@@ -97,3 +97,19 @@ def test_step_is_deterministic_and_leaves_workspace_clean():
         assert torch.equal(L.idx_out, i0) and torch.equal(L.out, o0) and torch.equal(L.lse, l0)
     ctl = dw.ws[: api.lib().csa2_workspace_control_bytes(dw.rows)].view(torch.int32)
     assert int(torch.count_nonzero(ctl)) == 0
+
+
+def test_forty_layer_plan_small():
+    """The 40-layer static plan (2 window-only layers, then 4 groups of Full,
+    Reindex and Reuse layers, each group over its own cache copy) against the
+    oracle, layer by layer."""
+    w = I.small("t_forty", 64, B=1, N=3000, K=256, modes=I.forty_layer_modes())
+    dw = Hn.DeviceWorkload(w)
+    assert dw.ngroups == 4 and len(dw.caches) == 4
+    dw.step()
+    torch.cuda.synchronize()
+    ores, oc = run_group(w, keep_scores=True)
+    assert compare_group(w, dw, ores, oc) >= 6
+    ctl = dw.ws[: api.lib().csa2_workspace_control_bytes(dw.rows)].view(torch.int32)
+    assert int(torch.count_nonzero(ctl)) == 0
+

@@ -206,3 +206,25 @@ def test_prefill_one_token_equals_decode(oracle):
     assert np.array_equal(b.out[2], a.out[0])
     # causality: the first token of the chunk sees nothing beyond itself
     assert b.idx[0].max() <= w.N - 3
+
+
+def test_forty_layer_plan_and_window_only_layer(oracle):
+    """The 40-layer plan's counts (helmcode.com/deepseek-v41-flash, section
+    "03 · CSA2": 4 Full, 4 Reindex, 30 Reuse, 2 window-only) and grouping, and
+    a window-only layer equal to dense attention over its window rows."""
+    modes = I.forty_layer_modes()
+    assert len(modes) == 40 and modes[:2] == (I.SWA, I.SWA)
+    assert [modes.count(m) for m in (I.FULL, I.REINDEX, I.REUSE, I.SWA)] == [4, 4, 30, 2]
+    g = I.group_of_layers(modes)
+    starts = [i for i, m in enumerate(modes) if m == I.FULL]
+    assert g[:2] == [0, 0] and [g[i] for i in starts] == [0, 1, 2, 3]
+    assert all(modes[i + 1] == I.REINDEX for i in starts)
+    from oracle.group import SeqGroup
+    w = I.small("t_swa", 91, B=1, N=500, K=32, modes=(I.SWA, I.FULL, I.REUSE), W=16)
+    res = SeqGroup(w, 0).step()
+    L = I.layer_inputs(w, 0, 0)
+    rows = fp8_decode(L.swa.numpy()) * L.swa_scale  # S = W rows, positions N-W .. N-1
+    ref_o, ref_l = dense_attention(L.q.float().numpy()[0], rows, w.sm_scale, w.DV)
+    assert np.allclose(res[0].out[0], ref_o, rtol=1e-9, atol=1e-12)
+    assert np.allclose(res[0].lse[0], ref_l, rtol=1e-9, atol=1e-12)
+    assert (res[0].idx.size == 0) or (res[0].idx == -1).all()
