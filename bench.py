@@ -75,6 +75,38 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"{el:.1f} s (set-up {setup:.1f} s untimed)"}
 
 
+def time_rope_quantize(rows: int, reps: int = 50) -> dict:
+    """Fused rotary + quantize-on-write of `rows` bf16 rows of 576 channels
+    (last 64 rotary) against the plain quantize-on-write, HIP events around
+    `reps` launches of each; rows scattered into a 4x larger cache."""
+    import torch
+    from sparse_attention_decode_e2m1_amd import api
+    from sparse_attention_decode_e2m1_amd import inputs as I
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(rows, 576, generator=g).to(torch.bfloat16).cuda()
+    cs = I.rope_cos_sin(torch.randint(0, 1 << 20, (rows,), generator=g), 64).cuda()
+    dst = torch.randperm(4 * rows, generator=g)[:rows].cuda()
+    codes = torch.zeros((4 * rows, 288), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((4 * rows, 36), dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, fn in (("rope_quantize", lambda: api.rope_quantize_kv(x, 64, cs, codes, scales, dst)),
+                     ("quantize", lambda: api.quantize_kv(x, codes, scales, dst))):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = rows * (576 * 2 + 324 + 8) + (rows * 32 * 8 if name == "rope_quantize" else 0)
+        res[name] = {"us_per_launch": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+    return {"rope_quantize_rows": rows, "channels": 576, "rotary_channels": 64, "input": "bf16",
+            **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +117,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--rope-quantize-rows", type=int, default=0,
+                    help="only time the fused rotary + quantize-on-write of this many bf16 rows "
+                         "(576 channels, 64 rotary) against the plain quantize-on-write, and exit")
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (the "
                          "reference kernel that calibrates the HBM byte counters) and exit")
@@ -107,6 +142,10 @@ def main():
             torch.mul(src, 1.0, out=dst)  # one elementwise pass: reads n*4, writes n*4 bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "passes": 5}), flush=True)
+        return
+
+    if args.rope_quantize_rows:
+        print(json.dumps(time_rope_quantize(args.rope_quantize_rows)), flush=True)
         return
 
     w = I.WORKLOADS[args.workload]

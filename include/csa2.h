@@ -108,6 +108,27 @@ csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int3
                              int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
                              uint8_t* scales, void* stream);
 
+/* Rotary embedding fused with the quantize-on-write ([P1 §04 "FP4"]: the
+ * quantisation is applied after RoPE; the pages give no rotary parameters, so
+ * the angles come from the caller).  The last rope_dim channels of each row
+ * hold rotary pairs (channels dim-rope_dim+2i, +2i+1); pair i of row r is
+ * rotated by the caller's (c, s) = cos_sin[r][i]:
+ *   y0 = x0*c - x1*s,  y1 = x0*s + x1*c,
+ * each product and each sum rounded to fp32 separately (no fused
+ * multiply-add), then every 16-channel block is quantized exactly as by
+ * csa2_quantize_kv.
+ *
+ *   rope_dim : a multiple of 16 in [0, dim] (0: plain quantize-on-write).
+ *   cos_sin  : device fp32 [rows][rope_dim/2][2] (cos, sin); may be NULL
+ *              when rope_dim == 0.
+ *   other arguments as csa2_quantize_kv.
+ * Errors: those of csa2_quantize_kv, a rope_dim out of range, cos_sin NULL
+ * with rope_dim > 0. */
+csa2_status csa2_rope_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                                  int64_t x_row_stride, int32_t rope_dim, const float* cos_sin,
+                                  const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                                  void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Indexer scoring ([P1 §03 "CSA2"]: a Reindex layer scores positions again
  * with its own query; [P4 "Share the cache and the search work"]: the first

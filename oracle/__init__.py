@@ -109,6 +109,32 @@ def quantize(x) -> tuple[np.ndarray, np.ndarray]:
     return codes, scales
 
 
+def rope_rotate(x, cos_sin, rope_dim: int) -> np.ndarray:
+    """Rotary pairs of the last rope_dim channels ([P1 §04]: the FP4
+    quantisation is applied after RoPE; the pages give no rotary parameters,
+    so the per-pair (cos, sin) come in as inputs).  Pair i = channels
+    (dim - rope_dim + 2i, +1): y0 = x0 c - x1 s, y1 = x0 s + x1 c, written in
+    float32 with every product and every sum rounded on its own (numpy's
+    float32 arithmetic: no fused multiply-add).  x: [rows][dim];
+    cos_sin: [rows][rope_dim/2][2]."""
+    x = np.array(x, dtype=np.float32, copy=True)
+    if rope_dim == 0:
+        return x
+    cs = np.asarray(cos_sin, dtype=np.float32)
+    c, sn = cs[..., 0], cs[..., 1]
+    base = x.shape[1] - rope_dim
+    x0 = x[:, base::2].copy()
+    x1 = x[:, base + 1::2].copy()
+    x[:, base::2] = (x0 * c) - (x1 * sn)
+    x[:, base + 1::2] = (x0 * sn) + (x1 * c)
+    return x
+
+
+def rope_quantize(x, cos_sin, rope_dim: int) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize-on-write after the rotary step: quantize(rope_rotate(x))."""
+    return quantize(rope_rotate(x, cos_sin, rope_dim))
+
+
 def dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)

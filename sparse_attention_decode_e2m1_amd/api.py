@@ -65,6 +65,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "csa2_quantize_kv": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p, c_p]),
+            "csa2_rope_quantize_kv": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i64, c_i32, c_p, c_p,
+                                              c_p, c_p, c_p]),
             "csa2_index_score": (c_i32, [ctypes.POINTER(Fp4Cache), c_i32, c_i32, c_p, c_p, c_i32,
                                          c_p, c_p, c_i32, c_i64, c_p, c_p]),
             "csa2_topk_workspace_bytes": (c_sz, [c_i32, c_i64, c_i32]),
@@ -153,6 +155,18 @@ def quantize_kv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     rows, dim = x.shape
     _check(lib().csa2_quantize_kv(_ptr(x), dt, rows, dim, x.stride(0), _ptr(dst_rows),
                                   _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def rope_quantize_kv(x: torch.Tensor, rope_dim: int, cos_sin: Optional[torch.Tensor],
+                     codes: torch.Tensor, scales: torch.Tensor,
+                     dst_rows: Optional[torch.Tensor] = None, stream=None):
+    """csa2_rope_quantize_kv: rotary pairs of the last rope_dim channels
+    rotated by cos_sin [rows][rope_dim/2][2] (fp32), then quantize-on-write."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    rows, dim = x.shape
+    _check(lib().csa2_rope_quantize_kv(_ptr(x), dt, rows, dim, x.stride(0), rope_dim,
+                                       _ptr(cos_sin), _ptr(dst_rows), _ptr(codes), _ptr(scales),
+                                       _stream(stream)))
 
 
 def index_score(icache: Fp4Cache, B: int, T: int, q_idx: torch.Tensor, w: torch.Tensor,

@@ -245,6 +245,28 @@ csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int3
   return CSA2_OK;
 }
 
+csa2_status csa2_rope_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                                  int64_t x_row_stride, int32_t rope_dim, const float* cos_sin,
+                                  const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                                  void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(dtype == CSA2_F32 || dtype == CSA2_BF16, CSA2_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  CSA2_REQUIRE(rows >= 0, CSA2_ERR_SHAPE, "rows < 0");
+  CSA2_REQUIRE(dim > 0 && dim % 16 == 0 && dim <= 4096, CSA2_ERR_SHAPE,
+               "dim must be a positive multiple of 16 <= 4096 (got %d)", dim);
+  CSA2_REQUIRE(rope_dim >= 0 && rope_dim % 16 == 0 && rope_dim <= dim, CSA2_ERR_SHAPE,
+               "rope_dim must be a multiple of 16 in [0, dim] (got %d)", rope_dim);
+  CSA2_REQUIRE(x_row_stride >= dim, CSA2_ERR_SHAPE, "row stride %lld < dim %d",
+               (long long)x_row_stride, dim);
+  if (rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(x && codes && scales, CSA2_ERR_NULL, "x, codes and scales are required");
+  CSA2_REQUIRE(rope_dim == 0 || cos_sin, CSA2_ERR_NULL, "cos_sin is required when rope_dim > 0");
+  CSA2_LAUNCH(0, PROF_STREAM, launch_rope_quantize(x, dtype == CSA2_BF16, rows, dim, x_row_stride, rope_dim,
+                                                   cos_sin, dst_rows, codes, scales, as_stream(stream)),
+              "rope quantize launch");
+  return CSA2_OK;
+}
+
 // ------------------------------------------------------------ index score
 static csa2_status check_icache(const csa2_fp4_cache* c, const char* name) {
   CSA2_REQUIRE(c, CSA2_ERR_NULL, "%s cache descriptor is NULL", name);

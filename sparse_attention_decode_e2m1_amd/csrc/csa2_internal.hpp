@@ -85,6 +85,10 @@ LaunchTiming& launch_timing();
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
                            const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
+hipError_t launch_rope_quantize(const void* x, bool bf16, int64_t rows, int32_t dim,
+                                int64_t stride, int32_t rope_dim, const float* cos_sin,
+                                const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st);
 hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32_t DI,
                               int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
                               const float* w, int32_t HI, const int32_t* n_valid,

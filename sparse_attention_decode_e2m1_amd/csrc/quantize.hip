@@ -64,17 +64,13 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) {
   return bf16_to_f32(*p);
 }
 
-// Quantize one 16-channel block: 8 code bytes and one scale byte.
-template <typename In>
-__device__ __forceinline__ void quantize_block(const In* __restrict__ src, uint8_t* code_dst,
-                                               uint8_t* scale_dst) {
-  float v[16];
+// Quantize one 16-channel block held in registers: 8 code bytes and one
+// scale byte.
+__device__ __forceinline__ void quantize_values(const float (&v)[16], uint8_t* code_dst,
+                                                uint8_t* scale_dst) {
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    v[c] = load_elem<In>(src + c);
-    amax = fmaxf(amax, fabsf(v[c]));
-  }
+  for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
   const int sb = scale_byte(amax);
   const float s = e4m3_pos(sb);
   uint64_t packed = 0;
@@ -86,6 +82,16 @@ __device__ __forceinline__ void quantize_block(const In* __restrict__ src, uint8
   }
   *reinterpret_cast<uint64_t*>(code_dst) = packed;
   *scale_dst = (uint8_t)sb;
+}
+
+// Quantize one 16-channel block read from memory.
+template <typename In>
+__device__ __forceinline__ void quantize_block(const In* __restrict__ src, uint8_t* code_dst,
+                                               uint8_t* scale_dst) {
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v[c] = load_elem<In>(src + c);
+  quantize_values(v, code_dst, scale_dst);
 }
 
 // One thread per 16-channel block.
@@ -103,6 +109,60 @@ __global__ __launch_bounds__(256) void quantize_kernel(const In* __restrict__ x,
   const int64_t dr = dst_rows ? dst_rows[r] : r;
   quantize_block<In>(x + r * stride + (int64_t)blk * 16, codes + dr * (dim >> 1) + (int64_t)blk * 8,
                      scales + dr * nb + blk);
+}
+
+// Rotary embedding fused with the quantize-on-write (the quantisation is
+// applied after RoPE).  The last rope_dim channels of a row form pairs
+// (2i, 2i+1) of that region, rotated by the row's angle for pair i:
+//   y0 = x0 c - x1 s,  y1 = x0 s + x1 c
+// with c, s given per row and pair (cos_sin[row][i] = {c, s}); each product
+// and each sum is rounded to fp32 separately (no fused multiply-add), so the
+// rotated values, and hence the codes, are reproducible.  One thread per
+// 16-channel block.
+template <typename In>
+__global__ __launch_bounds__(256) void rope_quantize_kernel(
+    const In* __restrict__ x, int64_t rows, int32_t dim, int64_t stride, int32_t rope_dim,
+    const float2* __restrict__ cos_sin, const int64_t* __restrict__ dst_rows,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int32_t nb = dim >> 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * nb) return;
+  const int64_t r = t / nb;
+  const int32_t blk = (int32_t)(t - r * nb);
+  const int64_t dr = dst_rows ? dst_rows[r] : r;
+  float v[16];
+  const In* src = x + r * stride + (int64_t)blk * 16;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v[c] = load_elem<In>(src + c);
+  const int32_t c0 = blk * 16 - (dim - rope_dim);  // channel offset inside the rope region
+  if (c0 >= 0) {
+    const float2* cs = cos_sin + r * (rope_dim >> 1) + (c0 >> 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 a = cs[j];
+      const float x0 = v[2 * j], x1 = v[2 * j + 1];
+      v[2 * j] = __fsub_rn(__fmul_rn(x0, a.x), __fmul_rn(x1, a.y));
+      v[2 * j + 1] = __fadd_rn(__fmul_rn(x0, a.y), __fmul_rn(x1, a.x));
+    }
+  }
+  quantize_values(v, codes + dr * (dim >> 1) + (int64_t)blk * 8, scales + dr * nb + blk);
+}
+
+hipError_t launch_rope_quantize(const void* x, bool bf16, int64_t rows, int32_t dim,
+                                int64_t stride, int32_t rope_dim, const float* cos_sin,
+                                const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st) {
+  const int64_t n = rows * (dim / 16);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  const float2* cs = reinterpret_cast<const float2*>(cos_sin);
+  if (bf16)
+    CSA2_KERNEL(true, true, rope_quantize_kernel<uint16_t>, grid, block, 0, st,
+                (const uint16_t*)x, rows, dim, stride, rope_dim, cs, dst_rows, codes, scales);
+  else
+    CSA2_KERNEL(true, true, rope_quantize_kernel<float>, grid, block, 0, st, (const float*)x,
+                rows, dim, stride, rope_dim, cs, dst_rows, codes, scales);
+  return hipGetLastError();
 }
 
 // The write of a decode or prefill step: query row r of x1 and x2 lands on

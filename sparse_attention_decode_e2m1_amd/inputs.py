@@ -125,6 +125,17 @@ def fp8_rows(x: torch.Tensor):
     return b.contiguous(), float(scale)
 
 
+def rope_cos_sin(positions, rope_dim: int, base: float = 10000.0) -> torch.Tensor:
+    """Rotary angles of the standard form (upstream of the path; the pages
+    give no rotary parameters): pair i of a row at position p turns by
+    p * base**(-2i/rope_dim).  Returns fp32 [len(positions)][rope_dim/2][2]
+    (cos, sin), evaluated in float64 and rounded once."""
+    pos = torch.as_tensor(positions, dtype=torch.float64).reshape(-1, 1)
+    i = torch.arange(rope_dim // 2, dtype=torch.float64).reshape(1, -1)
+    ang = pos * torch.pow(torch.tensor(base, dtype=torch.float64), -2.0 * i / rope_dim)
+    return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).to(torch.float32).contiguous()
+
+
 def salient_direction(w: Workload, b: int) -> torch.Tensor:
     u = randn((w.DI,), seed(w.index, b, 0, T_SAL))
     return u / u.norm()

@@ -56,6 +56,16 @@ def test_quantize_rejects(L):
     assert q(None, 0, 0, 576, 576, None, None, None, None) == 0          # nothing to do
 
 
+def test_rope_quantize_rejects(L):
+    q = L.csa2_rope_quantize_kv
+    assert q(FAKE, 7, 4, 576, 576, 64, FAKE, None, FAKE, FAKE, None) == 3   # dtype
+    assert q(FAKE, 0, 4, 576, 576, 60, FAKE, None, FAKE, FAKE, None) == 2   # rope_dim % 16
+    assert q(FAKE, 0, 4, 576, 576, 592, FAKE, None, FAKE, FAKE, None) == 2  # rope_dim > dim
+    assert q(FAKE, 0, 4, 576, 576, 64, None, None, FAKE, FAKE, None) == 1   # cos_sin missing
+    assert b"cos_sin" in L.csa2_last_error()
+    assert q(FAKE, 0, 0, 576, 576, 64, None, None, None, None, None) == 0   # nothing to do
+
+
 def test_index_score_rejects(L):
     c = api.Fp4Cache(FAKE, FAKE, 100, 16)
     f = L.csa2_index_score

@@ -83,6 +83,35 @@ def test_quantize_bf16_and_scatter():
     assert (hc[untouched] == 0).all()
 
 
+@pytest.mark.parametrize("dim,rope,dtype", [(576, 64, "f32"), (576, 64, "bf16"), (576, 0, "f32"),
+                                             (128, 128, "f32")])
+def test_rope_quantize_bit_exact(dim, rope, dtype):
+    """Fused rotary step + quantize-on-write against the oracle's rope_quantize
+    on the same inputs and angle tables (scattered destination rows)."""
+    rng = np.random.default_rng(dim + rope)
+    n = 1500
+    x = (rng.standard_normal((n, dim)) * 10.0 ** rng.uniform(-3, 2, (n, 1))).astype(np.float32)
+    xt = torch.from_numpy(x)
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+        x = xt.float().numpy()
+    pos = rng.integers(0, 1 << 20, n)
+    cs = I.rope_cos_sin(pos, rope) if rope else torch.zeros((n, 0, 2))
+    dst = torch.from_numpy(rng.permutation(2 * n)[:n].astype(np.int64))
+    codes = torch.zeros((2 * n, dim // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((2 * n, dim // 16), dtype=torch.uint8, device="cuda")
+    api.rope_quantize_kv(xt.cuda(), rope, cs.cuda() if rope else None, codes, scales,
+                         dst_rows=dst.cuda())
+    torch.cuda.synchronize()
+    oc, os_ = oracle.rope_quantize(x, cs.numpy(), rope)
+    hc, hs = host(codes), host(scales)
+    assert np.array_equal(hs[dst.numpy()], os_)
+    assert np.array_equal(hc[dst.numpy()], oc)
+    if rope:
+        plain_c, _ = oracle.quantize(x)
+        assert not np.array_equal(plain_c[:, (dim - rope) // 2:], oc[:, (dim - rope) // 2:])
+
+
 # ------------------------------------------------------------ index score
 def _index_case(seed, B, cap, DI, HI, n_valid):
     rng = np.random.default_rng(seed)

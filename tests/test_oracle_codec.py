@@ -229,3 +229,63 @@ def test_bytes_per_token(oracle):
     # a 1,048,576-token main cache is about 0.3 GB (0.34 GB)
     gb = 1048576 * 324 / 1e9
     assert 0.3 <= gb < 0.35
+
+
+# ------------------------------------------------------------ rotary step
+def _rope_case(seed, rows=40, dim=576, rope=64):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, dim)).astype(np.float32)
+    from sparse_attention_decode_e2m1_amd import inputs as I
+    pos = rng.integers(0, 1 << 20, rows)
+    return x, pos, I.rope_cos_sin(pos, rope).numpy()
+
+
+def test_rope_identity_and_quarter_turn(oracle):
+    """Angle 0 leaves a row unchanged (so the codes equal plain quantize);
+    a quarter turn maps each pair (x0, x1) to (-x1, x0) exactly."""
+    x, _, cs = _rope_case(30)
+    ident = np.zeros_like(cs)
+    ident[..., 0] = 1.0
+    assert np.array_equal(oracle.rope_rotate(x, ident, 64), x)
+    for a, b in zip(oracle.rope_quantize(x, ident, 64), oracle.quantize(x)):
+        assert np.array_equal(a, b)
+    quarter = np.zeros_like(cs)
+    quarter[..., 1] = 1.0
+    y = oracle.rope_rotate(x, quarter, 64)
+    assert np.array_equal(y[:, :512], x[:, :512])
+    assert np.array_equal(y[:, 512::2], -x[:, 513::2])
+    assert np.array_equal(y[:, 513::2], x[:, 512::2])
+
+
+def test_rope_matches_complex_rotation(oracle):
+    """Against the rotation as a float64 complex product (the plain
+    definition): each output within two float32 rounding steps of the pair's
+    size; the pair norm is kept; turning back by -angle restores the row."""
+    x, _, cs = _rope_case(31)
+    y = oracle.rope_rotate(x, cs, 64).astype(np.float64)
+    z = (x[:, 512::2] + 1j * x[:, 513::2]).astype(np.complex128) * \
+        (cs[..., 0] + 1j * cs[..., 1]).astype(np.complex128)
+    mag = np.abs(x[:, 512::2].astype(np.float64)) + np.abs(x[:, 513::2].astype(np.float64))
+    tol = 2.0 ** -22 * mag + 1e-30
+    assert (np.abs(y[:, 512::2] - z.real) <= tol).all()
+    assert (np.abs(y[:, 513::2] - z.imag) <= tol).all()
+    n0 = np.hypot(x[:, 512::2].astype(np.float64), x[:, 513::2].astype(np.float64))
+    n1 = np.hypot(y[:, 512::2], y[:, 513::2])
+    assert np.allclose(n1, n0, rtol=1e-6, atol=1e-7)
+    back = cs.copy()
+    back[..., 1] = -back[..., 1]
+    r = oracle.rope_rotate(y.astype(np.float32), back, 64)
+    assert np.allclose(r, x, rtol=1e-6, atol=1e-6)
+
+
+def test_rope_angle_table():
+    """Pair 0 turns by the position itself, the last pair by
+    position * base^(-(rope-2)/rope); position 0 gives (1, 0)."""
+    from sparse_attention_decode_e2m1_amd import inputs as I
+    cs = I.rope_cos_sin([0, 1, 12345], 64).numpy().astype(np.float64)
+    assert np.array_equal(cs[0, :, 0], np.ones(32)) and np.array_equal(cs[0, :, 1], np.zeros(32))
+    assert math.isclose(cs[2, 0, 0], math.cos(12345.0), abs_tol=1e-7)
+    assert math.isclose(cs[2, 0, 1], math.sin(12345.0), abs_tol=1e-7)
+    a = 12345.0 * 10000.0 ** (-62.0 / 64.0)
+    assert math.isclose(cs[2, 31, 0], math.cos(a), abs_tol=1e-7)
+    assert math.isclose(cs[1, 31, 1], math.sin(10000.0 ** (-62.0 / 64.0)), rel_tol=1e-6)
