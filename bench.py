@@ -107,6 +107,72 @@ def time_rope_quantize(rows: int, reps: int = 50) -> dict:
             **res}
 
 
+def time_attn_fp4_vs_fp8(B: int, N: int, K: int, W: int, copies: int, reps: int = 64) -> dict:
+    """Sparse attention of B decode queries (16 heads, 576 channels, Top-K K
+    plus a W-token FP8 window) over an FP4 main cache (E2M1 + E4M3 per 16
+    channels, 324 B a row) and over an FP8 one (E4M3 + fp32 per row, 580 B a
+    row) holding the same quantized rows' source values.  HIP events around
+    `reps` launches of each; every launch takes the next of `copies` cache
+    sets and its own random Top-K rows, so that rows are gathered from HBM
+    rather than found in the last-level cache."""
+    import torch
+    from sparse_attention_decode_e2m1_amd import api
+    from sparse_attention_decode_e2m1_amd import inputs as I
+    g = torch.Generator().manual_seed(11)
+    gd = torch.Generator(device="cuda").manual_seed(11)
+    D, S = 576, 128
+    c4 = torch.empty((B, N, D // 2), dtype=torch.uint8, device="cuda")
+    s4 = torch.empty((B, N, D // 16), dtype=torch.uint8, device="cuda")
+    c8 = torch.empty((B, N, D), dtype=torch.uint8, device="cuda")
+    s8 = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        x = torch.randn((N, D), generator=gd, device="cuda").to(torch.bfloat16)
+        api.quantize_kv(x, c4[b], s4[b])
+        api.quantize_kv_fp8(x, c8[b], s8[b])
+        del x
+    sets4 = [(c4, s4)] + [(c4.clone(), s4.clone()) for _ in range(copies - 1)]
+    sets8 = [(c8, s8)] + [(c8.clone(), s8.clone()) for _ in range(copies - 1)]
+    swa_b, swa_s = I.fp8_rows(torch.randn((B * S, D), generator=g))
+    swa = swa_b.reshape(B, S, D).cuda()
+    swa_scale = torch.full((B,), float(swa_s), dtype=torch.float32, device="cuda")
+    pos0 = torch.full((B,), N - S, dtype=torch.int32, device="cuda")
+    q_pos = torch.full((B,), N - 1, dtype=torch.int32, device="cuda")
+    q = torch.randn((B, 16, D), generator=g).to(torch.bfloat16).cuda()
+    idx = [torch.stack([torch.sort(torch.randperm(N, generator=g)[:K])[0] for _ in range(B)])
+           .to(torch.int32).cuda() for _ in range(copies)]
+    out = torch.empty((B, 16, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, 16), dtype=torch.float32, device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(B, K, W, 512))
+    sm = 1.0 / D ** 0.5
+    cache4 = [api.cache(c, s, D, N) for c, s in sets4]
+    cache8 = [api.fp8_cache(c, s, D, N) for c, s in sets8]
+    run = {
+        "fp4": lambda i: api.sparse_attn(q, B, 1, cache4[i % copies], idx[i % copies], K, swa,
+                                         swa_scale, pos0, S, W, q_pos, sm, 512, out, lse, ws),
+        "fp8": lambda i: api.sparse_attn_fp8(q, B, 1, cache8[i % copies], idx[i % copies], K, swa,
+                                             swa_scale, pos0, S, W, q_pos, sm, 512, out, lse, ws),
+    }
+    row_bytes = {"fp4": D // 2 + D // 16, "fp8": D + 4}
+    res = {}
+    for name, fn in run.items():
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        per_q = K * row_bytes[name] + W * D
+        res[name] = {"us_per_launch": round(us, 2), "kv_bytes_per_query": per_q,
+                     "GBps": round(B * per_q / us / 1e3, 1)}
+    res["fp8_over_fp4_time"] = round(res["fp8"]["us_per_launch"] / res["fp4"]["us_per_launch"], 3)
+    return {"attn_kv_compare": {"B": B, "N": N, "K": K, "W": W, "heads": 16, "channels": D,
+                                "copies": copies, "launches": reps}, **res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +186,12 @@ def main():
     ap.add_argument("--rope-quantize-rows", type=int, default=0,
                     help="only time the fused rotary + quantize-on-write of this many bf16 rows "
                          "(576 channels, 64 rotary) against the plain quantize-on-write, and exit")
+    ap.add_argument("--attn-kv-compare", action="store_true",
+                    help="only time the sparse attention of the workload's decode queries over "
+                         "an FP4 and an FP8 main cache (same Top-K, window), and exit")
+    ap.add_argument("--attn-batch", type=int, default=0,
+                    help="with --attn-kv-compare: decode queries per launch (default: the "
+                         "workload's batch)")
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 5 times (the "
                          "reference kernel that calibrates the HBM byte counters) and exit")
@@ -149,6 +221,12 @@ def main():
         return
 
     w = I.WORKLOADS[args.workload]
+    if args.attn_kv_compare:
+        api.lib()
+        print(json.dumps(time_attn_fp4_vs_fp8(args.attn_batch or w.B, w.N, w.K, w.W,
+                                              max(args.copies, 8))),
+              flush=True)
+        return
     api.lib()  # fails loudly if the HIP library is missing
     print(f"[bench] workload {w.name}: B={w.B} N={w.N} T={w.T} K={w.K} modes={w.modes}; "
           f"set-up with {args.copies} cache copies", file=sys.stderr, flush=True)

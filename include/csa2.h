@@ -81,6 +81,15 @@ typedef struct {
   int64_t cap;     /* rows per sequence */
 } csa2_fp4_cache;
 
+/* Main cache in the FP8 variant (E4M3 rows with one fp32 scale per row; the
+ * earlier format the pages describe for V4 Flash's global KV, [P1 §04]). */
+typedef struct {
+  uint8_t* codes;  /* [B][cap][dim] E4M3 bytes */
+  float* scales;   /* [B][cap] */
+  int32_t dim;     /* channels per row */
+  int64_t cap;     /* rows per sequence */
+} csa2_fp8_cache;
+
 /* Limits of the kernels in this build. */
 #define CSA2_MAX_K 16384        /* Top-K and pool size */
 #define CSA2_MAX_W 16384        /* sliding-window length */
@@ -107,6 +116,17 @@ typedef struct {
 csa2_status csa2_quantize_kv(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
                              int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
                              uint8_t* scales, void* stream);
+
+/* FP8 quantize-on-write of main-cache rows (the FP8 variant; the pages give
+ * no scale layout for it, read here as one fp32 scale per row): scale =
+ * amax/448 over the row (1 for an all-zero row), byte = E4M3 of
+ * clamp(x/scale, -448, 448) rounded to nearest even (IEEE fp32 divisions).
+ *   codes  : device [rows][dim] bytes;  scales : device f32 [rows] (both at
+ *            the destination rows);  other arguments as csa2_quantize_kv.
+ * Errors: as csa2_quantize_kv. */
+csa2_status csa2_quantize_kv_fp8(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                                 int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
+                                 float* scales, void* stream);
 
 /* Rotary embedding fused with the quantize-on-write ([P1 §04 "FP4"]: the
  * quantisation is applied after RoPE; the pages give no rotary parameters, so
@@ -213,6 +233,20 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
                              int32_t S, int32_t W, const int32_t* q_pos, float sm_scale,
                              int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* The same attention over an FP8 main cache (csa2_fp8_cache; the V4-Flash
+ * style global KV of [P1 §04], E4M3 with one fp32 scale per row): a selected
+ * row's key and value are e4m3(byte) * scale[row].  The window and every
+ * other argument are as for csa2_sparse_attn (the same workspace size).
+ * Inside a split, each row's scale multiplies its logit, and the value
+ * product uses p_j * scale_j / max_scale (rounded to fp16) with the split's
+ * largest row scale applied to its partial output. */
+csa2_status csa2_sparse_attn_fp8(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                                 const csa2_fp8_cache* kv, const int32_t* idx, int32_t K,
+                                 const uint8_t* swa, const float* swa_scale,
+                                 const int32_t* swa_pos0, int32_t S, int32_t W,
+                                 const int32_t* q_pos, float sm_scale, int32_t dv, float* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* One CSA2 layer for B sequences of T query tokens each ([P1 §03 "CSA2"]:

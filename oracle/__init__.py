@@ -109,6 +109,52 @@ def quantize(x) -> tuple[np.ndarray, np.ndarray]:
     return codes, scales
 
 
+def quantize_fp8(x) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 variant of the main cache ([P1 §04]: V4 Flash stored its global
+    KV in FP8; the pages give no scale layout, read here as one fp32 scale
+    per row).  scale = amax/448 over the row (1 for an all-zero row), both
+    in IEEE float32; bytes = E4M3 of clamp(x/scale, -448, 448) in float32,
+    rounded to nearest even (torch's float8_e4m3fn cast is that rounding).
+    Returns bytes [rows][dim] u8 and scales [rows] f32."""
+    import torch
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    assert np.isfinite(x).all(), "non-finite inputs are unsupported"
+    amax = np.abs(x).max(axis=1)
+    sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = np.clip(x / sc[:, None], np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    b = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(b), sc
+
+
+def e4m3_decode(b) -> np.ndarray:
+    """E4M3 bytes to their values (float64) through the oracle's own table."""
+    table = np.array([e4m3_value(v & 0x7F) * (-1.0 if v & 0x80 else 1.0) for v in range(256)])
+    return table[np.asarray(b, dtype=np.uint8)]
+
+
+def sparse_attn_fp8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, idx: np.ndarray,
+                    wrows: np.ndarray, swa_scale: float, sm_scale: float, dv: int):
+    """Sparse attention over an FP8 main cache, as the plain definition in
+    float64: the selected rows (entries < 0 skipped) decoded as
+    e4m3(byte) * scale[row], the window rows as e4m3(byte) * swa_scale, one
+    softmax over their concatenation ([P4 "Share the cache and the search
+    work"]), values = the first dv channels.  Returns out [H][dv], lse [H]."""
+    q = np.asarray(q, dtype=np.float64)
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[sel >= 0]
+    rows = e4m3_decode(codes[sel]) * np.asarray(scales, np.float64)[sel][:, None]
+    if len(wrows):
+        rows = np.concatenate([rows, e4m3_decode(wrows) * float(swa_scale)])
+    H = q.shape[0]
+    if len(rows) == 0:
+        return np.zeros((H, dv)), np.full(H, -np.inf)
+    logits = (q @ rows.T) * float(sm_scale)
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ rows[:, :dv]) / l, (m + np.log(l))[:, 0]
+
+
 def rope_rotate(x, cos_sin, rope_dim: int) -> np.ndarray:
     """Rotary pairs of the last rope_dim channels ([P1 §04]: the FP4
     quantisation is applied after RoPE; the pages give no rotary parameters,

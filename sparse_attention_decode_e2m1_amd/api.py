@@ -30,6 +30,10 @@ class Fp4Cache(ctypes.Structure):
     _fields_ = [("codes", c_p), ("scales", c_p), ("dim", c_i32), ("cap", c_i64)]
 
 
+class Fp8Cache(ctypes.Structure):
+    _fields_ = [("codes", c_p), ("scales", c_p), ("dim", c_i32), ("cap", c_i64)]
+
+
 class LayerArgs(ctypes.Structure):
     _fields_ = [
         ("B", c_i32), ("T", c_i32), ("H", c_i32), ("D", c_i32), ("dv", c_i32),
@@ -67,6 +71,10 @@ def lib():
             "csa2_quantize_kv": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p, c_p]),
             "csa2_rope_quantize_kv": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i64, c_i32, c_p, c_p,
                                               c_p, c_p, c_p]),
+            "csa2_quantize_kv_fp8": (c_i32, [c_p, c_i32, c_i64, c_i32, c_i64, c_p, c_p, c_p, c_p]),
+            "csa2_sparse_attn_fp8": (c_i32, [c_p, c_i32, c_i32, c_i32, ctypes.POINTER(Fp8Cache),
+                                             c_p, c_i32, c_p, c_p, c_p, c_i32, c_i32, c_p, c_f32,
+                                             c_i32, c_p, c_p, c_p, c_sz, c_p]),
             "csa2_index_score": (c_i32, [ctypes.POINTER(Fp4Cache), c_i32, c_i32, c_p, c_p, c_i32,
                                          c_p, c_p, c_i32, c_i64, c_p, c_p]),
             "csa2_topk_workspace_bytes": (c_sz, [c_i32, c_i64, c_i32]),
@@ -205,6 +213,34 @@ def sparse_attn(q: torch.Tensor, B: int, T: int, kv: Fp4Cache, idx: Optional[tor
                                   _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), S, W, _ptr(q_pos),
                                   float(sm_scale), dv, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def fp8_cache(codes: torch.Tensor, scales: torch.Tensor, dim: int, cap: int) -> Fp8Cache:
+    """Descriptor of an FP8 main cache: codes [B][cap][dim] u8, scales [B][cap]
+    f32; like cache(), it keeps its tensors alive."""
+    c = Fp8Cache(_ptr(codes), _ptr(scales), dim, cap)
+    c._keep = (codes, scales)
+    return c
+
+
+def quantize_kv_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                    dst_rows: Optional[torch.Tensor] = None, stream=None):
+    dt = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    rows, dim = x.shape
+    _check(lib().csa2_quantize_kv_fp8(_ptr(x), dt, rows, dim, x.stride(0), _ptr(dst_rows),
+                                      _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def sparse_attn_fp8(q: torch.Tensor, B: int, T: int, kv: Fp8Cache, idx: Optional[torch.Tensor],
+                    K: int, swa: Optional[torch.Tensor], swa_scale: Optional[torch.Tensor],
+                    swa_pos0: Optional[torch.Tensor], S: int, W: int, q_pos: torch.Tensor,
+                    sm_scale: float, dv: int, out: torch.Tensor, lse: Optional[torch.Tensor],
+                    ws: torch.Tensor, stream=None):
+    H = q.shape[-2]
+    _check(lib().csa2_sparse_attn_fp8(_ptr(_bf16_bits(q)), B, T, H, ctypes.byref(kv), _ptr(idx), K,
+                                      _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), S, W,
+                                      _ptr(q_pos), float(sm_scale), dv, _ptr(out), _ptr(lse),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def layer_args(**kw) -> LayerArgs:

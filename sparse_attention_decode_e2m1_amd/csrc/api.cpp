@@ -409,6 +409,60 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
   return CSA2_OK;
 }
 
+csa2_status csa2_quantize_kv_fp8(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,
+                                 int64_t x_row_stride, const int64_t* dst_rows, uint8_t* codes,
+                                 float* scales, void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(dtype == CSA2_F32 || dtype == CSA2_BF16, CSA2_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  CSA2_REQUIRE(rows >= 0, CSA2_ERR_SHAPE, "rows < 0");
+  CSA2_REQUIRE(dim > 0 && dim % 16 == 0 && dim <= 4096, CSA2_ERR_SHAPE,
+               "dim must be a positive multiple of 16 <= 4096 (got %d)", dim);
+  CSA2_REQUIRE(x_row_stride >= dim, CSA2_ERR_SHAPE, "row stride %lld < dim %d",
+               (long long)x_row_stride, dim);
+  if (rows == 0) return CSA2_OK;
+  CSA2_REQUIRE(x && codes && scales, CSA2_ERR_NULL, "x, codes and scales are required");
+  CSA2_LAUNCH(0, PROF_STREAM, launch_quantize_fp8(x, dtype == CSA2_BF16, rows, dim, x_row_stride,
+                                                  dst_rows, codes, scales, as_stream(stream)),
+              "fp8 quantize launch");
+  return CSA2_OK;
+}
+
+csa2_status csa2_sparse_attn_fp8(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                                 const csa2_fp8_cache* kv, const int32_t* idx, int32_t K,
+                                 const uint8_t* swa, const float* swa_scale,
+                                 const int32_t* swa_pos0, int32_t S, int32_t W,
+                                 const int32_t* q_pos, float sm_scale, int32_t dv, float* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(kv, CSA2_ERR_NULL, "kv cache descriptor is NULL");
+  // the shared checks see the FP8 planes through an FP4 descriptor of the same shape
+  const csa2_fp4_cache shape{kv->codes, reinterpret_cast<uint8_t*>(kv->scales), kv->dim, kv->cap};
+  csa2_status s = check_attn(q, B, T, H, &shape, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, dv, out);
+  if (s) return s;
+  const int32_t rows = B * T;
+  const int32_t Weff = (S > 0) ? W : 0;
+  const size_t need = csa2_sparse_attn_workspace_bytes(rows, K, Weff, dv);
+  CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
+               need, ws_bytes);
+  const int32_t rc = std::min(rows, kRowChunk);
+  Carve c(ws);
+  AttnWs aw;
+  carve_ctl(c, rc, nullptr);
+  carve_attn(c, rc, K, Weff, dv, &aw);
+  const int32_t D = kv->dim;
+  for (int32_t r0 = 0; r0 < rows; r0 += rc) {
+    const int32_t nr = std::min(rc, rows - r0);
+    CSA2_LAUNCH(3, PROF_STREAM,
+                launch_sparse_attn(q + (size_t)r0 * H * D, nr, T, D, dv, kv->codes, nullptr,
+                                   kv->cap, idx ? idx + (size_t)r0 * K : nullptr, K, swa,
+                                   swa_scale, swa_pos0, S, Weff, q_pos + r0, sm_scale,
+                                   out + (size_t)r0 * H * dv, lse ? lse + (size_t)r0 * H : nullptr,
+                                   aw, as_stream(stream), r0, kv->scales),
+                "fp8 sparse attention launch");
+  }
+  return CSA2_OK;
+}
+
 // ------------------------------------------------------------ layer step
 namespace {
 

@@ -85,6 +85,11 @@ LaunchTiming& launch_timing();
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
                            const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
+// FP8 main-cache rows: per row, scale = amax/448 (1 for an all-zero row) and
+// byte = E4M3(clamp(x / scale, +-448)), round to nearest even.
+hipError_t launch_quantize_fp8(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
+                               const int64_t* dst_rows, uint8_t* codes, float* scales,
+                               hipStream_t st);
 hipError_t launch_rope_quantize(const void* x, bool bf16, int64_t rows, int32_t dim,
                                 int64_t stride, int32_t rope_dim, const float* cos_sin,
                                 const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
@@ -107,7 +112,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_
                               const int32_t* idx, int32_t K, const uint8_t* swa,
                               const float* swa_scale, const int32_t* swa_pos0, int32_t S,
                               int32_t W, const int32_t* q_pos, float sm_scale, float* out,
-                              float* lse, const AttnWs& w, hipStream_t st, int32_t row0 = 0);
+                              float* lse, const AttnWs& w, hipStream_t st, int32_t row0 = 0,
+                              const float* row_scale = nullptr);
 size_t attn_lds_bytes(int32_t dv);
 // out[r][s] = scores[r][pool[r][s]] for s < count[r], and the histogram of
 // those scores into hist (row stride hist_stride).

@@ -111,6 +111,56 @@ __global__ __launch_bounds__(256) void quantize_kernel(const In* __restrict__ x,
                      scales + dr * nb + blk);
 }
 
+// FP8 main-cache rows (the E4M3 variant of the global KV, with one fp32
+// scale per row): one wave per row.  scale = amax / 448 (1 for an all-zero
+// row), byte = E4M3(clamp(x / scale, -448, 448)) rounded to nearest even by
+// the hardware conversion; the divisions are IEEE fp32.
+template <typename In>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const In* __restrict__ x, int64_t rows,
+                                                           int32_t dim, int64_t stride,
+                                                           const int64_t* __restrict__ dst_rows,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // uniform per wave
+  const In* src = x + r * stride;
+  float amax = 0.0f;
+  for (int c = lane; c < dim; c += 64) amax = fmaxf(amax, fabsf(load_elem<In>(src + c)));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+  const float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+  const int64_t dr = dst_rows ? dst_rows[r] : r;
+  uint8_t* dst = codes + dr * dim;
+  // four channels per lane and step: lane l takes channels 4*(l + 64*k) ..
+  for (int c = 4 * lane; c < dim; c += 256) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float y = load_elem<In>(src + c + j) / sc;
+      v[j] = fminf(fmaxf(y, -448.0f), 448.0f);
+    }
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+    *reinterpret_cast<uint32_t*>(dst + c) = (uint32_t)word;
+  }
+  if (lane == 0) scales[dr] = sc;
+}
+
+hipError_t launch_quantize_fp8(const void* x, bool bf16, int64_t rows, int32_t dim, int64_t stride,
+                               const int64_t* dst_rows, uint8_t* codes, float* scales,
+                               hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (bf16)
+    CSA2_KERNEL(true, true, quantize_fp8_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)x,
+                rows, dim, stride, dst_rows, codes, scales);
+  else
+    CSA2_KERNEL(true, true, quantize_fp8_kernel<float>, grid, block, 0, st, (const float*)x, rows,
+                dim, stride, dst_rows, codes, scales);
+  return hipGetLastError();
+}
+
 // Rotary embedding fused with the quantize-on-write (the quantisation is
 // applied after RoPE).  The last rope_dim channels of a row form pairs
 // (2i, 2i+1) of that region, rotated by the row's angle for pair i:

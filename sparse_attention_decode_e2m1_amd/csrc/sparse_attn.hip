@@ -91,15 +91,22 @@ struct AttnArgs {
   float sm_scale;
   float* part;
   int32_t nsg, nsplit, rounds, row0;
+  // FP8 main cache: codes holds D E4M3 bytes per row and row_scale one fp32
+  // scale per row (null for the FP4 cache)
+  const float* row_scale;
 };
 
 // One split of one query row.  WIN: the split holds window entries (raw
-// E4M3 rows); MULTI: the split runs several rounds of 64 entries.  Each
-// instantiation is straight-line code from the index load to the row loads,
-// so the row loads issue as soon as the index arrives.
-template <int D, int DV, bool WIN, bool MULTI>
+// E4M3 rows); MULTI: the split runs several rounds of 64 entries; KV8: the
+// main cache holds E4M3 rows with one fp32 scale each (the per-entry scale
+// multiplies the logit, and P.V uses p * s_j / s_max with s_max, the split's
+// largest scale, applied to the partial output).  Each instantiation is
+// straight-line code from the index load to the row loads, so the row loads
+// issue as soon as the index arrives.
+template <int D, int DV, bool WIN, bool MULTI, bool KV8>
 __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _Float16* Vs,
-                                           float* Lg) {
+                                           float* Lg, float* Sg) {
+  static_assert(!(KV8 && MULTI), "FP8 main-cache splits take one round");
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
   constexpr int VST = vs_stride<DV>();
@@ -141,8 +148,23 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   }
   uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
   bool valid;
+  float sj = 0.0f;  // KV8: this lane's entry scale (0 for no entry)
   auto load_row = [&](int e) {
-    if constexpr (!WIN) {
+    if constexpr (!WIN && KV8) {
+      valid = e < a.K && ix >= 0 && ix < a.cap;
+      const int64_t row = (int64_t)b * a.cap + (valid ? ix : 0);
+      const uint8_t* wr = a.codes + row * D;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wr + 64 * m + 16 * g);
+        w0[m] = v.x;
+        w1[m] = v.y;
+        w2[m] = v.z;
+        w3[m] = v.w;
+      }
+      const float sv = a.row_scale[row];
+      sj = valid ? sv : 0.0f;
+    } else if constexpr (!WIN) {
       valid = e < a.K && ix >= 0 && ix < a.cap;
       const int64_t row = (int64_t)b * a.cap + (valid ? ix : 0);
       const uint8_t* cr = a.codes + row * (D / 2);
@@ -207,6 +229,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   // running softmax state of head i (every lane of the block holds its
   // head's), and this wave's P.V tiles
   float mrun = -INFINITY, lrun = 0.0f;
+  float smax = 1.0f;  // KV8: the split's largest entry scale (one round)
   f32x4 o[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -226,7 +249,20 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         f16x8 k0, k1;
-        if constexpr (!WIN) {
+        if constexpr (!WIN && KV8) {
+          // E4M3 -> fp16 is exact; two bytes per conversion
+          const uint32_t wv[4] = {w0[m], w1[m], w2[m], w3[m]};
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[q4], 1.0f, false);
+            const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wv[q4], 1.0f, true);
+            f16x8& k = (q4 < 2) ? k0 : k1;
+            k[4 * (q4 & 1)] = lo[0];
+            k[4 * (q4 & 1) + 1] = lo[1];
+            k[4 * (q4 & 1) + 2] = hi[0];
+            k[4 * (q4 & 1) + 3] = hi[1];
+          }
+        } else if constexpr (!WIN) {
           const f16x2 s2 = scale_pair(sc[m]);
           k0 = fp4x8_to_f16(w0[m], s2);
           k1 = fp4x8_to_f16(w1[m], s2);
@@ -250,10 +286,16 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     // one barrier, lane (i, g) reads head i's logits at its P.V operand slots
     // (entries 32ks + 8g + [0, 8)), and the four lanes of head i agree on its
     // maximum and sum with lane exchanges.  Every wave thus builds P itself.
+    const float escale = (!WIN && KV8) ? lscale * sj : lscale;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
       Lg[(4 * g + rr) * kLgStride + wave * 16 + i] =
-          valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * lscale : -INFINITY;
+          valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * escale : -INFINITY;
+    if constexpr (!WIN && KV8) {
+      if (g == 0) Sg[wave * 16 + i] = sj;
+      const float wm = row16_max(sj);
+      if (lane == 0) Sg[64 + wave] = wm;
+    }
     __syncthreads();  // every wave's logits and value rows are in LDS
     float lv[2][8];
 #pragma unroll
@@ -274,13 +316,25 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     const float alpha = (mnew == -INFINITY) ? 1.0f : __expf(mrun - mnew);
     f16x8 pa[2];
     float ps = 0.0f;  // the sum uses the unrounded probabilities
+    float ew[2][8];   // KV8: s_j / s_max of the lane's entries
+    if constexpr (!WIN && KV8) {
+      smax = fmaxf(fmaxf(Sg[64], Sg[65]), fmaxf(Sg[66], Sg[67]));
+      const float inv = (smax > 0.0f) ? 1.0f / smax : 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ew[ks][j] = Sg[32 * ks + 8 * g + j] * inv;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lv[ks][j] - mnew);
         ps += pr;
-        pa[ks][j] = (_Float16)pr;
+        if constexpr (!WIN && KV8)
+          pa[ks][j] = (_Float16)(pr * ew[ks][j]);
+        else
+          pa[ks][j] = (_Float16)pr;
       }
     ps += shfl_xor(ps, 16);
     ps += shfl_xor(ps, 32);
@@ -304,14 +358,15 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   }
 
   // ---- partial result of this split: o[16][DV], m[16], l[16]
+  const float oscale = (!WIN && KV8) ? smax : wscale;
   float* pb = a.part + ((int64_t)r * a.nsplit + sidx) * PSTRIDE;
   static_assert(NT % 2 == 0, "tiles stored in pairs");
 #pragma unroll
   for (int nt = 0; nt < NT; nt += 2)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      st_pair(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * wscale,
-              o[nt + 1][rr] * wscale);
+      st_pair(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * oscale,
+              o[nt + 1][rr] * oscale);
   // running max and sum of head i, written by lanes g == 0 of wave 0
   if (wave == 0 && g == 0) {
     pb[16 * DV + i] = mrun;
@@ -321,17 +376,18 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
 
 // Block (s, r): split s of query row r (global entries for s < nsg, window
 // entries after).
-template <int D, int DV, bool MULTI>
+template <int D, int DV, bool MULTI, bool KV8>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
   // 16-byte aligned: the V tile is written and read with 16- and 8-byte LDS
   // accesses, so its base must not follow the static arrays unaligned
   extern __shared__ __attribute__((aligned(16))) _Float16 Vs[];  // [64 entries][vs_stride]
   __shared__ __attribute__((aligned(16))) float Lg[16 * kLgStride];  // [head][entry of the round]
+  __shared__ float Sg[64 + 4];  // KV8: entry scales of the round, then each wave's largest
   const int r = blockIdx.y, sidx = blockIdx.x;
   if (sidx >= a.nsg)
-    split_body<D, DV, true, MULTI>(a, r, sidx, Vs, Lg);
+    split_body<D, DV, true, MULTI, false>(a, r, sidx, Vs, Lg, Sg);
   else
-    split_body<D, DV, false, MULTI>(a, r, sidx, Vs, Lg);
+    split_body<D, DV, false, MULTI, KV8>(a, r, sidx, Vs, Lg, Sg);
 }
 
 // Merge kernel.  Unit u of row r is the value-slot pair (2(u % (dv/2)), +1)
@@ -429,36 +485,44 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
                               const uint8_t* swa, const float* swa_scale,
                               const int32_t* swa_pos0, int32_t S, int32_t W,
                               const int32_t* q_pos, float sm_scale, float* out, float* lse,
-                              const AttnWs& w, hipStream_t st, int32_t row0) {
+                              const AttnWs& w, hipStream_t st, int32_t row0,
+                              const float* row_scale) {
   const size_t lds = attn_lds_bytes(DV);
   static bool lds_raised = false;
   if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, DV, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    for (const void* k : {(const void*)sparse_attn_kernel<D, DV, false, false>,
+                          (const void*)sparse_attn_kernel<D, DV, true, false>,
+                          (const void*)sparse_attn_kernel<D, DV, false, true>}) {
+      hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
     lds_raised = true;
   }
   // An empty window array contributes no entries (its pointers may be null).
   if (S == 0) W = 0;
   // One round (64 entries) per split unless the grid would be many times the
-  // device: then splits of several rounds keep the partials few.
-  const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true>, lds);
+  // device: then splits of several rounds keep the partials few (FP4 main
+  // cache only; the FP8 variant always takes one round).
+  const bool kv8 = row_scale != nullptr;
+  const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true, false>, lds);
   int32_t rounds = 1;
   AttnSplit sp = attn_split(K, W, rounds);
-  while ((int64_t)sp.nsplit * rows > 8 * cap_blocks && sp.nsplit > 2 && rounds < 64) {
+  while (!kv8 && (int64_t)sp.nsplit * rows > 8 * cap_blocks && sp.nsplit > 2 && rounds < 64) {
     rounds *= 2;
     sp = attn_split(K, W, rounds);
   }
   const AttnArgs args{q, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos,
-                      sm_scale, w.part, sp.nsg, sp.nsplit, rounds, row0};
+                      sm_scale, w.part, sp.nsg, sp.nsplit, rounds, row0, row_scale};
   const dim3 grid((unsigned)sp.nsplit, (unsigned)rows);
-  if (rounds > 1)
-    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, true>), grid, dim3(256), lds, st, args);
+  if (kv8)
+    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false, true>), grid, dim3(256), lds, st,
+                args);
+  else if (rounds > 1)
+    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, true, false>), grid, dim3(256), lds, st,
+                args);
   else
-    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false>), grid, dim3(256), lds, st, args);
+    CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false, false>), grid, dim3(256), lds, st,
+                args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // four threads per output unit; each pass takes 4 KB splits
@@ -481,13 +545,14 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_
                               const int32_t* idx, int32_t K, const uint8_t* swa,
                               const float* swa_scale, const int32_t* swa_pos0, int32_t S,
                               int32_t W, const int32_t* q_pos, float sm_scale, float* out,
-                              float* lse, const AttnWs& w, hipStream_t st, int32_t row0) {
+                              float* lse, const AttnWs& w, hipStream_t st, int32_t row0,
+                              const float* row_scale) {
   if (D == 576 && dv == 512)
     return launch_attn<576, 512>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
-                                 S, W, q_pos, sm_scale, out, lse, w, st, row0);
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale);
   if (D == 128 && dv == 128)
     return launch_attn<128, 128>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
-                                 S, W, q_pos, sm_scale, out, lse, w, st, row0);
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale);
   return hipErrorInvalidValue;
 }
 

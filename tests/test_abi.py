@@ -104,6 +104,29 @@ def test_sparse_attn_rejects(L):
     assert f(*args(ws=None)) == 4
 
 
+def test_fp8_entry_points_reject(L):
+    q = L.csa2_quantize_kv_fp8
+    assert q(FAKE, 7, 4, 576, 576, None, FAKE, FAKE, None) == 3    # dtype
+    assert q(FAKE, 0, 4, 570, 576, None, FAKE, FAKE, None) == 2    # dim % 16
+    assert q(FAKE, 0, 4, 576, 500, None, FAKE, FAKE, None) == 2    # stride < dim
+    assert q(FAKE, 0, 4, 576, 576, None, FAKE, None, None) == 1    # scales missing
+    assert q(None, 0, 0, 576, 576, None, None, None, None) == 0    # nothing to do
+    kv = api.Fp8Cache(FAKE, FAKE, 576, 100)
+    f = L.csa2_sparse_attn_fp8
+    need = L.csa2_sparse_attn_workspace_bytes(1, 64, 128, 512)
+    args = lambda H=16, dv=512, K=64, ws=FAKE, nb=need, c=ctypes.byref(kv): (
+        FAKE, 1, 1, H, c, FAKE, K, FAKE, FAKE, FAKE, 128, 128, FAKE,
+        ctypes.c_float(0.04), dv, FAKE, None, ws, nb, None)
+    assert f(*args(c=None)) == 1
+    assert f(*args(H=8)) == 5
+    assert f(*args(dv=256)) == 5
+    assert f(*args(K=-1)) == 2
+    assert f(*args(nb=need - 1)) == 4
+    assert f(*args(ws=None)) == 4
+    kv.scales = None
+    assert f(*args()) == 1
+
+
 def test_layer_step_rejects(L):
     assert L.csa2_layer_step(0, None, FAKE, 1 << 20, None) == 1
     a = api.LayerArgs(B=1, T=1, H=16, D=576, dv=512, H_I=4, D_I=128, K=64, S=128, W=128)

@@ -318,6 +318,66 @@ def test_sparse_attn_parity(K, W, npad):
         assert np.allclose(gl[t], l, atol=1e-4, rtol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_fp8_bit_exact(dtype):
+    """FP8 variant of the main cache: bytes and per-row scales equal the
+    oracle's (scattered destination rows, rows of very different sizes, an
+    all-zero row)."""
+    rng = np.random.default_rng(17)
+    n = 2000
+    x = (rng.standard_normal((n, 576)) * 10.0 ** rng.uniform(-6, 4, (n, 1))).astype(np.float32)
+    x[5] = 0.0
+    x[9, 100] = 1e30
+    xt = torch.from_numpy(x)
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+        x = xt.float().numpy()
+    dst = torch.from_numpy(rng.permutation(3 * n)[:n].astype(np.int64))
+    codes = torch.zeros((3 * n, 576), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((3 * n,), dtype=torch.float32, device="cuda")
+    api.quantize_kv_fp8(xt.cuda(), codes, scales, dst_rows=dst.cuda())
+    torch.cuda.synchronize()
+    ob, os_ = oracle.quantize_fp8(x)
+    d = dst.numpy()
+    assert np.array_equal(host(scales)[d].view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(host(codes)[d], ob)
+
+
+@pytest.mark.parametrize("K,W,npad", [(2048, 128, 0), (2048, 128, 37), (256, 0, 5), (100, 128, 0)])
+def test_sparse_attn_fp8_parity(K, W, npad):
+    """Attention over an FP8 main cache against the oracle's float64
+    definition, at the FP4 attention's tolerance."""
+    N, T = 6000, 3
+    rng = np.random.default_rng(K + 3 * W + npad)
+    kv = (rng.standard_normal((N, 576)) * rng.uniform(0.5, 1.5, (N, 1))).astype(np.float32)
+    b8, s8 = oracle.quantize_fp8(kv)
+    swa_b, swa_s = I.fp8_rows(torch.from_numpy(rng.standard_normal((128, 576)).astype(np.float32)))
+    swa = swa_b.numpy()
+    idx = np.full((T, K), -1, np.int32)
+    for t in range(T):
+        sel = np.sort(rng.choice(N, K - npad, replace=False))
+        idx[t, : len(sel)] = sel
+    q = torch.randn(T, 16, 576, generator=torch.Generator().manual_seed(K + W + 1)).to(torch.bfloat16)
+    q_pos = np.array([N - 1, N - 50, N - 200], np.int32)
+    S, pos0 = 128, N - 128
+    sm = float(np.float32(1.0 / np.sqrt(576)))
+    out = torch.full((T, 16, 512), np.nan, device="cuda")
+    lse = torch.full((T, 16), np.nan, device="cuda")
+    ws = api.workspace(api.sparse_attn_workspace_bytes(T, K, W, 512))
+    kv8 = api.fp8_cache(dev(b8), dev(s8), 576, N)
+    api.sparse_attn_fp8(q.cuda(), 1, T, kv8, dev(idx), K, dev(swa[None]),
+                        dev(np.array([swa_s], np.float32)), dev(np.array([pos0], np.int32)), S, W,
+                        dev(q_pos), sm, 512, out, lse, ws)
+    torch.cuda.synchronize()
+    assert ctl_words_zero(ws, T)
+    go, gl = host(out), host(lse)
+    for t in range(T):
+        wrows = oracle.window_rows(swa, pos0, int(q_pos[t]), W)
+        o, l = oracle.sparse_attn_fp8(q[t].float().numpy(), b8, s8, idx[t], wrows, swa_s, sm, 512)
+        assert_attention_close(go[t], o, what=(K, W, t))
+        assert np.allclose(gl[t], l, atol=1e-4, rtol=1e-5)
+
+
 def test_sparse_attn_no_entries():
     N = 100
     codes, scales, swa, swa_s = _attn_case(1, N)

@@ -289,3 +289,55 @@ def test_rope_angle_table():
     a = 12345.0 * 10000.0 ** (-62.0 / 64.0)
     assert math.isclose(cs[2, 31, 0], math.cos(a), abs_tol=1e-7)
     assert math.isclose(cs[1, 31, 1], math.sin(10000.0 ** (-62.0 / 64.0)), rel_tol=1e-6)
+
+
+# ------------------------------------------------------------ FP8 variant
+def test_fp8_rounding_primitive_matches_e4m3_table(oracle):
+    """The rounding primitive of quantize_fp8 (torch's E4M3 cast) agrees with
+    the oracle's own E4M3 table on every finite byte, and rounds each
+    midpoint between neighbours to the even byte."""
+    vals = np.array([oracle.e4m3_value(b) for b in range(127)], np.float64)
+    t = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert list(t) == list(range(127))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[:-1] + vals[1:]) / 2)  # exact in fp32
+    r = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(int)
+    lo = np.arange(126)
+    assert np.array_equal(r, np.where(lo % 2 == 0, lo, lo + 1))
+
+
+def test_fp8_rows(oracle):
+    """Each row's largest magnitude maps to 448 (byte 0x7E or 0xFE); an
+    all-zero row has scale 1 and zero bytes; the decoded row is within half
+    an E4M3 step (2^-4 relative, or the subnormal step) of the input."""
+    rng = np.random.default_rng(40)
+    x = (rng.standard_normal((50, 576)) * 10.0 ** rng.uniform(-3, 3, (50, 1))).astype(np.float32)
+    x[7] = 0.0
+    b, s = oracle.quantize_fp8(x)
+    assert s[7] == 1.0 and (b[7] == 0).all()
+    dec = oracle.e4m3_decode(b) * s[:, None].astype(np.float64)
+    for r in range(50):
+        if r == 7:
+            continue
+        j = int(np.abs(x[r]).argmax())
+        assert (b[r, j] & 0x7F) == 0x7E
+        err = np.abs(dec[r] - x[r].astype(np.float64))
+        bound = np.maximum(np.abs(x[r]) * 2.0 ** -4, 2.0 ** -10 * float(s[r])) * (1 + 1e-6)
+        assert (err <= bound).all(), r
+
+
+def test_fp8_attention_closed_forms(oracle):
+    """One selected row and no window: the output is that row's decoded
+    values; two copies of a row: the same output (equal logits average equal
+    values); lse of one entry is its logit."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((10, 576)).astype(np.float32)
+    b, s = oracle.quantize_fp8(x)
+    q = rng.standard_normal((16, 576)).astype(np.float32)
+    none = np.zeros((0, 576), np.uint8)
+    o1, l1 = oracle.sparse_attn_fp8(q, b, s, np.array([3]), none, 1.0, 0.05, 512)
+    row = oracle.e4m3_decode(b[3]) * float(s[3])
+    assert np.allclose(o1, np.broadcast_to(row[:512], (16, 512)), rtol=0, atol=1e-12)
+    assert np.allclose(l1, 0.05 * (q.astype(np.float64) @ row), rtol=1e-12)
+    o2, _ = oracle.sparse_attn_fp8(q, b, s, np.array([3, -1, 3]), none, 1.0, 0.05, 512)
+    assert np.allclose(o2, o1, rtol=0, atol=1e-12)
