@@ -186,6 +186,9 @@ def main():
     ap.add_argument("--rope-quantize-rows", type=int, default=0,
                     help="only time the fused rotary + quantize-on-write of this many bf16 rows "
                          "(576 channels, 64 rotary) against the plain quantize-on-write, and exit")
+    ap.add_argument("--reuse-one-launch", action="store_true",
+                    help="run the Reuse (and window-only) layers through the one-launch "
+                         "attention (split and merge in one kernel) instead of split + merge")
     ap.add_argument("--attn-kv-compare", action="store_true",
                     help="only time the sparse attention of the workload's decode queries over "
                          "an FP4 and an FP8 main cache (same Top-K, window), and exit")
@@ -231,7 +234,7 @@ def main():
     print(f"[bench] workload {w.name}: B={w.B} N={w.N} T={w.T} K={w.K} modes={w.modes}; "
           f"set-up with {args.copies} cache copies", file=sys.stderr, flush=True)
     t_set = time.perf_counter()
-    dw = harness.DeviceWorkload(w, copies=args.copies)
+    dw = harness.DeviceWorkload(w, copies=args.copies, reuse_one_launch=args.reuse_one_launch)
     print(f"[bench] set-up {time.perf_counter() - t_set:.1f} s", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
@@ -300,7 +303,9 @@ def main():
                    "pool": w.P, "window": w.W, "heads": w.H, "latent": w.D, "index_heads": w.HI,
                    "index_dim": w.DI, "kv_bytes_per_query": kvb["total"],
                    "kv_GBps": round(kv_gbps, 1), "kv_frac_of_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
-                   "cache_copies": args.copies, "storage": "fp4 e2m1 + e4m3/16 (kv, index), fp8 e4m3 window",
+                   "cache_copies": args.copies,
+                   "reuse_attention": "one launch" if args.reuse_one_launch else "split + merge",
+                   "storage": "fp4 e2m1 + e4m3/16 (kv, index), fp8 e4m3 window",
                    "compute": "fp16 MFMA operands, fp32 accumulation"},
         "roofline": roofline,
         "cpu_baseline": cpu,

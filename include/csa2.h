@@ -234,6 +234,25 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
                              int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* The same attention in one launch (a Reuse layer's whole decode step):
+ * each block computes its split, publishes the partial with device-coherent
+ * stores and waits until all splits of its query row have arrived, then
+ * merges a slice of the row's output.  Used when every block of the grid
+ * fits on the device at once (rows x splits within the occupancy limit, one
+ * round of 64 entries per split); otherwise the split and merge kernels of
+ * csa2_sparse_attn run.  Arguments, workspace and results are those of
+ * csa2_sparse_attn, bit for bit.  The wait is bounded: if it runs out (the
+ * grid did not become resident, e.g. with other work occupying the device),
+ * a control word stays nonzero and the output is not written.  Callers that
+ * run other kernels concurrently on the device should use csa2_sparse_attn. */
+csa2_status csa2_sparse_attn_one_launch(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                                        const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                                        const uint8_t* swa, const float* swa_scale,
+                                        const int32_t* swa_pos0, int32_t S, int32_t W,
+                                        const int32_t* q_pos, float sm_scale, int32_t dv,
+                                        float* out, float* lse, void* ws, size_t ws_bytes,
+                                        void* stream);
+
 /* The same attention over an FP8 main cache (csa2_fp8_cache; the V4-Flash
  * style global KV of [P1 §04], E4M3 with one fp32 scale per row): a selected
  * row's key and value are e4m3(byte) * scale[row].  The window and every

@@ -83,6 +83,10 @@ def lib():
             "csa2_sparse_attn": (c_i32, [c_p, c_i32, c_i32, c_i32, ctypes.POINTER(Fp4Cache), c_p,
                                          c_i32, c_p, c_p, c_p, c_i32, c_i32, c_p, c_f32, c_i32,
                                          c_p, c_p, c_p, c_sz, c_p]),
+            "csa2_sparse_attn_one_launch": (c_i32, [c_p, c_i32, c_i32, c_i32,
+                                                    ctypes.POINTER(Fp4Cache), c_p, c_i32, c_p,
+                                                    c_p, c_p, c_i32, c_i32, c_p, c_f32, c_i32,
+                                                    c_p, c_p, c_p, c_sz, c_p]),
             "csa2_workspace_bytes": (c_sz, [c_i32, ctypes.POINTER(LayerArgs)]),
             "csa2_layer_step": (c_i32, [c_i32, ctypes.POINTER(LayerArgs), c_p, c_sz, c_p]),
             "csa2_fp4_bytes_per_token": (c_i64, [c_i32]),
@@ -213,6 +217,20 @@ def sparse_attn(q: torch.Tensor, B: int, T: int, kv: Fp4Cache, idx: Optional[tor
                                   _ptr(swa), _ptr(swa_scale), _ptr(swa_pos0), S, W, _ptr(q_pos),
                                   float(sm_scale), dv, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def sparse_attn_one_launch(q: torch.Tensor, B: int, T: int, kv: Fp4Cache,
+                           idx: Optional[torch.Tensor], K: int, swa: Optional[torch.Tensor],
+                           swa_scale: Optional[torch.Tensor], swa_pos0: Optional[torch.Tensor],
+                           S: int, W: int, q_pos: torch.Tensor, sm_scale: float, dv: int,
+                           out: torch.Tensor, lse: Optional[torch.Tensor], ws: torch.Tensor,
+                           stream=None):
+    H = q.shape[-2]
+    _check(lib().csa2_sparse_attn_one_launch(_ptr(_bf16_bits(q)), B, T, H, ctypes.byref(kv),
+                                             _ptr(idx), K, _ptr(swa), _ptr(swa_scale),
+                                             _ptr(swa_pos0), S, W, _ptr(q_pos), float(sm_scale),
+                                             dv, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                             _stream(stream)))
 
 
 def fp8_cache(codes: torch.Tensor, scales: torch.Tensor, dim: int, cap: int) -> Fp8Cache:

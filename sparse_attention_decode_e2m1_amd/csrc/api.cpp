@@ -376,12 +376,13 @@ static csa2_status check_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H
   return CSA2_OK;
 }
 
-csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
-                             const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
-                             const uint8_t* swa, const float* swa_scale, const int32_t* swa_pos0,
-                             int32_t S, int32_t W, const int32_t* q_pos, float sm_scale,
-                             int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
-                             void* stream) {
+static csa2_status sparse_attn_impl(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                                    const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                                    const uint8_t* swa, const float* swa_scale,
+                                    const int32_t* swa_pos0, int32_t S, int32_t W,
+                                    const int32_t* q_pos, float sm_scale, int32_t dv, float* out,
+                                    float* lse, void* ws, size_t ws_bytes, void* stream,
+                                    bool one_launch) {
   g_last_error.clear();
   csa2_status s = check_attn(q, B, T, H, kv, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, dv, out);
   if (s) return s;
@@ -403,10 +404,32 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
                                    kv->cap, idx ? idx + (size_t)r0 * K : nullptr, K, swa,
                                    swa_scale, swa_pos0, S, Weff, q_pos + r0, sm_scale,
                                    out + (size_t)r0 * H * dv, lse ? lse + (size_t)r0 * H : nullptr,
-                                   aw, as_stream(stream), r0),
+                                   aw, as_stream(stream), r0, nullptr,
+                                   one_launch ? static_cast<uint32_t*>(ws) + kAttnCtlWord : nullptr),
                 "sparse attention launch");
   }
   return CSA2_OK;
+}
+
+csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                             const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                             const uint8_t* swa, const float* swa_scale, const int32_t* swa_pos0,
+                             int32_t S, int32_t W, const int32_t* q_pos, float sm_scale,
+                             int32_t dv, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return sparse_attn_impl(q, B, T, H, kv, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale,
+                          dv, out, lse, ws, ws_bytes, stream, false);
+}
+
+csa2_status csa2_sparse_attn_one_launch(const uint16_t* q, int32_t B, int32_t T, int32_t H,
+                                        const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
+                                        const uint8_t* swa, const float* swa_scale,
+                                        const int32_t* swa_pos0, int32_t S, int32_t W,
+                                        const int32_t* q_pos, float sm_scale, int32_t dv,
+                                        float* out, float* lse, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  return sparse_attn_impl(q, B, T, H, kv, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos, sm_scale,
+                          dv, out, lse, ws, ws_bytes, stream, true);
 }
 
 csa2_status csa2_quantize_kv_fp8(const void* x, csa2_dtype dtype, int64_t rows, int32_t dim,

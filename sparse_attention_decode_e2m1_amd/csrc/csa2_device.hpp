@@ -23,6 +23,17 @@ constexpr int kHistShift = 20;
 // MI355X), so the merge of many blocks is spread over the copies.
 constexpr int kHistCopies = 8;
 
+// Device-coherent accesses for data one block writes and another block of
+// the same launch reads (agent scope: no full-cache write-back or invalidate).
+template <typename T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // --------------------------------------------------------------- FP8 / FP4
 // E4M3 byte -> f32 (gfx950 converts the OCP "FN" encoding).  `sel` picks the
 // byte of `word`.

@@ -113,7 +113,11 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_
                               const float* swa_scale, const int32_t* swa_pos0, int32_t S,
                               int32_t W, const int32_t* q_pos, float sm_scale, float* out,
                               float* lse, const AttnWs& w, hipStream_t st, int32_t row0 = 0,
-                              const float* row_scale = nullptr);
+                              const float* row_scale = nullptr,
+                              uint32_t* one_launch_ctl = nullptr);
+// Control words of the one-launch attention within a row's control block
+// (arrivals, departures, the failed-wait flag).
+constexpr int64_t kAttnCtlWord = kHistWords + 8;
 size_t attn_lds_bytes(int32_t dv);
 // out[r][s] = scores[r][pool[r][s]] for s < count[r], and the histogram of
 // those scores into hist (row stride hist_stride).

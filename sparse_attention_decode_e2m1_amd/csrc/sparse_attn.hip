@@ -102,8 +102,9 @@ struct AttnArgs {
 // multiplies the logit, and P.V uses p * s_j / s_max with s_max, the split's
 // largest scale, applied to the partial output).  Each instantiation is
 // straight-line code from the index load to the row loads, so the row loads
-// issue as soon as the index arrives.
-template <int D, int DV, bool WIN, bool MULTI, bool KV8>
+// issue as soon as the index arrives.  COH: the partial is stored with
+// device-coherent stores, for blocks of the same launch to read.
+template <int D, int DV, bool WIN, bool MULTI, bool KV8, bool COH = false>
 __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _Float16* Vs,
                                            float* Lg, float* Sg) {
   static_assert(!(KV8 && MULTI), "FP8 main-cache splits take one round");
@@ -364,13 +365,23 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
 #pragma unroll
   for (int nt = 0; nt < NT; nt += 2)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      st_pair(pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i, o[nt][rr] * oscale,
-              o[nt + 1][rr] * oscale);
+    for (int rr = 0; rr < 4; ++rr) {
+      float* dst = pb + (4 * g + rr) * DV + wave * CPW + 16 * nt + 2 * i;
+      if constexpr (COH)
+        st_coh(reinterpret_cast<uint64_t*>(dst),
+               __builtin_bit_cast(uint64_t, make_float2(o[nt][rr] * oscale, o[nt + 1][rr] * oscale)));
+      else
+        st_pair(dst, o[nt][rr] * oscale, o[nt + 1][rr] * oscale);
+    }
   // running max and sum of head i, written by lanes g == 0 of wave 0
   if (wave == 0 && g == 0) {
-    pb[16 * DV + i] = mrun;
-    pb[16 * DV + 16 + i] = lrun;
+    if constexpr (COH) {
+      st_coh(pb + 16 * DV + i, mrun);
+      st_coh(pb + 16 * DV + 16 + i, lrun);
+    } else {
+      pb[16 * DV + i] = mrun;
+      pb[16 * DV + 16 + i] = lrun;
+    }
   }
 }
 
@@ -398,16 +409,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
 // maximum and add their shares with lane moves, so the merge needs no LDS
 // and no barrier:
 //   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L.
-template <int DV, int SUB, int KB>  // KB: splits per thread per pass
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
-                                                           int32_t nsplit, float* __restrict__ out,
-                                                           float* __restrict__ lse) {
+// One pass of 256 threads merges units [vb * 256 / SUB, (vb + 1) * 256 / SUB)
+// of row r.  COH: the partials were written by blocks of the same launch.
+template <int DV, int SUB, int KB, bool COH>  // KB: splits per thread per pass
+__device__ __forceinline__ void merge_units(const float* __restrict__ part, int32_t nsplit, int r,
+                                            int vb, float* __restrict__ out,
+                                            float* __restrict__ lse) {
   static_assert(SUB == 4, "lane moves below cover groups of four lanes");
   constexpr int PSTRIDE = 16 * DV + 32;
   constexpr int UPH = DV / 2;          // units per head
-  constexpr int UPB = 256 / SUB;       // units per block
-  const int r = blockIdx.y, tid = threadIdx.x, sub = tid % SUB;
-  const int u = blockIdx.x * UPB + tid / SUB;  // the grid covers the units exactly
+  constexpr int UPB = 256 / SUB;       // units per pass
+  const int tid = threadIdx.x, sub = tid % SUB;
+  const int u = vb * UPB + tid / SUB;  // the passes cover the units exactly
   const int h = u / UPH, pp = 2 * (u % UPH);
   const float* prow = part + (int64_t)r * nsplit * PSTRIDE;
   float Mrun = -INFINITY, L = 0.0f, nx = 0.0f, ny = 0.0f;
@@ -418,9 +431,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     for (int k = 0; k < KB; ++k) {
       const int sc = min(s0 + sub + SUB * k, nsplit - 1);  // clamped: every load in bounds
       const float* ps = prow + (int64_t)sc * PSTRIDE;
-      ov[k] = ld_pair(ps + h * DV + pp);
-      mv[k] = ps[16 * DV + h];
-      lv[k] = ps[16 * DV + 16 + h];
+      if constexpr (COH) {
+        ov[k] = __builtin_bit_cast(float2, ld_coh(reinterpret_cast<const uint64_t*>(ps + h * DV + pp)));
+        mv[k] = ld_coh(ps + 16 * DV + h);
+        lv[k] = ld_coh(ps + 16 * DV + 16 + h);
+      } else {
+        ov[k] = ld_pair(ps + h * DV + pp);
+        mv[k] = ps[16 * DV + h];
+        lv[k] = ps[16 * DV + 16 + h];
+      }
     }
     float cm = -INFINITY;
 #pragma unroll
@@ -460,6 +479,67 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   }
 }
 
+template <int DV, int SUB, int KB>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
+                                                           int32_t nsplit, float* __restrict__ out,
+                                                           float* __restrict__ lse) {
+  merge_units<DV, SUB, KB, false>(part, nsplit, blockIdx.y, blockIdx.x, out, lse);
+}
+
+// Split and merge in one launch, for grids whose blocks all fit on the
+// device at once (the host checks).  Each block computes its split as the
+// split kernel does, stores the partial with device-coherent stores, counts
+// itself in its row's arrival word and waits (a bounded poll, the only wait
+// on another block) until every split of the row has arrived; it then
+// merges passes vb = split, split + nsplit, ... of the row's output with the
+// merge kernel's arithmetic and split grouping, so the result is the same
+// bit for bit.  Words of row r at ctl + r * ctl_stride: arrivals, departures,
+// and a flag set if the wait ran out; the row's last block to leave zeroes
+// the two counters.
+constexpr uint32_t kAttnSpinLimit = 1u << 20;
+
+template <int D, int DV, int KB>
+__global__ __launch_bounds__(256, 2) void sparse_attn_one_launch_kernel(AttnArgs a, uint32_t* ctl,
+                                                                        int64_t ctl_stride,
+                                                                        float* out, float* lse) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 Vs[];
+  __shared__ __attribute__((aligned(16))) float Lg[16 * kLgStride];
+  __shared__ float Sg[64 + 4];
+  __shared__ uint32_t s_ok;
+  const int r = blockIdx.y, sidx = blockIdx.x;
+  if (sidx >= a.nsg)
+    split_body<D, DV, true, false, false, true>(a, r, sidx, Vs, Lg, Sg);
+  else
+    split_body<D, DV, false, false, false, true>(a, r, sidx, Vs, Lg, Sg);
+  // arrival: every thread's partial stores have completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* c = ctl + (int64_t)r * ctl_stride;
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t it = 0;
+    bool ok;
+    while (!(ok = ld_coh(c) >= (uint32_t)a.nsplit) && ++it < kAttnSpinLimit)
+      __builtin_amdgcn_s_sleep(2);
+    if (!ok) st_coh(c + 2, 1u);  // flagged in the control words; the output is not written
+    s_ok = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_ok) {
+    constexpr int NVB = 16 * DV / 2 / 64;  // passes of 64 units per row
+    for (int vb = sidx; vb < NVB; vb += a.nsplit)
+      merge_units<DV, 4, KB, true>(a.part, a.nsplit, r, vb, out, lse);
+  }
+  // departure: the row's last block leaves the counters zero
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(c + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)a.nsplit - 1u) {
+      st_coh(c, 0u);
+      st_coh(c + 1, 0u);
+    }
+  }
+}
+
 size_t attn_lds_bytes(int32_t dv) {
   return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
 }
@@ -479,6 +559,43 @@ static int64_t resident_blocks(F kernel, size_t lds) {
   return cached;
 }
 
+// Launches the one-launch kernel if its grid fits the device at once
+// (blocks per compute unit from the occupancy query, per device); sets
+// *launched accordingly.
+template <int D, int DV, int KB>
+static hipError_t try_one_launch(const AttnArgs& args, int32_t rows, size_t lds, uint32_t* ctl,
+                                 float* out, float* lse, hipStream_t st, bool* launched) {
+  *launched = false;
+  static bool lds_raised = false;
+  if (!lds_raised) {
+    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_one_launch_kernel<D, DV, KB>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_raised = true;
+  }
+  static int64_t cap[64];
+  static bool known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
+  if (!known[dev]) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sparse_attn_one_launch_kernel<D, DV, KB>,
+                                                     256, lds) != hipSuccess) {
+      (void)hipGetLastError();
+      return hipSuccess;  // unknown capacity: the split + merge kernels run instead
+    }
+    cap[dev] = (int64_t)cus * per;
+    known[dev] = true;
+  }
+  if ((int64_t)args.nsplit * rows > cap[dev]) return hipSuccess;
+  const dim3 grid((unsigned)args.nsplit, (unsigned)rows);
+  CSA2_KERNEL(true, true, (sparse_attn_one_launch_kernel<D, DV, KB>), grid, dim3(256), lds, st,
+              args, ctl, (int64_t)kCtlWordsPerRow, out, lse);
+  *launched = true;
+  return hipGetLastError();
+}
+
 template <int D, int DV>
 static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const uint8_t* codes,
                               const uint8_t* scales, int64_t cap, const int32_t* idx, int32_t K,
@@ -486,7 +603,7 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
                               const int32_t* swa_pos0, int32_t S, int32_t W,
                               const int32_t* q_pos, float sm_scale, float* out, float* lse,
                               const AttnWs& w, hipStream_t st, int32_t row0,
-                              const float* row_scale) {
+                              const float* row_scale, uint32_t* one_launch_ctl) {
   const size_t lds = attn_lds_bytes(DV);
   static bool lds_raised = false;
   if (!lds_raised) {
@@ -513,6 +630,17 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   }
   const AttnArgs args{q, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos,
                       sm_scale, w.part, sp.nsg, sp.nsplit, rounds, row0, row_scale};
+  if (one_launch_ctl && !kv8 && rounds == 1) {
+    bool launched = false;
+    hipError_t e;
+    if (sp.nsplit <= 16)
+      e = try_one_launch<D, DV, 4>(args, rows, lds, one_launch_ctl, out, lse, st, &launched);
+    else if (sp.nsplit <= 40)
+      e = try_one_launch<D, DV, 10>(args, rows, lds, one_launch_ctl, out, lse, st, &launched);
+    else
+      e = try_one_launch<D, DV, 16>(args, rows, lds, one_launch_ctl, out, lse, st, &launched);
+    if (e != hipSuccess || launched) return e;
+  }
   const dim3 grid((unsigned)sp.nsplit, (unsigned)rows);
   if (kv8)
     CSA2_KERNEL(true, false, (sparse_attn_kernel<D, DV, false, true>), grid, dim3(256), lds, st,
@@ -546,13 +674,15 @@ hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_
                               const float* swa_scale, const int32_t* swa_pos0, int32_t S,
                               int32_t W, const int32_t* q_pos, float sm_scale, float* out,
                               float* lse, const AttnWs& w, hipStream_t st, int32_t row0,
-                              const float* row_scale) {
+                              const float* row_scale, uint32_t* one_launch_ctl) {
   if (D == 576 && dv == 512)
     return launch_attn<576, 512>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
-                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale);
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale,
+                                 one_launch_ctl);
   if (D == 128 && dv == 128)
     return launch_attn<128, 128>(q, rows, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0,
-                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale);
+                                 S, W, q_pos, sm_scale, out, lse, w, st, row0, row_scale,
+                                 one_launch_ctl);
   return hipErrorInvalidValue;
 }
 

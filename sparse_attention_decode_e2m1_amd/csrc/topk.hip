@@ -39,17 +39,6 @@ namespace csa2 {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-// Device-coherent accesses for data one block writes and another block of
-// the same launch reads (agent scope: no full-cache write-back or invalidate).
-template <typename T>
-__device__ __forceinline__ void st_coh(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_coh(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ scores,
                                                         int64_t n,
                                                         const int32_t* __restrict__ n_valid,

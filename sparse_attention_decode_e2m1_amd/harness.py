@@ -42,9 +42,14 @@ class DeviceWorkload:
     layer buffers."""
 
     def __init__(self, w: I.Workload, copies: int = 1, device: str = "cuda",
-                 seqs: Optional[List[int]] = None):
+                 seqs: Optional[List[int]] = None, reuse_one_launch: bool = False):
         self.w = w
         self.dev = device
+        # Reuse and window-only layers through csa2_sparse_attn_one_launch
+        # (the same attention, split and merge in one launch) instead of
+        # csa2_layer_step
+        self.reuse_one_launch = reuse_one_launch
+        self._attn_kw = {}
         B, N, T = w.B, w.N, w.T
         self.rows = B * T
         # ---- caches: rows [0, ctx0) quantized at set-up, rows of the step
@@ -109,6 +114,8 @@ class DeviceWorkload:
         self._args = [self._layer_args(li, c) for c in range(self.rot)
                       for li in range(len(self.layers))]
         nbytes = max(api.workspace_bytes(a[0], a[1]) for a in self._args)
+        for k in self._attn_kw.values():
+            nbytes = max(nbytes, api.sparse_attn_workspace_bytes(w.B * w.T, k["K"], w.W, w.DV))
         self.ws = api.workspace(nbytes, device)
         torch.cuda.synchronize()
 
@@ -148,19 +155,29 @@ class DeviceWorkload:
                           P_in=w.P)
         elif mode == I.REUSE:
             kw.update(idx_in=src_idx)
+        if mode in (I.REUSE, I.SWA):
+            self._attn_kw[(copy, li)] = dict(
+                q=L.q, B=w.B, T=w.T, kv=kw["kv"], idx=src_idx if mode == I.REUSE else None,
+                K=kw["K"], swa=L.swa, swa_scale=L.swa_scale, swa_pos0=L.swa_pos0, S=self.S,
+                W=w.W, q_pos=self.q_pos, sm_scale=w.sm_scale, dv=w.DV, out=L.out, lse=L.lse)
         # a window-only layer is a Reuse call with no global entries
         return (I.REUSE if mode == I.SWA else mode), api.layer_args(**kw)
 
     def step(self, copy: int = 0, stream=None):
         """One pass of every layer of the group, in order."""
-        n = len(self.layers)
-        c = copy % self.rot
-        for li in range(n):
-            mode, args = self._args[c * n + li]
-            api.layer_step(mode, args, self.ws, stream=stream)
+        for li in range(len(self.layers)):
+            self.run_layer(li, copy, stream)
 
     def run_layer(self, li: int, copy: int = 0, stream=None):
-        mode, args = self._args[(copy % self.rot) * len(self.layers) + li]
+        c = copy % self.rot
+        if self.reuse_one_launch and (c, li) in self._attn_kw:
+            k = self._attn_kw[(c, li)]
+            api.sparse_attn_one_launch(k["q"], k["B"], k["T"], k["kv"], k["idx"], k["K"], k["swa"],
+                                       k["swa_scale"], k["swa_pos0"], k["S"], k["W"], k["q_pos"],
+                                       k["sm_scale"], k["dv"], k["out"], k["lse"], self.ws,
+                                       stream=stream)
+            return
+        mode, args = self._args[c * len(self.layers) + li]
         api.layer_step(mode, args, self.ws, stream=stream)
 
     def cache_bytes(self):

@@ -413,6 +413,68 @@ def test_sparse_attn_window_without_rows():
     assert np.allclose(host(lse)[0], l, atol=1e-4, rtol=1e-5)
 
 
+def _attn_batch(B, T, N, K, npad, D, seed):
+    """Seeded attention inputs: B sequences of T decode rows over an FP4 cache
+    of N rows each, a window per sequence, K sorted Top-K entries per row (the
+    last npad of them -1)."""
+    rng = np.random.default_rng(seed)
+    codes, scales = oracle.quantize(rng.standard_normal((B * N, D)).astype(np.float32))
+    S = 128 if D == 576 else 64
+    sw = [I.fp8_rows(torch.from_numpy(rng.standard_normal((S, D)).astype(np.float32)))
+          for _ in range(B)]
+    swa = np.stack([s[0].numpy() for s in sw])
+    swa_s = np.array([s[1] for s in sw], np.float32)
+    rows = B * T
+    idx = np.full((rows, K), -1, np.int32)
+    for r in range(rows):
+        sel = np.sort(rng.choice(N, K - npad, replace=False))
+        idx[r, : len(sel)] = sel
+    q = torch.from_numpy(rng.standard_normal((rows, 16, D)).astype(np.float32)).to(torch.bfloat16)
+    q_pos = np.array([N - 1 - 7 * (r % T) for r in range(rows)], np.int32)
+    pos0 = np.full(B, N - S, np.int32)
+    return codes, scales, swa, swa_s, idx, q, q_pos, pos0, S
+
+
+@pytest.mark.parametrize("B,T,N,K,W,npad,D", [
+    (4, 1, 6000, 2048, 128, 0, 576),   # the decode group's grid: 4 rows x 34 splits
+    (1, 3, 6000, 2048, 128, 37, 576),
+    (2, 2, 3000, 100, 128, 0, 576),
+    (2, 1, 3000, 256, 0, 5, 576),      # no window
+    (3, 1, 2000, 300, 64, 0, 128),     # the 128-channel kernel
+    (16, 4, 3000, 2048, 128, 0, 576),  # 64 rows x 34 splits: more blocks than the device holds
+])
+def test_sparse_attn_one_launch(B, T, N, K, W, npad, D):
+    """csa2_sparse_attn_one_launch equals csa2_sparse_attn bit for bit (the
+    same split arithmetic and merge grouping; the split + merge kernels when
+    the grid does not fit the device at once), matches the oracle, and leaves
+    the control words zero for the next call on the same workspace."""
+    codes, scales, swa, swa_s, idx, q, q_pos, pos0, S = _attn_batch(B, T, N, K, npad, D, K + B)
+    dv = 512 if D == 576 else 128
+    rows = B * T
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    args = (q.cuda(), B, T, api.cache(dev(codes), dev(scales), D, N), dev(idx), K, dev(swa),
+            dev(swa_s), dev(pos0), S, W, dev(q_pos), sm, dv)
+    ws = api.workspace(api.sparse_attn_workspace_bytes(rows, K, W, dv))
+    ref_o = torch.full((rows, 16, dv), np.nan, device="cuda")
+    ref_l = torch.full((rows, 16), np.nan, device="cuda")
+    api.sparse_attn(*args, ref_o, ref_l, ws)
+    for _ in range(2):
+        out = torch.full((rows, 16, dv), np.nan, device="cuda")
+        lse = torch.full((rows, 16), np.nan, device="cuda")
+        api.sparse_attn_one_launch(*args, out, lse, ws)
+        torch.cuda.synchronize()
+        assert ctl_words_zero(ws, rows)
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    go, gl = host(out), host(lse)
+    for r in (0, rows - 1):
+        b = r // T
+        wrows = oracle.window_rows(swa[b], int(pos0[b]), int(q_pos[r]), W)
+        o, l = oracle.sparse_attn(q[r].float().numpy(), codes[b * N:(b + 1) * N],
+                                  scales[b * N:(b + 1) * N], idx[r], wrows, float(swa_s[b]), sm, dv)
+        assert_attention_close(go[r], o, what=(B, T, K, r))
+        assert np.allclose(gl[r], l, atol=1e-4, rtol=1e-5)
+
+
 def test_sparse_attn_small_dims_and_batch():
     """D = dv = 128 kernel variant, several sequences."""
     B, N, K = 3, 2000, 300

@@ -23,6 +23,23 @@ def test_group_decode_small():
     assert compare_group(w, dw, ores, oc) >= 3
 
 
+def test_group_reuse_layers_in_one_launch():
+    """The decode group with its Reuse layers run by the one-launch attention
+    gives every layer's output and lse bit for bit as csa2_layer_step does."""
+    w = I.small("t_group1", 62, B=4, N=20000, K=2048,
+                modes=(I.FULL, I.REINDEX, I.REUSE, I.REUSE))
+    ref = Hn.DeviceWorkload(w)
+    ref.step()
+    one = Hn.DeviceWorkload(w, reuse_one_launch=True)
+    for _ in range(2):
+        one.step()
+    torch.cuda.synchronize()
+    for a, b in zip(ref.layers, one.layers):
+        assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+    words = one.ws[: api.lib().csa2_workspace_control_bytes(w.B * w.T)].view(torch.int32)
+    assert int(torch.count_nonzero(words)) == 0
+
+
 def test_group_pool_small():
     w = I.small("t_pool", 61, B=1, N=60000, K=512, P=4096,
                 modes=(I.FULL, I.REINDEX, I.REINDEX), salient=True)
