@@ -97,11 +97,12 @@ def test_sparse_attn_rejects(L):
     args = lambda H=16, dv=512, K=64, ws=FAKE, nb=need: (
         FAKE, 1, 1, H, ctypes.byref(kv), FAKE, K, FAKE, FAKE, FAKE, 128, 128, FAKE,
         ctypes.c_float(0.04), dv, FAKE, None, ws, nb, None)
-    assert f(*args(H=8)) == 5
-    assert f(*args(dv=256)) == 5
-    assert f(*args(K=-1)) == 2
-    assert f(*args(nb=need - 1)) == 4
-    assert f(*args(ws=None)) == 4
+    for f in (L.csa2_sparse_attn, L.csa2_sparse_attn_one_launch):
+        assert f(*args(H=8)) == 5
+        assert f(*args(dv=256)) == 5
+        assert f(*args(K=-1)) == 2
+        assert f(*args(nb=need - 1)) == 4
+        assert f(*args(ws=None)) == 4
 
 
 def test_fp8_entry_points_reject(L):
