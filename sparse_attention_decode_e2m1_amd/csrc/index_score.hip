@@ -242,10 +242,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   if (hist) {
     __syncthreads();
     uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
-    for (int k = tid; k < kHistBins; k += 256) {
-      const uint32_t c = lhist[k];
-      if (c) atomicAdd(gh + k, c);
-    }
+    // every bin of this thread is read before any is added, so the LDS reads
+    // overlap; bin tid + 256 j keeps each atomic instruction on 256
+    // contiguous bytes
+    uint32_t cv[kHistBins / 256];
+#pragma unroll
+    for (int j = 0; j < kHistBins / 256; ++j) cv[j] = lhist[tid + 256 * j];
+#pragma unroll
+    for (int j = 0; j < kHistBins / 256; ++j)
+      if (cv[j]) atomicAdd(gh + tid + 256 * j, cv[j]);
   }
 }
 
