@@ -256,14 +256,22 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 
 
 // ---------------------------------------------------------------- prefill
+// Row groups of 4 tokens per wave, and positions per block, of the prefill
+// scoring kernel (4 groups: 178 registers, two waves per SIMD; 8 groups need
+// 448 and leave one).
+constexpr int kPrefillGroups = 4;
+constexpr int32_t kPrefillChunk = 512;
+
 // Many query tokens of one sequence score the same positions, so the scan
 // becomes a tokens x positions contraction: MFMA rows = 4 tokens x 4 heads,
 // columns = 16 positions, k = channels.  A wave holds the query fragments of
-// 32 tokens (8 row groups) in registers and dequantizes each key tile once
-// for all of them: 32 MFMAs per 16-position tile.  Lane (i, g) of row group
+// 4 NG tokens (NG row groups) in registers and dequantizes each key tile once
+// for all of them: 4 NG MFMAs per 16-position tile.  Lane (i, g) of row group
 // j then holds the four heads of token 4j + g at position i, so the score
 // needs no cross-lane sum.  Token t sees positions below n_valid[t] + nv_add.
-template <int NCH>
+// The fragments take 16 NG registers, so NG trades the dequantisation's share
+// against waves per SIMD.
+template <int NCH, int NG>
 __global__ __launch_bounds__(256) void index_score_tokens_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
@@ -272,19 +280,20 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
   constexpr int DI = 128 * NCH;
   constexpr int ROWB = DI / 2;
   constexpr int ROWS = DI / 16;
-  constexpr int NG = 8;  // row groups of 4 tokens per wave
+  constexpr int TPW = 4 * NG;  // tokens per wave
+  static_assert(TPW <= 32, "the visible-length reduction covers 32 lanes");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int rbase = blockIdx.y * 128 + wave * 32;  // first token row of this wave
-  if (rbase >= rows) return;                       // no block-wide barrier below
-  const int b = (row0 + rbase) / T;                // all 32 tokens share the sequence
+  const int rbase = blockIdx.y * 4 * TPW + wave * TPW;  // first token row of this wave
+  if (rbase >= rows) return;                             // no block-wide barrier below
+  const int b = (row0 + rbase) / T;                      // the wave's tokens share the sequence
   // the wave's longest visible length
   int64_t nvmax;
   {
-    const int tr = min(rbase + (lane & 31), rows - 1);
+    const int tr = min(rbase + (lane & (TPW - 1)), rows - 1);
     int64_t m = min(min((int64_t)n_valid[tr] + nv_add, n_out), cap);
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) m = max(m, (int64_t)__shfl_xor(m, d, kWave));
+    for (int d = 1; d < TPW; d <<= 1) m = max(m, (int64_t)__shfl_xor(m, d, kWave));
     nvmax = m;
   }
   const int64_t start = (int64_t)blockIdx.x * chunk;
@@ -409,10 +418,11 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   // sequence, 128-channel keys) take the tokens x positions kernel; the Top-K histogram is then
   // built from the written scores.
   if (!pool && HI <= 4 && T >= 32 && T % 32 == 0 && row0 % 32 == 0 && DI == 128) {
-    const int32_t pchunk = 1024;
-    const dim3 g2((unsigned)((n_max + pchunk - 1) / pchunk), (unsigned)((rows + 127) / 128));
-    CSA2_KERNEL(true, !hist, (index_score_tokens_kernel<1>), g2, dim3(256), 0, st, codes, scales,
-                cap, q_idx, w, HI, T, n_valid, nv_add, rows, scores, n_out, pchunk, row0);
+    constexpr int NG = kPrefillGroups;
+    const int32_t pchunk = kPrefillChunk;
+    const dim3 g2((unsigned)((n_max + pchunk - 1) / pchunk), (unsigned)((rows + 16 * NG - 1) / (16 * NG)));
+    CSA2_KERNEL(true, !hist, (index_score_tokens_kernel<1, NG>), g2, dim3(256), 0, st, codes,
+                scales, cap, q_idx, w, HI, T, n_valid, nv_add, rows, scores, n_out, pchunk, row0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !hist) return e;
     return launch_topk_hist(scores, rows, n_out, n_valid, nv_add, n_max, hist, hist_stride,
