@@ -333,11 +333,13 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
     const float* sc = scores + (size_t)r0 * n;
     const int32_t* nv = n_valid + r0;
     const int32_t* sp = slot_pos ? slot_pos + (size_t)r0 * n : nullptr;
-    CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(sc, nr, n, nv, 0, n, tw.hist, tw.hist_stride, tw.hist_copies, st),
-                "top-k histogram launch");
+    const bool row = topk_row_pass(nr, n);  // one block per row: no histogram
+    if (!row)
+      CSA2_LAUNCH(2, PROF_STREAM, launch_topk_hist(sc, nr, n, nv, 0, n, tw.hist, tw.hist_stride, tw.hist_copies, st),
+                  "top-k histogram launch");
     CSA2_LAUNCH(2, PROF_STREAM,
                 launch_topk_select(sc, nr, n, nv, 0, n, sp, k, idx_out + (size_t)r0 * k,
-                                   count_out ? count_out + r0 : nullptr, tw, st),
+                                   count_out ? count_out + r0 : nullptr, tw, st, row),
                 "top-k select launch");
   }
   return CSA2_OK;
@@ -598,10 +600,12 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       const int32_t nv_add = pooled_in ? 0 : 1;
       const int32_t* pool = pooled_in ? a->pool_in + (size_t)r0 * a->P_in : nullptr;
       const int64_t n_max = pooled_in ? a->P_in : a->icache.cap;
+      // one Top-K block per row (many rows, no pool kept): no score histogram
+      const bool row = !(mode == CSA2_MODE_FULL && a->P > 0) && topk_row_pass(nr, n_max);
       CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
                                   qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
-                                  L.scores, L.n_out, L.tw.hist, L.tw.hist_stride, L.tw.hist_copies,
-                                  st, r0),
+                                  L.scores, L.n_out, row ? nullptr : L.tw.hist, L.tw.hist_stride,
+                                  L.tw.hist_copies, st, r0),
                "index score launch");
       int32_t* idx = a->idx_out + (size_t)r0 * a->K;
       if (mode == CSA2_MODE_FULL && a->P > 0) {
@@ -618,7 +622,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
                  "top-k select launch");
       } else {
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,
-                                    pooled_in ? pool : nullptr, a->K, idx, nullptr, L.tw, st),
+                                    pooled_in ? pool : nullptr, a->K, idx, nullptr, L.tw, st, row),
                  "top-k select launch");
       }
     }

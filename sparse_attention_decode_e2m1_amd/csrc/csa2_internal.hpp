@@ -103,10 +103,17 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
                             int32_t hist_copies, hipStream_t st, bool first = true);
+// Passes of at least kRowTopkMinRows rows of at most kRowTopkMaxN slots can
+// select with one block per row (topk_row_pass); that path reads no score
+// histogram, so a caller that takes it (row_ok = true) builds none.
+constexpr int32_t kRowTopkMinRows = 64;
+constexpr int64_t kRowTopkMaxN = 262144;
+bool topk_row_pass(int32_t rows, int64_t n_max);
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
-                              int32_t* count_out, const TopkWs& w, hipStream_t st);
+                              int32_t* count_out, const TopkWs& w, hipStream_t st,
+                              bool row_ok = false);
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_t D, int32_t dv,
                               const uint8_t* codes, const uint8_t* scales, int64_t cap,
                               const int32_t* idx, int32_t K, const uint8_t* swa,

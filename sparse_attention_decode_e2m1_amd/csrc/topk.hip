@@ -1223,6 +1223,208 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   }
 }
 
+// ------------------------------------------------------- one block per row
+// Passes of many rows (at least kRowTopkMinRows) of up to kRowTopkMaxN
+// slots: one block of kRowThreads per row does the whole selection in LDS,
+// so no block waits on another and no histogram is built beforehand.
+//   1. a 12-bit key histogram of the row and the bin b1 of the k-th largest;
+//   2. a pass marking the slots above b1 in a bitmap and listing b1's
+//      candidates (key, slot) -- or, if b1 holds more than kRowCand, further
+//      passes over the row for the next digits;
+//   3. the exact threshold key T from 11- and 9-bit histograms; keys above T
+//      are kept, keys equal to T go to a tie bitmap whose lowest `need` slots
+//      are kept (the lower slot wins a tie);
+//   4. the kept slots written in slot order from the bitmaps.
+constexpr int kRowThreads = 1024;
+constexpr int kRowCand = 4096;
+
+// The bin (of nbins, counted from the top) where the running count from the
+// top reaches `need` (1 <= need <= total); *bin and *above (count in the bins
+// above it) are written by the thread that finds it.
+template <int NT>
+__device__ __forceinline__ void find_bin_desc(const uint32_t* h, int nbins, uint32_t need,
+                                              uint32_t* tmp, uint32_t* bin, uint32_t* above) {
+  const int tid = threadIdx.x;
+  constexpr int BPT = kHistBins / NT;  // at most 4 bins per thread
+  const int bpt = nbins >= NT ? nbins / NT : 1;
+  uint32_t c[BPT];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int d = tid * bpt + q;  // d-th bin from the top
+    c[q] = (q < bpt && d < nbins) ? h[nbins - 1 - d] : 0u;
+    sum += c[q];
+  }
+  uint32_t tot;
+  uint32_t acc = block_scan<NT>(sum, tmp, &tot);
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    if (q < bpt && acc < need && acc + c[q] >= need) {
+      *bin = (uint32_t)(nbins - 1 - (tid * bpt + q));
+      *above = acc;
+    }
+    acc += c[q];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
+    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
+    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, int32_t nwp) {
+  constexpr int NT = kRowThreads, NW = NT / 64, UN = 8;
+  extern __shared__ uint32_t lds[];
+  uint32_t* hist = lds;               // kHistBins
+  uint32_t* keep = hist + kHistBins;  // nwp words: slots kept
+  uint32_t* tie = keep + nwp;         // nwp words: slots whose key equals the threshold
+  uint32_t* ckey = tie + nwp;         // kRowCand candidate keys
+  uint32_t* cslot = ckey + kRowCand;  // and their slots
+  __shared__ uint32_t tmp[NW];
+  __shared__ uint32_t s_bin, s_above, s_ncand;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n), (int64_t)0);
+  const float* srow = scores + (int64_t)r * n;
+  const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
+  int32_t* orow = idx_out + (int64_t)r * k;
+  if (nv <= k) {  // every visible slot is kept, in place
+    for (int64_t s = tid; s < k; s += NT) orow[s] = (s < nv) ? (sp ? sp[s] : (int32_t)s) : -1;
+    if (count_out && tid == 0) count_out[r] = (int32_t)nv;
+    return;
+  }
+  // every slot of the row in UN-deep batches of coalesced loads; fn runs on
+  // every lane (slots past nv have ok == false), so it may use ballots
+  auto for_slots = [&](auto&& fn) {
+    for (int64_t base = 0; base < nv; base += (int64_t)NT * UN) {
+      float v[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) v[u] = srow[min(base + (int64_t)u * NT + tid, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int64_t s = base + (int64_t)u * NT + tid;
+        fn(s, s < nv, score_key(v[u]));
+      }
+    }
+  };
+  // a wave's 64 consecutive slots start at an even word it alone writes
+  auto mark_wave = [&](uint32_t* bm, int64_t s, uint64_t m) {
+    if (lane == 0 && m) {
+      const int64_t w0 = (s - lane) >> 5;
+      bm[w0] |= (uint32_t)m;
+      if (m >> 32) bm[w0 + 1] |= (uint32_t)(m >> 32);
+    }
+  };
+
+  // ---- 1. 12-bit histogram, cut bin b1
+  for (int j = tid; j < kHistBins + 2 * nwp; j += NT) lds[j] = 0u;
+  __syncthreads();
+  for_slots([&](int64_t, bool ok, uint32_t key) {
+    if (ok) atomicAdd(&hist[key >> kHistShift], 1u);
+  });
+  __syncthreads();
+  find_bin_desc<NT>(hist, kHistBins, (uint32_t)k, tmp, &s_bin, &s_above);
+  const uint32_t b1 = s_bin, need1 = (uint32_t)k - s_above, cnt1 = hist[b1];
+  __syncthreads();  // hist is reused below
+  for (int j = tid; j < kHistBins; j += NT) hist[j] = 0u;
+  if (tid == 0) s_ncand = 0u;
+  __syncthreads();
+
+  // ---- 2. slots above b1; the next digit (key bits 19..9) of b1's keys
+  const bool in_lds = cnt1 <= (uint32_t)kRowCand;
+  for_slots([&](int64_t s, bool ok, uint32_t key) {
+    const uint32_t bin = key >> kHistShift;
+    const bool isc = ok && bin == b1;
+    mark_wave(keep, s, __ballot(ok && bin > b1));
+    if (isc) atomicAdd(&hist[(key >> 9) & 2047u], 1u);
+    if (in_lds) {
+      const uint64_t mc = __ballot(isc);
+      if (mc) {
+        uint32_t cb = 0;
+        if (lane == 0) cb = atomicAdd(&s_ncand, (uint32_t)__popcll(mc));
+        cb = __builtin_amdgcn_readfirstlane(cb);
+        if (isc) {
+          const uint32_t p = cb + (uint32_t)__popcll(mc & lanemask_lt());
+          ckey[p] = key;
+          cslot[p] = (uint32_t)s;
+        }
+      }
+    }
+  });
+  __syncthreads();
+  find_bin_desc<NT>(hist, 2048, need1, tmp, &s_bin, &s_above);
+  const uint32_t b2 = s_bin, need2 = need1 - s_above;
+  const uint32_t p23 = (b1 << 11) | b2;  // key bits 31..9 of the threshold
+  __syncthreads();
+  for (int j = tid; j < 512; j += NT) hist[j] = 0u;
+  __syncthreads();
+
+  // ---- 3. the last digit (key bits 8..0), the threshold key, the marks
+  if (in_lds) {
+    for (uint32_t c = tid; c < cnt1; c += NT)
+      if ((ckey[c] >> 9) == p23) atomicAdd(&hist[ckey[c] & 511u], 1u);
+  } else {
+    for_slots([&](int64_t, bool ok, uint32_t key) {
+      if (ok && (key >> 9) == p23) atomicAdd(&hist[key & 511u], 1u);
+    });
+  }
+  __syncthreads();
+  find_bin_desc<NT>(hist, 512, need2, tmp, &s_bin, &s_above);
+  const uint32_t T = (p23 << 9) | s_bin, need3 = need2 - s_above;
+  if (in_lds) {
+    for (uint32_t c = tid; c < cnt1; c += NT) {
+      const uint32_t key = ckey[c], s = cslot[c];
+      if (key > T) atomicOr(&keep[s >> 5], 1u << (s & 31));
+      else if (key == T) atomicOr(&tie[s >> 5], 1u << (s & 31));
+    }
+  } else {
+    for_slots([&](int64_t s, bool ok, uint32_t key) {
+      const bool inb = ok && (key >> kHistShift) == b1;
+      mark_wave(keep, s, __ballot(inb && key > T));
+      mark_wave(tie, s, __ballot(inb && key == T));
+    });
+  }
+  __syncthreads();
+
+  // ---- 4. the lowest need3 tie slots join the kept ones; output in slot order
+  const int nw = (int)((nv + 31) >> 5);
+  const int wpt = (nw + NT - 1) / NT;  // words per thread, contiguous
+  const int w_lo = min(tid * wpt, nw), w_hi = min(w_lo + wpt, nw);
+  uint32_t tcount = 0;
+  for (int w = w_lo; w < w_hi; ++w) tcount += (uint32_t)__popc(tie[w]);
+  uint32_t tot;
+  uint32_t tb = block_scan<NT>(tcount, tmp, &tot);  // tie slots before this thread's words
+  uint32_t kcount = 0;
+  for (int w = w_lo; w < w_hi; ++w) {
+    uint32_t tw = tie[w], take = 0;
+    const uint32_t c = (uint32_t)__popc(tw);
+    if (tb + c <= need3) {
+      take = tw;
+    } else {
+      for (uint32_t i = tb; i < need3; ++i) {  // the lowest need3 - tb bits
+        take |= tw & (0u - tw);
+        tw &= tw - 1u;
+      }
+    }
+    tb += c;
+    const uint32_t sel = keep[w] | take;
+    keep[w] = sel;
+    kcount += (uint32_t)__popc(sel);
+  }
+  uint32_t o = block_scan<NT>(kcount, tmp, &tot);  // tot == k
+  for (int w = w_lo; w < w_hi; ++w) {
+    uint32_t m = keep[w];
+    while (m) {
+      const int64_t s = (int64_t)w * 32 + (__ffs(m) - 1);
+      orow[o++] = sp ? sp[s] : (int32_t)s;
+      m &= m - 1u;
+    }
+  }
+  if (count_out && tid == 0) count_out[r] = k;
+}
+
+bool topk_row_pass(int32_t rows, int64_t n_max) {
+  return rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN;
+}
+
 static int32_t topk_blocks(int64_t n_max, int32_t chunk) {
   const int64_t b = (n_max + chunk - 1) / chunk;
   return (int32_t)(b < 1 ? 1 : b);
@@ -1262,7 +1464,25 @@ hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const 
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
-                              int32_t* count_out, const TopkWs& w, hipStream_t st) {
+                              int32_t* count_out, const TopkWs& w, hipStream_t st,
+                              bool row_ok) {
+  // Many rows, no histogram built: one block per row.
+  if (row_ok && topk_row_pass(rows, n_max)) {
+    const int32_t nwp = (int32_t)(((n + 31) / 32 + 3) & ~3);
+    const size_t lds = (size_t)(kHistBins + 2 * nwp + 2 * kRowCand) * sizeof(uint32_t);
+    static bool raised = false;
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) +
+                                                2 * kRowCand) * sizeof(uint32_t)));
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+    CSA2_KERNEL(true, true, topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), lds, st,
+                scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp);
+    return hipGetLastError();
+  }
   // Passes whose blocks can all be resident at once take the one-wait variant.
   {
     const int32_t nblk = topk_blocks(n_max, kTopkChunk);

@@ -247,13 +247,39 @@ def test_topk_large_rows():
 
 
 def test_topk_many_rows():
-    # more select blocks than the device holds at once: the path whose last
-    # block completes each row by itself
+    # more select blocks than the device holds at once, fewer rows than take
+    # one block per row: the path whose last block completes each row
     rng = np.random.default_rng(5)
-    rows, n = 144, 16384 + 100
+    rows, n = 48, 100000 + 100
     s = rng.standard_normal((rows, n)).astype(np.float32)
     nv = rng.integers(200, n + 1, rows).astype(np.int32)
     _check_topk(s, nv, 256)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "three_values", "slot_map"])
+def test_topk_one_block_per_row(kind):
+    """64 or more rows of at most 2^18 slots: one block per row selects in LDS
+    (the cut bin's candidates listed there, or, past 4096 of them, further
+    passes over the row).  Rows at and below k visible slots included."""
+    rng = np.random.default_rng(len(kind))
+    rows, n = 72, 40000 + 7
+    if kind == "ties":
+        s = np.round(rng.standard_normal((rows, n)), 1)
+        s[3] = np.where(rng.random(n) < 0.5, -0.0, 0.0)   # -0 == +0
+        s[4] = 0.0                                        # one tie storm
+    elif kind == "three_values":
+        s = rng.integers(0, 3, (rows, n)).astype(np.float64)
+    else:
+        s = rng.standard_normal((rows, n))
+    s = s.astype(np.float32)
+    pool = None
+    if kind == "slot_map":
+        pool = np.stack([np.sort(rng.choice(1 << 20, n, replace=False))
+                         for _ in range(rows)]).astype(np.int32)
+    for k in (1, 256, 2048):
+        nv = rng.integers(k + 1, n + 1, rows).astype(np.int32)
+        nv[0], nv[1], nv[2] = max(k - 5, 0), k, k + 1
+        _check_topk(s, nv, k, slot_pos=pool)
 
 
 def test_topk_slot_map():
