@@ -1328,27 +1328,48 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   if (tid == 0) s_ncand = 0u;
   __syncthreads();
 
-  // ---- 2. slots above b1; the next digit (key bits 19..9) of b1's keys
+  // ---- 2. slots above b1; the next digit (key bits 19..9) of b1's keys.
+  // The bitmap words are still zero and each belongs to one wave, so they
+  // are stored, not or-ed; a wave reserves room for a whole batch's
+  // candidates with one counter update.
   const bool in_lds = cnt1 <= (uint32_t)kRowCand;
-  for_slots([&](int64_t s, bool ok, uint32_t key) {
-    const uint32_t bin = key >> kHistShift;
-    const bool isc = ok && bin == b1;
-    mark_wave(keep, s, __ballot(ok && bin > b1));
-    if (isc) atomicAdd(&hist[(key >> 9) & 2047u], 1u);
-    if (in_lds) {
-      const uint64_t mc = __ballot(isc);
-      if (mc) {
-        uint32_t cb = 0;
-        if (lane == 0) cb = atomicAdd(&s_ncand, (uint32_t)__popcll(mc));
-        cb = __builtin_amdgcn_readfirstlane(cb);
-        if (isc) {
-          const uint32_t p = cb + (uint32_t)__popcll(mc & lanemask_lt());
-          ckey[p] = key;
-          cslot[p] = (uint32_t)s;
+  for (int64_t base = 0; base < nv; base += (int64_t)NT * UN) {
+    float v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) v[u] = srow[min(base + (int64_t)u * NT + tid, nv - 1)];
+    uint64_t mc[UN];
+    uint32_t nc = 0;
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int64_t s = base + (int64_t)u * NT + tid;
+      const bool ok = s < nv;
+      const uint32_t key = score_key(v[u]), bin = key >> kHistShift;
+      const uint64_t mk = __ballot(ok && bin > b1);
+      if (lane == 0 && s - lane < nv) {
+        const int64_t w0 = (s - lane) >> 5;
+        keep[w0] = (uint32_t)mk;
+        if (mk >> 32) keep[w0 + 1] = (uint32_t)(mk >> 32);
+      }
+      const bool isc = ok && bin == b1;
+      if (isc) atomicAdd(&hist[(key >> 9) & 2047u], 1u);
+      mc[u] = __ballot(isc);
+      nc += (uint32_t)__popcll(mc[u]);
+    }
+    if (in_lds && nc) {  // wave-uniform
+      uint32_t cb = 0;
+      if (lane == 0) cb = atomicAdd(&s_ncand, nc);
+      cb = __builtin_amdgcn_readfirstlane(cb);
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        if ((mc[u] >> lane) & 1ull) {
+          const uint32_t p = cb + (uint32_t)__popcll(mc[u] & lanemask_lt());
+          ckey[p] = score_key(v[u]);
+          cslot[p] = (uint32_t)(base + (int64_t)u * NT + tid);
         }
+        cb += (uint32_t)__popcll(mc[u]);
       }
     }
-  });
+  }
   __syncthreads();
   find_bin_desc<NT>(hist, 2048, need1, tmp, &s_bin, &s_above);
   const uint32_t b2 = s_bin, need2 = need1 - s_above;
