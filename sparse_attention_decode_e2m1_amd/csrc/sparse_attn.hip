@@ -191,6 +191,27 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       }
     }
   };
+  // FP4 global splits of several rounds request the next round's rows into
+  // a second set of registers once the current round's logits are done, so
+  // they arrive during its softmax and P.V.
+  constexpr bool PREF = MULTI && !WIN && !KV8;
+  uint32_t p0[PREF ? NM : 1], p1[PREF ? NM : 1], psc[PREF ? NM : 1];
+  bool pvalid = false;
+  auto prefetch_row = [&](int e) {
+    if constexpr (PREF) {
+      pvalid = e < a.K && ix >= 0 && ix < a.cap;
+      const int64_t row = (int64_t)b * a.cap + (pvalid ? ix : 0);
+      const uint8_t* cr = a.codes + row * (D / 2);
+      const uint8_t* sr = a.scales + row * (D / 16);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
+        p0[m] = cw.x;
+        p1[m] = cw.y;
+        psc[m] = sr[4 * m + g];
+      }
+    }
+  };
   load_row(e0);
   // keep the row loads ahead of the query conversion (the scheduler would
   // otherwise sink them below it, after the query has arrived)
@@ -240,7 +261,17 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   for (int rnd = 0; rnd < rounds; ++rnd) {
     if (MULTI && rnd > 0) {
       __syncthreads();  // the previous round's reads of Vs and Lg are done
-      load_row(e0 + 64 * rnd);
+      if constexpr (PREF) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          w0[m] = p0[m];
+          w1[m] = p1[m];
+          sc[m] = psc[m];
+        }
+        valid = pvalid;
+      } else {
+        load_row(e0 + 64 * rnd);
+      }
     }
     if (MULTI && rnd + 1 < rounds) ix = load_ix(e0 + 64 * (rnd + 1));  // next round's index
     // ---- dequantize this wave's tile, logits (rows = heads 4g + rr, column = entry i)
@@ -282,6 +313,9 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
           *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
         }
       }
+    }
+    if constexpr (PREF) {
+      if (rnd + 1 < rounds) prefetch_row(e0 + 64 * (rnd + 1));
     }
     // ---- softmax: the tile's logits (heads 4g + rr, entry i) go to LDS; after
     // one barrier, lane (i, g) reads head i's logits at its P.V operand slots
