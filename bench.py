@@ -200,7 +200,7 @@ def main():
                          "reference kernel that calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU; the path shards by sequence or by "
+        print("bench.py: measures one GPU only; the path shards by sequence or by "
               "context across GPUs only in design (no multi-GPU run)", file=sys.stderr)
         sys.exit(2)
 

@@ -90,7 +90,7 @@ typedef struct {
   int64_t cap;     /* rows per sequence */
 } csa2_fp8_cache;
 
-/* Limits of the kernels in this build. */
+/* Limits the kernels accept. */
 #define CSA2_MAX_K 16384        /* Top-K and pool size */
 #define CSA2_MAX_W 16384        /* sliding-window length */
 #define CSA2_HEADS 16           /* query heads of the attention kernel */
