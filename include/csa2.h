@@ -60,7 +60,8 @@ typedef enum {
   CSA2_ERR_DTYPE = 3,       /* unknown dtype code */
   CSA2_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   CSA2_ERR_UNSUPPORTED = 5, /* valid request outside what the kernels cover */
-  CSA2_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+  CSA2_ERR_HIP = 6,         /* a HIP runtime call or launch failed */
+  CSA2_ERR_INCOMPLETE = 7   /* a bounded wait of a one-wait launch ran out (csa2_workspace_check) */
 } csa2_status;
 
 /* Static per-layer mode ([P1 §03 "CSA2"]; [P5 "Then every layer stops asking
@@ -196,6 +197,31 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
                       const int32_t* slot_pos, int32_t k, int32_t* idx_out, int32_t* count_out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* How a pass selects (chosen from its shape; csa2_set_topk_variant can force
+ * one for tests).  The one-wait variant runs when all of the pass's select
+ * blocks fit on the device at once by the occupancy query: each block then
+ * waits, with a bounded poll, for a record that the row's last block sends
+ * it.  If another process or stream keeps some of those blocks from being
+ * resident, the poll runs out: that block writes nothing of its part of
+ * idx_out and sets a flag in the workspace's control words.  The call still
+ * returns CSA2_OK (the failure happens on the device, after the return);
+ * csa2_workspace_check reports it as CSA2_ERR_INCOMPLETE and clears the
+ * flag.  Records carry the launch's generation, so a record left behind by
+ * such a launch is never taken by a later one, and later calls on the same
+ * workspace are correct. */
+typedef enum {
+  CSA2_TOPK_AUTO = 0,             /* chosen from the shape */
+  CSA2_TOPK_ROW = 1,              /* one block per row, in LDS (rows of <= 2^18 slots) */
+  CSA2_TOPK_ONE_WAIT = 2,         /* resident blocks; the row's last block sends records */
+  CSA2_TOPK_SELECT = 3,           /* 4096-score blocks; the row's last block finishes */
+  CSA2_TOPK_SELECT_CUT = 4,       /* ... after a kernel that finds each row's cut bin */
+  CSA2_TOPK_SELECT_LARGE = 5,     /* 16384-score blocks; the row's last block finishes */
+  CSA2_TOPK_SELECT_LARGE_CUT = 6  /* ... after the cut kernel */
+} csa2_topk_variant;
+/* Flag in csa2_topk_last_variant(): the finishing block merged two sorted
+ * lists (rows over 2^19 slots) instead of reading back a bitmap. */
+#define CSA2_TOPK_LIST_FINISH 16
+
 /* ------------------------------------------------------------------ */
 /* Sparse attention ([P4 "Share the cache and the search work"]: attention
  * over the selected global entries alongside a local 128-token window;
@@ -243,8 +269,9 @@ csa2_status csa2_sparse_attn(const uint16_t* q, int32_t B, int32_t T, int32_t H,
  * csa2_sparse_attn run.  Arguments, workspace and results are those of
  * csa2_sparse_attn, bit for bit.  The wait is bounded: if it runs out (the
  * grid did not become resident, e.g. with other work occupying the device),
- * a control word stays nonzero and the output is not written.  Callers that
- * run other kernels concurrently on the device should use csa2_sparse_attn. */
+ * a control word stays set and the output is not written; csa2_workspace_check
+ * reports it as CSA2_ERR_INCOMPLETE.  Callers that run other kernels
+ * concurrently on the device should use csa2_sparse_attn. */
 csa2_status csa2_sparse_attn_one_launch(const uint16_t* q, int32_t B, int32_t T, int32_t H,
                                         const csa2_fp4_cache* kv, const int32_t* idx, int32_t K,
                                         const uint8_t* swa, const float* swa_scale,
@@ -284,7 +311,8 @@ csa2_status csa2_sparse_attn_fp8(const uint16_t* q, int32_t B, int32_t T, int32_
  *             pool_count_in valid slots; Top-K -> idx_out; attend.
  *   REUSE   : attend over idx_in.
  * kv / icache are the layer's own caches for FULL and the referenced
- * layer's caches otherwise. */
+ * layer's caches otherwise.  Its Top-K passes select as csa2_topk does
+ * (including the one-wait variant and its csa2_workspace_check report). */
 typedef struct {
   int32_t B, T;          /* sequences, query tokens per sequence */
   int32_t H, D, dv;      /* 16 query heads, row channels, value channels */
@@ -349,6 +377,32 @@ csa2_status csa2_profile_end(int32_t* counts, double* total_ms);
  * library, so bindings can check their struct layout. */
 size_t csa2_layer_args_size(void);
 size_t csa2_fp4_cache_size(void);
+
+/* Reports whether a one-wait launch on this workspace gave up waiting
+ * (see the Top-K variants above and csa2_sparse_attn_one_launch).  Waits
+ * for `stream`, reads the wait-failure flags of the control words of
+ * min(rows, 256) query rows (rows = the largest B*T used with the
+ * workspace), and returns CSA2_ERR_INCOMPLETE if any is set, after zeroing
+ * the whole control block (every call on the workspace has finished, so
+ * nothing is still writing to it).  The outputs of the calls since the last
+ * check are then incomplete.  Returns CSA2_OK when no flag is set.
+ * Errors: NULL workspace, ws_bytes below csa2_workspace_control_bytes(rows),
+ * a HIP failure while reading. */
+csa2_status csa2_workspace_check(void* ws, size_t ws_bytes, int32_t rows, void* stream);
+
+/* Diagnostics for tests (process-wide, not for use while other threads
+ * launch).  csa2_set_topk_variant forces a Top-K variant on every later pass
+ * that it can serve (a pass it cannot serve -- rows too long for ROW, a grid
+ * too large for ONE_WAIT -- keeps its own choice) and returns the previous
+ * setting; CSA2_TOPK_AUTO restores the default.  csa2_topk_last_variant
+ * gives the variant the calling thread's last Top-K pass ran (with
+ * CSA2_TOPK_LIST_FINISH or-ed in when it applies), -1 before any.
+ * csa2_set_wait_limit sets the polls a one-wait block makes before it gives
+ * up (default 2^20, about 10 ms or more; 0 gives up at once, which forces
+ * the failure path) and returns the previous limit. */
+int32_t csa2_set_topk_variant(int32_t variant);
+int32_t csa2_topk_last_variant(void);
+uint32_t csa2_set_wait_limit(uint32_t polls);
 
 #ifdef __cplusplus
 }

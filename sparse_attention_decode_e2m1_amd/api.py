@@ -21,6 +21,11 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "csa2.h")
 FULL, REINDEX, REUSE = 0, 1, 2
 F32, BF16 = 0, 1
 HEADS = 16
+ERR_INCOMPLETE = 7
+# csa2_topk_variant
+TOPK_AUTO, TOPK_ROW, TOPK_ONE_WAIT, TOPK_SELECT, TOPK_SELECT_CUT, TOPK_SELECT_LARGE, \
+    TOPK_SELECT_LARGE_CUT = range(7)
+TOPK_LIST_FINISH = 16
 
 c_i32, c_i64, c_f32, c_p, c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                   ctypes.c_void_p, ctypes.c_size_t)
@@ -99,6 +104,10 @@ def lib():
             "csa2_workspace_control_bytes": (c_sz, [c_i32]),
             "csa2_profile_begin": (c_i32, []),
             "csa2_profile_end": (c_i32, [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]),
+            "csa2_workspace_check": (c_i32, [c_p, c_sz, c_i32, c_p]),
+            "csa2_set_topk_variant": (c_i32, [c_i32]),
+            "csa2_topk_last_variant": (c_i32, []),
+            "csa2_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -300,6 +309,25 @@ def profile_end() -> dict:
     tot = (ctypes.c_double * n)()
     _check(lib().csa2_profile_end(counts, tot))
     return {k: (int(counts[i]), float(tot[i])) for i, k in enumerate(PROFILE_KERNELS)}
+
+
+def workspace_check(ws: torch.Tensor, rows: int, stream=None):
+    """csa2_workspace_check: raises Csa2Error (status ERR_INCOMPLETE) if a
+    one-wait launch on this workspace gave up waiting."""
+    _check(lib().csa2_workspace_check(_ptr(ws), ws.numel(), rows, _stream(stream)))
+
+
+def set_topk_variant(variant: int) -> int:
+    """Force a Top-K variant (TOPK_*); returns the previous setting."""
+    return int(lib().csa2_set_topk_variant(variant))
+
+
+def topk_last_variant() -> int:
+    return int(lib().csa2_topk_last_variant())
+
+
+def set_wait_limit(polls: int) -> int:
+    return int(lib().csa2_set_wait_limit(polls))
 
 
 def raw_call(name: str, *args):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -20,6 +21,14 @@ LaunchTiming& launch_timing() {
   static thread_local LaunchTiming t;
   return t;
 }
+std::atomic<int32_t> g_topk_forced{kTopkAuto};
+std::atomic<uint32_t> g_wait_limit{1u << 20};
+std::atomic<uint32_t> g_generation{0};
+thread_local int32_t g_topk_last = -1;
+int32_t topk_variant_forced() { return g_topk_forced.load(std::memory_order_relaxed); }
+void set_topk_last(int32_t v) { g_topk_last = v; }
+uint32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+uint32_t next_generation() { return g_generation.fetch_add(1, std::memory_order_relaxed) + 1; }
 }  // namespace csa2
 
 namespace {
@@ -170,6 +179,7 @@ const char* csa2_status_string(csa2_status s) {
     case CSA2_ERR_WORKSPACE: return "workspace too small";
     case CSA2_ERR_UNSUPPORTED: return "unsupported";
     case CSA2_ERR_HIP: return "hip error";
+    case CSA2_ERR_INCOMPLETE: return "a one-wait launch gave up waiting";
   }
   return "unknown status";
 }
@@ -217,6 +227,53 @@ int64_t csa2_fp4_bytes_per_token(int32_t dim) {
   if (dim <= 0 || dim % 16) return -1;
   return dim / 2 + dim / 16;
 }
+
+csa2_status csa2_workspace_check(void* ws, size_t ws_bytes, int32_t rows, void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(ws, CSA2_ERR_NULL, "workspace is NULL");
+  CSA2_REQUIRE(rows >= 1, CSA2_ERR_SHAPE, "rows must be >= 1");
+  const size_t ctl = csa2_workspace_control_bytes(rows);
+  CSA2_REQUIRE(ws_bytes >= ctl, CSA2_ERR_WORKSPACE, "workspace needs %zu control bytes (got %zu)",
+               ctl, ws_bytes);
+  const int32_t rc = std::min(rows, kRowChunk);
+  const hipStream_t st = as_stream(stream);
+  CSA2_TRY(hipStreamSynchronize(st), "stream wait");
+  // per row: 16 words after the histogram copies; word 2 is the Top-K
+  // one-wait flag, word kAttnCtlWord - kHistWords + 2 the one-launch
+  // attention's
+  constexpr int kSpan = 16;
+  static_assert(kAttnCtlWord - kHistWords + 2 < kSpan, "flags inside the words read");
+  std::vector<uint32_t> words((size_t)rc * kSpan);
+  CSA2_TRY(hipMemcpy2D(words.data(), kSpan * sizeof(uint32_t),
+                       static_cast<char*>(ws) + kHistWords * sizeof(uint32_t),
+                       kCtlWordsPerRow * sizeof(uint32_t), kSpan * sizeof(uint32_t), (size_t)rc,
+                       hipMemcpyDeviceToHost),
+           "control word read");
+  int32_t first = -1, nbad = 0;
+  for (int32_t r = 0; r < rc; ++r) {
+    const uint32_t* w = words.data() + (size_t)r * kSpan;
+    if (w[2] != 0u || w[kAttnCtlWord - kHistWords + 2] != 0u) {
+      if (first < 0) first = r;
+      ++nbad;
+    }
+  }
+  if (nbad == 0) return CSA2_OK;
+  CSA2_TRY(launch_fill_zero(ws, ctl, st), "control block clear");
+  CSA2_TRY(hipStreamSynchronize(st), "stream wait");
+  return fail(CSA2_ERR_INCOMPLETE,
+              "a one-wait launch gave up waiting for another block (%d row slot(s), first %d): "
+              "the outputs of the calls since the last check are incomplete",
+              nbad, first);
+}
+
+int32_t csa2_set_topk_variant(int32_t variant) {
+  if (variant < kTopkAuto || variant >= kTopkVariants) variant = kTopkAuto;
+  return g_topk_forced.exchange(variant);
+}
+
+int32_t csa2_topk_last_variant(void) { return g_topk_last; }
+
+uint32_t csa2_set_wait_limit(uint32_t polls) { return g_wait_limit.exchange(polls); }
 
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();

@@ -61,6 +61,24 @@ inline AttnSplit attn_split(int32_t K, int32_t W, int32_t rounds = 1) {
   return s;
 }
 
+// Process-wide diagnostic controls (set through csa2_set_topk_variant and
+// csa2_set_wait_limit) and what the last Top-K launch of this thread ran.
+enum TopkVariant : int32_t {
+  kTopkAuto = 0,         // chosen from the pass's shape
+  kTopkRow = 1,          // one block per row, selection in LDS (rows <= kRowTopkMaxN slots)
+  kTopkOneWait = 2,      // every block resident; the row's last block sends records
+  kTopkSelect = 3,       // 4096-score blocks; the row's last block finishes
+  kTopkSelectCut = 4,    // ... after a per-row cut kernel
+  kTopkSelectLarge = 5,  // 16384-score blocks; the row's last block finishes
+  kTopkSelectLargeCut = 6,
+  kTopkVariants = 7,
+};
+constexpr int32_t kTopkListFinish = 16;  // flag: the finishing block merged sorted lists
+int32_t topk_variant_forced();
+void set_topk_last(int32_t v);
+uint32_t wait_limit();
+uint32_t next_generation();  // per one-wait launch (records carry it)
+
 // Launch timing: while the library profiles a call, its launchers attach
 // the call's start and stop events to the first and last kernel they launch
 // (the events then carry the kernels' own start and end times).

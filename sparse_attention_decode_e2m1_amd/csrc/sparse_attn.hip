@@ -528,14 +528,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 // merges passes vb = split, split + nsplit, ... of the row's output with the
 // merge kernel's arithmetic and split grouping, so the result is the same
 // bit for bit.  Words of row r at ctl + r * ctl_stride: arrivals, departures,
-// and a flag set if the wait ran out; the row's last block to leave zeroes
-// the two counters.
-constexpr uint32_t kAttnSpinLimit = 1u << 20;
-
+// and a flag set if the wait ran out (after wait_limit polls; 0 gives up
+// at once); the row's last block to leave zeroes the two counters.
 template <int D, int DV, int KB>
 __global__ __launch_bounds__(256, 2) void sparse_attn_one_launch_kernel(AttnArgs a, uint32_t* ctl,
                                                                         int64_t ctl_stride,
-                                                                        float* out, float* lse) {
+                                                                        float* out, float* lse,
+                                                                        uint32_t wait_limit) {
   extern __shared__ __attribute__((aligned(16))) _Float16 Vs[];
   __shared__ __attribute__((aligned(16))) float Lg[16 * kLgStride];
   __shared__ float Sg[64 + 4];
@@ -552,9 +551,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_one_launch_kernel(AttnArgs
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t it = 0;
-    bool ok;
-    while (!(ok = ld_coh(c) >= (uint32_t)a.nsplit) && ++it < kAttnSpinLimit)
-      __builtin_amdgcn_s_sleep(2);
+    bool ok = false;
+    if (wait_limit > 0) {
+      while (!(ok = ld_coh(c) >= (uint32_t)a.nsplit) && ++it < wait_limit)
+        __builtin_amdgcn_s_sleep(2);
+    }
     if (!ok) st_coh(c + 2, 1u);  // flagged in the control words; the output is not written
     s_ok = ok ? 1u : 0u;
   }
@@ -625,7 +626,7 @@ static hipError_t try_one_launch(const AttnArgs& args, int32_t rows, size_t lds,
   if ((int64_t)args.nsplit * rows > cap[dev]) return hipSuccess;
   const dim3 grid((unsigned)args.nsplit, (unsigned)rows);
   CSA2_KERNEL(true, true, (sparse_attn_one_launch_kernel<D, DV, KB>), grid, dim3(256), lds, st,
-              args, ctl, (int64_t)kCtlWordsPerRow, out, lse);
+              args, ctl, (int64_t)kCtlWordsPerRow, out, lse, wait_limit());
   *launched = true;
   return hipGetLastError();
 }

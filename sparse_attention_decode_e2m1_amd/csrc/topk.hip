@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4, 
 // block to arrive only finds the threshold among the candidates and sends
 // each block of the row a record: where the block's part of the output
 // starts and which of its candidates are chosen.  Each block waits for its
-// record (its only wait on another block, bounded by kSpinLimit polls) and
+// record (its only wait on another block, bounded by the wait limit's polls) and
 // writes its own kept slots from the scores it still holds.  512 threads and
 // 8 scores per thread, so two blocks fit on a compute unit.
 constexpr int kCoopThreads = 512;
@@ -761,7 +761,6 @@ constexpr int kCoopWaves = kCoopThreads / 64;
 constexpr int kCoopPL = kTopkChunk / kCoopThreads;  // scores per thread
 constexpr int kCoopCP = 8;                          // early candidate loads per thread
 constexpr size_t kCoopLds = 17 * 1024;               // dynamic LDS of a block
-constexpr uint32_t kSpinLimit = 1u << 20;
 // Records live in histogram copies 4..7 of the row's control block (the
 // passes that use this variant keep at most 4 copies); word 2 after the
 // histogram words flags a record that never came.
@@ -774,13 +773,21 @@ static_assert(kL2WordOffset + 2048 <= kHistWords, "records and digit bins fit th
 
 // Record of block b, written by the completing block and cleared by b: bit
 // 63 set; bit 62: no candidate chosen; bits 61..42: kt; bits 41..29: rel;
-// bits 28..0: the output offset of the block's first kept slot.  A candidate
-// of block b (its key's top 12 bits are the cut bin) with low 20 key bits lo
-// at block-relative slot l is chosen iff lo > kt, or lo == kt and l < rel.
+// bits 28..15: the launch's generation; bits 14..0: the output offset of the
+// block's first kept slot (< 2^15 since k <= 16384).  A candidate of block b
+// (its key's top 12 bits are the cut bin) with low 20 key bits lo at
+// block-relative slot l is chosen iff lo > kt, or lo == kt and l < rel.  A
+// block takes only a record of its own launch's generation, so a record left
+// by a launch whose wait gave up is never mistaken for the current one.
+constexpr uint32_t kGenMask = 0x3FFFu;
 __device__ __forceinline__ uint64_t coop_record(bool none, uint32_t kt, uint32_t rel,
-                                                uint32_t off) {
+                                                uint32_t gen, uint32_t off) {
   return (1ull << 63) | ((uint64_t)none << 62) | ((uint64_t)(kt & 0xFFFFFu) << 42) |
-         ((uint64_t)(rel & 0x1FFFu) << 29) | (uint64_t)(off & 0x1FFFFFFFu);
+         ((uint64_t)(rel & 0x1FFFu) << 29) | ((uint64_t)(gen & kGenMask) << 15) |
+         (uint64_t)(off & 0x7FFFu);
+}
+__device__ __forceinline__ bool record_is(uint64_t rec, uint32_t gen) {
+  return (rec >> 63) && (((uint32_t)(rec >> 15) & kGenMask) == (gen & kGenMask));
 }
 
 constexpr int kBucketMax = kCoopThreads;  // candidates of the cut digit ranked directly
@@ -831,7 +838,8 @@ __device__ __forceinline__ uint32_t pick_digit(Bins<2048 / NT> cv, uint32_t rem,
 // than kBucketMax share it).
 __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* __restrict__ orow,
                               int32_t* __restrict__ count_out, const TopkWs& w, uint32_t* smem,
-                              uint32_t* tmp, uint32_t* rh, uint64_t* recs, uint64_t* own) {
+                              uint32_t* tmp, uint32_t* rh, uint64_t* recs, uint64_t* own,
+                              uint32_t gen) {
   constexpr int NT = kCoopThreads, NW = kCoopWaves, CH = kTopkChunk, BPT = 2048 / NT;
   uint32_t* cntE = smem;                    // candidates per block
   uint32_t* chosen = cntE + NT;             // chosen candidates per block
@@ -1038,7 +1046,7 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
   const int64_t slot_t = (int64_t)(0xFFFFFFFFu - (uint32_t)(thr & 0xFFFFFFFFull));
   if (tid < nblk && (int64_t)tid * CH < nv) {
     const int64_t rel = min(max(slot_t - (int64_t)tid * CH + 1, (int64_t)0), (int64_t)CH);
-    const uint64_t rec = coop_record(none, kt, (uint32_t)rel, off);
+    const uint64_t rec = coop_record(none, kt, (uint32_t)rel, gen, off);
     if (tid == (int)blockIdx.x) *own = rec;
     else st_coh(recs + tid, rec);
   }
@@ -1050,7 +1058,7 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
 __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_coop_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, TopkWs w) {
+    int32_t* __restrict__ count_out, TopkWs w, uint32_t gen, uint32_t wait_limit) {
   constexpr int NT = kCoopThreads, NW = kCoopWaves, PL = kCoopPL;
   extern __shared__ uint64_t smem64[];
   uint32_t* smem = reinterpret_cast<uint32_t*>(smem64);
@@ -1167,7 +1175,7 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   __syncthreads();
   uint64_t* recs = reinterpret_cast<uint64_t*>(rh + kRecWordOffset);
   if (s_last) {
-    coop_complete(r, nv, k, nblk, orow, count_out, w, smem, tmp, rh, recs, &s_rec);
+    coop_complete(r, nv, k, nblk, orow, count_out, w, smem, tmp, rh, recs, &s_rec, gen);
     // every block of the row has read the histogram copies: leave them zero
     uint4* h4p = reinterpret_cast<uint4*>(rh);
     for (int j = tid; j < w.hist_copies * kHistBins / 4; j += NT) h4p[j] = make_uint4(0, 0, 0, 0);
@@ -1180,11 +1188,19 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
     if (s_last) {
       rec = s_rec;
     } else {
+      // A wait limit of 0 gives up at once (the host forces the failure path).
       uint64_t* mine = recs + blockIdx.x;
       uint32_t it = 0;
-      while (((rec = ld_coh(mine)) >> 63) == 0ull && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
-      if (rec >> 63) st_coh(mine, (uint64_t)0);
-      else st_coh(ctr + 2, 1u);  // no record: the pass failed (flagged in the control words)
+      bool got = false;
+      if (wait_limit > 0) {
+        while (!(got = record_is(rec = ld_coh(mine), gen)) && ++it < wait_limit)
+          __builtin_amdgcn_s_sleep(2);
+      }
+      if (got) st_coh(mine, (uint64_t)0);
+      else {
+        rec = 0ull;
+        st_coh(ctr + 2, 1u);  // no record: the pass failed (csa2_workspace_check reports it)
+      }
     }
     s_rec = rec;
   }
@@ -1193,7 +1209,7 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   if ((rec >> 63) == 0ull) return;
   const bool none = (rec >> 62) & 1ull;
   const uint32_t kt = (uint32_t)(rec >> 42) & 0xFFFFFu, rel = (uint32_t)(rec >> 29) & 0x1FFFu;
-  const uint32_t off = (uint32_t)rec & 0x1FFFFFFFu;
+  const uint32_t off = (uint32_t)rec & 0x7FFFu;
   const uint32_t b1 = (uint32_t)s_b1;
   // ---- kept slots of this block, in slot order, from offset `off`
   uint64_t msel[PL];
@@ -1443,6 +1459,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 }
 
 bool topk_row_pass(int32_t rows, int64_t n_max) {
+  const int32_t f = topk_variant_forced();
+  if (f == kTopkRow) return n_max <= kRowTopkMaxN;
+  if (f != kTopkAuto) return false;
   return rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN;
 }
 
@@ -1502,21 +1521,27 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     }
     CSA2_KERNEL(true, true, topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), lds, st,
                 scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp);
+    set_topk_last(kTopkRow);
     return hipGetLastError();
   }
+  // A variant forced by csa2_set_topk_variant runs when the pass allows it;
+  // otherwise the choice falls back to the shape's own.
+  const int32_t forced = topk_variant_forced();
   // Passes whose blocks can all be resident at once take the one-wait variant.
-  {
+  if (forced == kTopkAuto || forced == kTopkOneWait) {
     const int32_t nblk = topk_blocks(n_max, kTopkChunk);
     if (w.hist_copies <= 4 && nblk <= kCoopThreads &&
         (int64_t)rows * nblk <= coop_capacity()) {
       CSA2_KERNEL(true, true, topk_coop_kernel, dim3((unsigned)nblk, (unsigned)rows),
                   dim3(kCoopThreads), kCoopLds, st, scores, n, n_valid, nv_add, slot_pos, k,
-                  idx_out, count_out, w);
+                  idx_out, count_out, w, next_generation(), wait_limit());
+      set_topk_last(kTopkOneWait);
       return hipGetLastError();
     }
   }
   // many rows: bigger blocks (fewer, each with more scores)
-  const bool large = (int64_t)rows * topk_blocks(n_max, kTopkChunk) > 1024;
+  bool large = (int64_t)rows * topk_blocks(n_max, kTopkChunk) > 1024;
+  if (forced >= kTopkSelect && forced <= kTopkSelectLargeCut) large = forced >= kTopkSelectLarge;
   const int32_t chunk = large ? kTopkChunkLarge : kTopkChunk;
   const int32_t nblk = topk_blocks(n_max, chunk);
   // LDS of the completing block: radix bins, 2 offset arrays, the kept-slot
@@ -1539,7 +1564,12 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     lds_raised = true;
   }
   // many blocks per row: find each row's cut once instead of in every block
-  const bool use_cut = (int64_t)rows * nblk > 1024;
+  bool use_cut = (int64_t)rows * nblk > 1024;
+  if (forced >= kTopkSelect && forced <= kTopkSelectLargeCut)
+    use_cut = forced == kTopkSelectCut || forced == kTopkSelectLargeCut;
+  set_topk_last((large ? (use_cut ? kTopkSelectLargeCut : kTopkSelectLarge)
+                       : (use_cut ? kTopkSelectCut : kTopkSelect)) |
+                (bm_words == 0 ? kTopkListFinish : 0));
   if (use_cut)
     CSA2_KERNEL(true, false, topk_cut_kernel, dim3((unsigned)rows), dim3(kSelThreads), 0, st,
                 n_valid, nv_add, n, k, w);

@@ -40,8 +40,10 @@ def test_bytes_per_token(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.csa2_status_string(s)
+    assert b"gave up" in L.csa2_status_string(api.ERR_INCOMPLETE)
+    assert L.csa2_status_string(99) == b"unknown status"
     assert b"gfx950" in L.csa2_version()
 
 
@@ -155,3 +157,35 @@ def test_layer_step_rejects(L):
     # REUSE needs no index cache
     a.icache = api.Fp4Cache(None, None, 0, 0)
     assert L.csa2_workspace_bytes(2, ctypes.byref(a)) > 0
+
+
+def test_workspace_check_rejects(L):
+    """csa2_workspace_check validates before touching the device."""
+    f = L.csa2_workspace_check
+    ctl = L.csa2_workspace_control_bytes(4)
+    assert ctl > 0
+    assert f(None, ctl, 4, None) == 1                 # no workspace
+    assert f(FAKE, ctl, 0, None) == 2                 # rows < 1
+    assert f(FAKE, ctl - 1, 4, None) == 4             # smaller than the control block
+    assert b"control bytes" in L.csa2_last_error()
+    # the control block covers at most one pass of 256 rows
+    assert L.csa2_workspace_control_bytes(10_000) == L.csa2_workspace_control_bytes(256)
+
+
+def test_topk_variant_and_wait_limit_controls(L):
+    """The diagnostic setters return the previous value; an unknown variant
+    falls back to automatic choice."""
+    try:
+        assert api.set_topk_variant(api.TOPK_SELECT_CUT) == api.TOPK_AUTO
+        assert api.set_topk_variant(api.TOPK_ROW) == api.TOPK_SELECT_CUT
+        assert api.set_topk_variant(42) == api.TOPK_ROW
+        assert api.set_topk_variant(api.TOPK_AUTO) == api.TOPK_AUTO   # 42 was stored as AUTO
+        assert api.set_topk_variant(-3) == api.TOPK_AUTO
+    finally:
+        api.set_topk_variant(api.TOPK_AUTO)
+    try:
+        assert api.set_wait_limit(0) == 1 << 20
+        assert api.set_wait_limit(123) == 0
+    finally:
+        api.set_wait_limit(1 << 20)
+    assert api.topk_last_variant() == -1   # no Top-K pass ran on this thread

@@ -8,7 +8,7 @@ import torch
 from sparse_attention_decode_e2m1_amd import api
 from sparse_attention_decode_e2m1_amd import harness as Hn
 from sparse_attention_decode_e2m1_amd import inputs as I
-from tests.gpu_common import compare_group, host
+from tests.gpu_common import compare_group, expected_rows, host
 from tests.oracle_runner import run_group
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +20,8 @@ def test_group_decode_small():
     dw.step()
     torch.cuda.synchronize()
     ores, oc = run_group(w, keep_scores=True)
-    assert compare_group(w, dw, ores, oc) >= 3
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w) and chk.same_sets >= 3
 
 
 def test_group_reuse_layers_in_one_launch():
@@ -50,7 +51,8 @@ def test_group_pool_small():
     idx0 = set(host(dw.layers[0].idx_out)[0].tolist())
     assert idx0 <= set(host(dw.layers[0].pool_out)[0].tolist())
     ores, oc = run_group(w, keep_scores=True)
-    compare_group(w, dw, ores, oc)
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w) and chk.pools == 1
 
 
 def test_pool_larger_than_context_equals_flat():
@@ -74,7 +76,8 @@ def test_prefill_small():
     dw.step()
     torch.cuda.synchronize()
     ores, oc = run_group(w, keep_scores=True)
-    assert compare_group(w, dw, ores, oc) >= 32
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w) and chk.same_sets >= 32
 
 
 def test_reuse_and_reindex_reproduce_full_on_gpu():
@@ -126,7 +129,8 @@ def test_forty_layer_plan_small():
     dw.step()
     torch.cuda.synchronize()
     ores, oc = run_group(w, keep_scores=True)
-    assert compare_group(w, dw, ores, oc) >= 6
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w) and chk.same_sets >= 6
     ctl = dw.ws[: api.lib().csa2_workspace_control_bytes(dw.rows)].view(torch.int32)
     assert int(torch.count_nonzero(ctl)) == 0
 

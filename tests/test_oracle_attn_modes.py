@@ -228,3 +228,64 @@ def test_forty_layer_plan_and_window_only_layer(oracle):
     assert np.allclose(res[0].out[0], ref_o, rtol=1e-9, atol=1e-12)
     assert np.allclose(res[0].lse[0], ref_l, rtol=1e-9, atol=1e-12)
     assert (res[0].idx.size == 0) or (res[0].idx == -1).all()
+
+
+# ----------------------------------------------------------------- window rows
+def _window_positions_brute(S, pos0, p, W):
+    """Every array row (row r holds position pos0 + r) whose position is one
+    of the W most recent positions up to and including p."""
+    return [pos0 + r for r in range(S) if p - W < pos0 + r <= p]
+
+
+@pytest.mark.parametrize("W,T,pos0", [(128, 40, 1000), (128, 1, 0), (16, 200, 7), (1, 9, 3)])
+def test_window_rows_prefill_chunk_positions(oracle, W, T, pos0):
+    """A prefill chunk's window array holds S = W - 1 + T rows (the W - 1
+    positions before the chunk, then the chunk's own tokens): token i at
+    p = pos0 + W - 1 + i sees exactly positions [p - W + 1, p]."""
+    S = W - 1 + T
+    tagged = (pos0 + np.arange(S, dtype=np.int64))[:, None]  # each row carries its position
+    for i in range(T):
+        p = pos0 + W - 1 + i
+        got = oracle.window_rows(tagged, pos0, p, W)[:, 0].tolist()
+        assert got == _window_positions_brute(S, pos0, p, W) == list(range(p - W + 1, p + 1))
+        assert len(got) == W
+
+
+def test_window_rows_clipped_to_the_array(oracle):
+    """Positions outside the array are not invented: a query before the
+    array's first W positions sees fewer rows; one past its end sees only
+    rows still within its last W positions; W larger than S sees all."""
+    S, pos0 = 20, 100
+    tagged = (pos0 + np.arange(S, dtype=np.int64))[:, None]
+    for W in (1, 5, 20, 64):
+        for p in range(pos0 - 3, pos0 + S + 30):
+            got = oracle.window_rows(tagged, pos0, p, W)[:, 0].tolist()
+            assert got == _window_positions_brute(S, pos0, p, W), (W, p)
+    assert oracle.window_rows(tagged, pos0, pos0 - 1, 8).shape[0] == 0
+    assert oracle.window_rows(tagged, pos0, pos0 + S + 7, 8).shape[0] == 0
+
+
+def test_prefill_window_attention_equals_dense_over_brute_window(oracle):
+    """A window-only layer over a prefill chunk (S > W): each token's output is
+    dense attention over exactly the decoded rows of positions [p - W + 1, p]."""
+    from oracle.group import SeqGroup
+    w = I.small("t_swa_pre", 92, B=1, N=600, K=32, modes=(I.SWA,), W=16, T=24)
+    res = SeqGroup(w, 0).step()[0]
+    L = I.layer_inputs(w, 0, 0)
+    S = L.swa.shape[0]
+    assert S == w.W - 1 + w.T and L.swa_pos0 == w.N - S
+    dec = fp8_decode(L.swa.numpy()) * L.swa_scale
+    q = L.q.float().numpy()
+    for t in range(w.T):
+        p = w.ctx0 + t
+        pos = _window_positions_brute(S, L.swa_pos0, p, w.W)
+        assert len(pos) == w.W and pos[-1] == p
+        rows = dec[np.asarray(pos) - L.swa_pos0]
+        ref_o, ref_l = dense_attention(q[t], rows, w.sm_scale, w.DV)
+        assert np.allclose(res.out[t], ref_o, rtol=1e-9, atol=1e-12), t
+        assert np.allclose(res.lse[t], ref_l, rtol=1e-9, atol=1e-12), t
+    # an off-by-one (one row too many or too few) changes the result
+    p = w.ctx0 + 5
+    pos = _window_positions_brute(S, L.swa_pos0, p, w.W + 1)
+    wrong, _ = dense_attention(q[5], dec[np.asarray(pos) - L.swa_pos0], w.sm_scale, w.DV)
+    assert not np.allclose(res.out[5], wrong, rtol=1e-6, atol=1e-9)
