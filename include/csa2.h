@@ -348,6 +348,24 @@ size_t csa2_workspace_bytes(csa2_mode mode, const csa2_layer_args* a);
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* The layer step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It runs exactly the launches of csa2_layer_step, with the workspace taken
+ * from a static device array inside the library instead of an argument:
+ * CSA2_STATIC_SCRATCH_BYTES on every GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller still passes every input and
+ * output in `a`.  On the first call on a device the array's address is
+ * looked up and the array is zero-filled by a kernel on `stream` (again
+ * after a call that returned CSA2_ERR_HIP).  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that may overlap
+ * on one GPU (other host threads or streams) race and must be serialised by
+ * the caller.  Errors: those of csa2_layer_step, and CSA2_ERR_WORKSPACE when
+ * the step needs more than CSA2_STATIC_SCRATCH_BYTES (csa2_workspace_bytes
+ * gives the need; prefill chunks of thousands of tokens exceed it). */
+#define CSA2_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_layer_args* a, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Helpers. */
 /* Stored bytes per token of an FP4 row: dim/2 + dim/16 (324 for 576). */

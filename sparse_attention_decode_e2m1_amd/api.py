@@ -105,6 +105,7 @@ def lib():
             "csa2_profile_begin": (c_i32, []),
             "csa2_profile_end": (c_i32, [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]),
             "csa2_workspace_check": (c_i32, [c_p, c_sz, c_i32, c_p]),
+            "csa2_layer_step_static": (c_i32, [c_i32, ctypes.POINTER(LayerArgs), c_p]),
             "csa2_set_topk_variant": (c_i32, [c_i32]),
             "csa2_topk_last_variant": (c_i32, []),
             "csa2_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
@@ -293,6 +294,15 @@ def workspace_bytes(mode: int, args: LayerArgs) -> int:
 
 def layer_step(mode: int, args: LayerArgs, ws: torch.Tensor, stream=None):
     _check(lib().csa2_layer_step(mode, ctypes.byref(args), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def layer_step_static(mode: int, args: LayerArgs, stream=None):
+    """csa2_layer_step_static: the layer step with the library's static
+    scratch as its workspace (no allocation in the call)."""
+    _check(lib().csa2_layer_step_static(mode, ctypes.byref(args), _stream(stream)))
 
 
 PROFILE_KERNELS = ("quantize", "index_score", "topk_select", "sparse_attn", "pool_gather")

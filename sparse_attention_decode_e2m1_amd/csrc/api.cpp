@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -166,6 +167,48 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool attn_shape_ok(int32_t D, int32_t dv) { return (D == 576 && dv == 512) || (D == 128 && dv == 128); }
 
+}  // namespace
+
+// ------------------------------------------------------------ static scratch
+// Workspace of csa2_layer_step_static: one copy of this array per GPU,
+// held until the process ends.  Host code never uses the array's name as a
+// device address: the address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+namespace {
+constexpr size_t kStaticScratchBytes = CSA2_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+struct StaticScratch {
+  void* ptr = nullptr;  // device address of this GPU's copy
+  bool clean = false;   // control words known to be zero
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+StaticScratch g_scratch[kMaxDevices];
+
+// This device's scratch address; on first use (and after a call that failed
+// part-way) the whole array is zero-filled by a kernel on `st`.
+csa2_status static_scratch(hipStream_t st, int* dev_out, void** ptr_out) {
+  int dev = -1;
+  CSA2_TRY(hipGetDevice(&dev), "current device");
+  CSA2_REQUIRE(dev >= 0 && dev < kMaxDevices, CSA2_ERR_UNSUPPORTED, "device %d beyond %d", dev,
+               kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  StaticScratch& sc = g_scratch[dev];
+  if (!sc.ptr) {
+    void* p = nullptr;
+    CSA2_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "static scratch address");
+    CSA2_REQUIRE(p, CSA2_ERR_HIP, "static scratch address is NULL");
+    sc.ptr = p;
+  }
+  if (!sc.clean) {
+    CSA2_TRY(launch_fill_zero(sc.ptr, kStaticScratchBytes, st), "static scratch clear");
+    sc.clean = true;
+  }
+  *dev_out = dev;
+  *ptr_out = sc.ptr;
+  return CSA2_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -692,6 +735,27 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
              "sparse attention launch");
   }
   return CSA2_OK;
+}
+
+csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_layer_args* a, void* stream) {
+  g_last_error.clear();
+  csa2_status s = check_step(mode, a);
+  if (s) return s;
+  const size_t need = step_layout(mode, a, nullptr).bytes;
+  CSA2_REQUIRE(need <= kStaticScratchBytes, CSA2_ERR_WORKSPACE,
+               "this step needs %zu bytes of scratch, more than the static scratch's %zu; "
+               "call csa2_layer_step with a workspace instead",
+               need, kStaticScratchBytes);
+  int dev = -1;
+  void* ws = nullptr;
+  s = static_scratch(as_stream(stream), &dev, &ws);
+  if (s) return s;
+  s = csa2_layer_step(mode, a, ws, kStaticScratchBytes, stream);
+  if (s == CSA2_ERR_HIP) {  // launches may have stopped part-way: clear before the next use
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch[dev].clean = false;
+  }
+  return s;
 }
 
 }  // extern "C"
