@@ -680,7 +680,11 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
   const int32_t rows = a->B * a->T;
   const int32_t Weff = (a->S > 0) ? a->W : 0;
 
-  if (mode == CSA2_MODE_FULL)
+  // A decode step (one token per sequence, 1, 2 or 4 indexer heads) writes
+  // its new rows inside the scan launch; otherwise they are quantized first.
+  const bool fresh_in_scan =
+      mode == CSA2_MODE_FULL && fresh_rows_supported(false, a->T, a->H_I, a->D_I, a->D);
+  if (mode == CSA2_MODE_FULL && !fresh_in_scan)
     CSA2_LAUNCH(0, PROF_STREAM, launch_quantize_step(a->new_kv, a->new_ikey, a->new_dtype == CSA2_BF16, rows, a->T,
                                   a->q_pos, a->D, a->kv.cap, a->kv.codes, a->kv.scales, a->D_I,
                                   a->icache.cap, a->icache.codes, a->icache.scales, st),
@@ -702,10 +706,22 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       const int64_t n_max = pooled_in ? a->P_in : a->icache.cap;
       // one Top-K block per row (many rows, no pool kept): no score histogram
       const bool row = !(mode == CSA2_MODE_FULL && a->P > 0) && topk_row_pass(nr, n_max);
+      NewRows fresh;
+      if (fresh_in_scan) {
+        const size_t esz = a->new_dtype == CSA2_BF16 ? 2 : 4;
+        fresh.kv = static_cast<const char*>(a->new_kv) + (size_t)r0 * a->D * esz;
+        fresh.ikey = static_cast<const char*>(a->new_ikey) + (size_t)r0 * a->D_I * esz;
+        fresh.bf16 = a->new_dtype == CSA2_BF16;
+        fresh.q_pos = qpos;
+        fresh.kv_codes = a->kv.codes;
+        fresh.kv_scales = a->kv.scales;
+        fresh.kv_cap = a->kv.cap;
+        fresh.kv_dim = a->D;
+      }
       CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
                                   qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
                                   L.scores, L.n_out, row ? nullptr : L.tw.hist, L.tw.hist_stride,
-                                  L.tw.hist_copies, st, r0),
+                                  L.tw.hist_copies, st, r0, fresh_in_scan ? &fresh : nullptr),
                "index score launch");
       int32_t* idx = a->idx_out + (size_t)r0 * a->K;
       if (mode == CSA2_MODE_FULL && a->P > 0) {

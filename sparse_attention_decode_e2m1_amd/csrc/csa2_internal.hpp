@@ -112,12 +112,31 @@ hipError_t launch_rope_quantize(const void* x, bool bf16, int64_t rows, int32_t 
                                 int64_t stride, int32_t rope_dim, const float* cos_sin,
                                 const int64_t* dst_rows, uint8_t* codes, uint8_t* scales,
                                 hipStream_t st);
+// A Full layer's new rows in a decode step (one query token per sequence):
+// row r of kv / ikey goes to cache row (r / T) * cap + q_pos[r] of the main
+// and index caches.  The decode scan writes them itself (one extra block per
+// query row, which also scores the new position), so the step needs no
+// separate quantize-on-write launch.
+struct NewRows {
+  const void* kv = nullptr;    // [rows][kv_dim]
+  const void* ikey = nullptr;  // [rows][DI]
+  bool bf16 = false;
+  const int32_t* q_pos = nullptr;
+  uint8_t* kv_codes = nullptr;
+  uint8_t* kv_scales = nullptr;
+  int64_t kv_cap = 0;
+  int32_t kv_dim = 0;
+};
+// Shapes whose new rows the decode scan writes itself (otherwise a separate
+// quantize-on-write launch comes first).
+bool fresh_rows_supported(bool pool, int32_t T, int32_t HI, int32_t DI, int32_t kv_dim);
 hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32_t DI,
                               int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
                               const float* w, int32_t HI, const int32_t* n_valid,
                               int32_t nv_add, const int32_t* pool, int32_t P, int64_t n_max,
                               float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
-                              int32_t hist_copies, hipStream_t st, int32_t row0 = 0);
+                              int32_t hist_copies, hipStream_t st, int32_t row0 = 0,
+                              const NewRows* fresh = nullptr);
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
                             int32_t hist_copies, hipStream_t st, bool first = true);

@@ -31,6 +31,7 @@
 
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
+#include "csa2_quant.hpp"
 
 namespace csa2 {
 
@@ -40,6 +41,165 @@ __device__ __forceinline__ f16x2 scale_pair2(uint32_t word) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
 }
 
+// A Full layer's decode step writes its new rows inside the scan launch
+// (1, 2 or 4 indexer heads, H_I * D_I <= 512, D/16 + D_I/16 <= 64): wave 3 of
+// the first block of query row r quantizes them into both caches (lane j <
+// D/16 takes block j of the main-KV row, the next D_I/16 lanes the index
+// key's blocks; exactly as the quantize-on-write kernels do) and scores the
+// new position p = q_pos[r] from the index key it has just quantized.  No
+// block of the launch reads a cache row while it is being written: every
+// block of the row scans positions [0, p).  The wave issues these loads
+// first, ahead of its scan loads, uses them once its query is in, and never
+// waits on the rest of its block.  The score is sum_h w_h * max(0, q_h . k)
+// with the bf16 query and the exact dequantized key, summed in fp32; it
+// joins the row's histogram.
+
+// Raw registers of that wave between its loads and their use: nothing
+// consumes them before its scan loads are issued, so no wait sits between.
+struct FreshRegs {
+  uint4 raw[4];  // this lane's 16-channel block: 64 bytes (f32) or 32 (bf16)
+  uint32_t q[4]; // H_I*D_I/128 words of the query row [H_I][D_I] (bf16)
+  float wq;      // ... and the weight of the head those words belong to
+};
+constexpr int kFreshWave = 3;
+
+// Sixteen input elements from raw registers, as floats.
+template <typename In>
+__device__ __forceinline__ void raw16(const uint4 (&raw)[4], float (&v)[16]);
+template <>
+__device__ __forceinline__ void raw16<float>(const uint4 (&raw)[4], float (&v)[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[4 * k] = __uint_as_float(raw[k].x);
+    v[4 * k + 1] = __uint_as_float(raw[k].y);
+    v[4 * k + 2] = __uint_as_float(raw[k].z);
+    v[4 * k + 3] = __uint_as_float(raw[k].w);
+  }
+}
+template <>
+__device__ __forceinline__ void raw16<uint16_t>(const uint4 (&raw)[4], float (&v)[16]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * k + 2 * j] = bf16_to_f32(wd[j] & 0xFFFFu);
+      v[8 * k + 2 * j + 1] = bf16_to_f32(wd[j] >> 16);
+    }
+  }
+}
+
+// Loads only, for the whole wave (lanes past the blocks reload the last one,
+// and the query words past the row its last word; those registers go unused).
+template <typename In>
+__device__ __forceinline__ void fresh_load(const NewRows& nw, int r, int32_t DI,
+                                           const uint16_t* __restrict__ q_idx,
+                                           const float* __restrict__ w, int32_t HI,
+                                           FreshRegs& f) {
+  const int lane = threadIdx.x & 63;
+  constexpr int NW = (int)(16 * sizeof(In) / 16);  // 16-byte words of a block
+  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
+  const In* src = (lane < nkv)
+                      ? static_cast<const In*>(nw.kv) + (int64_t)r * nw.kv_dim + 16 * lane
+                      : static_cast<const In*>(nw.ikey) + (int64_t)r * DI +
+                            16 * min(lane - nkv, nix - 1);
+#pragma unroll
+  for (int k = 0; k < NW; ++k) f.raw[k] = reinterpret_cast<const uint4*>(src)[k];
+  const int nwq = (HI * DI) >> 7;  // 32-bit query words per lane (<= 4)
+  const int last = ((HI * DI) >> 1) - 1;
+  const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q_idx + (int64_t)r * HI * DI);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) f.q[m] = qrow[min(lane * nwq + m, last)];
+  f.wq = w[(int64_t)r * HI + lane / (64 / HI)];
+}
+
+// What the wave stores once its scan's loads are all issued (stores share
+// the load counter, so stores issued earlier would hold up its waits for the
+// scan's later loads): this lane's block of codes and its scale, and the
+// new position's score.
+struct FreshOut {
+  uint32_t lo, hi;  // 16 codes
+  uint32_t sb;      // scale byte
+  float sc;         // score (lane 0)
+};
+
+template <typename In>
+__device__ FreshOut fresh_compute(const NewRows& nw, int64_t p, int64_t cap, int32_t DI,
+                                  int32_t HI, int64_t nv, const FreshRegs& f) {
+  __shared__ float kdeq[512];  // dequantized new index key (DI <= 512), this wave's only
+  const int lane = threadIdx.x & 63;
+  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
+  const bool ix_lane = lane >= nkv && lane < nkv + nix;
+  FreshOut o{0u, 0u, 0u, 0.0f};
+  if (lane < nkv + nix) {
+    float v[16];
+    raw16<In>(f.raw, v);
+    uint8_t code8[8];
+    uint8_t sb;
+    quantize_values(v, code8, &sb);
+    o.lo = *reinterpret_cast<const uint32_t*>(code8);
+    o.hi = *reinterpret_cast<const uint32_t*>(code8 + 4);
+    o.sb = sb;
+    if (ix_lane) {  // exact values: grid(code) * e4m3(scale)
+      const int j = lane - nkv;
+      const float s = e4m3_pos(sb);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint32_t nib = (code8[c >> 1] >> (4 * (c & 1))) & 0xFu;
+        const uint32_t mg = nib & 7u;  // E2M1 magnitude code: 0, .5, 1, 1.5, 2, 3, 4, 6
+        // mantissa bit over exponent bits (bias 1): 0.5 * mg below 2, else (1 + m/2) 2^(e-1)
+        const float m = (mg < 2u ? 0.5f * (float)mg
+                                 : (1.0f + 0.5f * (float)(mg & 1u)) * (float)(1u << ((mg >> 1) - 1u))) * s;
+        kdeq[16 * j + c] = (nib & 8u) ? -m : m;
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the key's values are in LDS
+  // lane l holds query elements [l*E, (l+1)*E) of [HI][DI], E = HI*DI/64:
+  // one head per group of 64/HI lanes
+  const int nwq = (HI * DI) >> 7, G = 64 / HI;
+  const int c0 = (lane * 2 * nwq) % DI;
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (m < nwq) {
+      acc += bf16_to_f32(f.q[m] & 0xFFFFu) * kdeq[c0 + 2 * m];
+      acc += bf16_to_f32(f.q[m] >> 16) * kdeq[c0 + 2 * m + 1];
+    }
+  for (int m = G >> 1; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+  const float term = f.wq * fmaxf(acc, 0.0f);  // every lane of a group holds its head's term
+  for (int h = 0; h < HI; ++h) o.sc += __shfl(term, h * G, kWave);
+  (void)p; (void)cap; (void)nv;
+  return o;
+}
+
+__device__ __forceinline__ void fresh_store(const NewRows& nw, int64_t p, int b,
+                                            uint8_t* __restrict__ icodes,
+                                            uint8_t* __restrict__ iscales, int64_t cap,
+                                            int32_t DI, int64_t nv, float* __restrict__ srow,
+                                            uint32_t* __restrict__ hist, const FreshOut& o) {
+  const int lane = threadIdx.x & 63;
+  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
+  const uint64_t codes8 = ((uint64_t)o.hi << 32) | o.lo;
+  if (lane < nkv) {
+    if (p >= 0 && p < nw.kv_cap) {
+      const int64_t dr = (int64_t)b * nw.kv_cap + p;
+      *reinterpret_cast<uint64_t*>(nw.kv_codes + dr * (nw.kv_dim >> 1) + 8 * lane) = codes8;
+      nw.kv_scales[dr * nkv + lane] = (uint8_t)o.sb;
+    }
+  } else if (lane < nkv + nix && p >= 0 && p < cap) {
+    const int j = lane - nkv;
+    const int64_t dr = (int64_t)b * cap + p;
+    *reinterpret_cast<uint64_t*>(icodes + dr * (DI >> 1) + 8 * j) = codes8;
+    iscales[dr * nix + j] = (uint8_t)o.sb;
+  }
+  if (lane == 0 && p >= 0 && p < cap && p < nv) {  // the position is visible to this row
+    srow[p] = o.sc;
+    if (hist) atomicAdd(hist + (score_key(o.sc) >> kHistShift), 1u);
+  }
+}
+
 template <int NCH, int TPA, int GT, bool POOL>  // 128-channel chunks, tiles per accumulator,
                                                 // tiles per group, positions from a pool list
 __global__ __launch_bounds__(256) void index_score_kernel(
@@ -47,7 +207,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, int32_t HI, int32_t T,
     const int32_t* __restrict__ n_valid, const int32_t* __restrict__ pool, int32_t P,
     int32_t nv_add, float* __restrict__ scores, int64_t n_out, uint32_t* __restrict__ hist,
-    int64_t hist_stride, int32_t hist_copies, int32_t chunk, int32_t row0) {
+    int64_t hist_stride, int32_t hist_copies, int32_t chunk, int32_t row0, NewRows fresh) {
   constexpr int DI = 128 * NCH;
   constexpr int ROWB = DI / 2;    // code bytes per row
   constexpr int ROWS = DI / 16;   // scale bytes per row
@@ -60,9 +220,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int r = blockIdx.y;
   const int b = (row0 + r) / T;
   // visible entries, clamped to what the score row and the key list hold
-  const int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), POOL ? (int64_t)P : cap);
+  int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), POOL ? (int64_t)P : cap);
+  const bool fresh_on = !POOL && fresh.ikey;
+  const int64_t nv_all = nv;  // the new position counts as visible to the fresh score
+  // the new position (loaded once: later loads queue behind the scan's)
+  const int64_t p_new = fresh_on ? (int64_t)fresh.q_pos[r] : -1;
+  if (fresh_on) nv = min(nv, max(p_new, (int64_t)0));  // scanned: [0, q_pos)
   const int64_t start = (int64_t)blockIdx.x * chunk;
-  if (start >= nv) return;  // uniform for the whole block
+  // blocks past the scanned range still take their part of the new rows
+  if (start >= nv && !(fresh_on && blockIdx.x == 0)) return;  // uniform for the whole block
   const int64_t end = min(nv, start + chunk);
 
   // the wave index is uniform: kept in a scalar register, the whole-group
@@ -131,6 +297,13 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   uint32_t swA[GT][NCH], swB[GT][NCH];
   // the first group is requested before the query is prepared, so the
   // scan's first HBM round trip overlaps the query's
+  // the new rows' loads go first, ahead of this wave's scan loads
+  const bool fresh_wave = fresh_on && blockIdx.x == 0 && wave == kFreshWave;  // wave-uniform
+  FreshRegs fr;
+  if (fresh_wave) {
+    if (fresh.bf16) fresh_load<uint16_t>(fresh, r, DI, q_idx, w, HI, fr);
+    else fresh_load<float>(fresh, r, DI, q_idx, w, HI, fr);
+  }
   if (nrounds > 0) {
     if (whole) load_group(std::false_type{}, 0, cwA, swA);
     else load_group(std::true_type{}, 0, cwA, swA);
@@ -184,6 +357,22 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   }
   const int my_slot = g / GPS;
   const bool owner = (g % GPS) == 0;
+  // the new rows (one wave of the row's first block), once the wave's loads
+  // and its query are in; stored after its scan
+  FreshOut fo{0u, 0u, 0u, 0.0f};
+  if (fresh_wave) {
+    if (fresh.bf16) fo = fresh_compute<uint16_t>(fresh, p_new, cap, DI, HI, nv_all, fr);
+    else fo = fresh_compute<float>(fresh, p_new, cap, DI, HI, nv_all, fr);
+  }
+  auto fresh_done = [&]() {
+    if (fresh_wave)
+      fresh_store(fresh, p_new, b, const_cast<uint8_t*>(codes), const_cast<uint8_t*>(scales), cap,
+                  DI, nv_all, srow, hist ? hist + (int64_t)r * hist_stride : nullptr, fo);
+  };
+  if (fresh_on && start >= nv) {
+    fresh_done();
+    return;
+  }
   if (hist) __syncthreads();
 
   auto compute_group = [&](int rnd, const u32x4 (&cw)[GT][NCH], const uint32_t (&sw)[GT][NCH]) {
@@ -239,6 +428,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       compute_group(rnd + 1, cwB, swB);
     }
   }
+  fresh_done();
   if (hist) {
     __syncthreads();
     uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
@@ -407,13 +597,22 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
   }
 }
 
+bool fresh_rows_supported(bool pool, int32_t T, int32_t HI, int32_t DI, int32_t kv_dim) {
+  return !pool && T == 1 && (HI == 1 || HI == 2 || HI == 4) && HI * DI <= 512 && kv_dim > 0 &&
+         kv_dim % 16 == 0 && kv_dim / 16 + DI / 16 <= 64;
+}
+
 hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32_t DI,
                               int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
                               const float* w, int32_t HI, const int32_t* n_valid,
                               int32_t nv_add, const int32_t* pool, int32_t P, int64_t n_max,
                               float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
-                              int32_t hist_copies, hipStream_t st, int32_t row0) {
+                              int32_t hist_copies, hipStream_t st, int32_t row0,
+                              const NewRows* fresh) {
   if (n_max <= 0 || rows == 0) return hipSuccess;
+  const NewRows nw = fresh ? *fresh : NewRows{};
+  if (nw.ikey && !fresh_rows_supported(pool != nullptr, T, HI, DI, nw.kv_dim))
+    return hipErrorInvalidValue;
   // Prefill chunks (32 or more tokens per sequence, whole waves of one
   // sequence, 128-channel keys) take the tokens x positions kernel; the Top-K histogram is then
   // built from the written scores.
@@ -436,11 +635,11 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
     if (pool)                                                                                  \
       CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT, true>), grid, block, 0, st,    \
                   codes, scales, cap, q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, \
-                  hist, hist_stride, hist_copies, chunk, row0);                                \
+                  hist, hist_stride, hist_copies, chunk, row0, nw);                            \
     else                                                                                       \
       CSA2_KERNEL(true, true, (index_score_kernel<NCH, TPA, GT, false>), grid, block, 0, st,   \
                   codes, scales, cap, q_idx, w, HI, T, n_valid, pool, P, nv_add, scores, n_out, \
-                  hist, hist_stride, hist_copies, chunk, row0);                                \
+                  hist, hist_stride, hist_copies, chunk, row0, nw);                            \
   } while (0)
   switch (DI / 128) {
     case 1:

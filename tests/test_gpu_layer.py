@@ -5,6 +5,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from sparse_attention_decode_e2m1_amd import api
 from sparse_attention_decode_e2m1_amd import harness as Hn
 from sparse_attention_decode_e2m1_amd import inputs as I
@@ -134,3 +136,41 @@ def test_forty_layer_plan_small():
     ctl = dw.ws[: api.lib().csa2_workspace_control_bytes(dw.rows)].view(torch.int32)
     assert int(torch.count_nonzero(ctl)) == 0
 
+
+
+@pytest.mark.parametrize("new_dtype", ["f32", "bf16"])
+def test_full_decode_writes_and_scores_the_new_rows(new_dtype):
+    """A Full decode step writes its new rows inside the scan launch: the
+    written rows equal the oracle's quantization of the new rows bit for bit,
+    and the layer's score row (left in the workspace: it follows the control
+    block) equals the oracle's indexer scores at every visible position,
+    the new one included, within the fp32 accumulation bound."""
+    w = I.small("t_fresh", 68, B=3, N=7000, K=256, modes=(I.FULL,))
+    dw = Hn.DeviceWorkload(w)
+    if new_dtype == "bf16":
+        dw.new_kv = dw.new_kv.to(torch.bfloat16)
+        dw.new_ikey = dw.new_ikey.to(torch.bfloat16)
+        dw._args = [dw._layer_args(0, 0)]
+    dw.step()
+    torch.cuda.synchronize()
+    kvc, kvs, ixc, ixs = (host(t) for t in dw.caches[0])
+    p = w.N - 1
+    nkv = dw.new_kv.float().cpu().numpy()
+    nik = dw.new_ikey.float().cpu().numpy()
+    off = api.lib().csa2_workspace_control_bytes(w.B)
+    sc = host(dw.ws[off: off + w.B * w.N * 4].view(torch.float32).view(w.B, w.N))
+    L = dw.layers[0]
+    for b in range(w.B):
+        c, s = oracle.quantize(nkv[b:b + 1])
+        assert np.array_equal(kvc[b, p], c[0]) and np.array_equal(kvs[b, p], s[0]), b
+        c, s = oracle.quantize(nik[b:b + 1])
+        assert np.array_equal(ixc[b, p], c[0]) and np.array_equal(ixs[b, p], s[0]), b
+        q = L.q_idx[b].float().cpu().numpy()
+        wi = L.w_idx[b].cpu().numpy()
+        rows = np.arange(w.N, dtype=np.int64)
+        o = oracle.index_scores(ixc[b], ixs[b], q, wi, rows)
+        k = oracle.dequant(ixc[b], ixs[b])
+        bound = (np.abs(k) @ np.abs(q.astype(np.float64)).T * np.abs(wi.astype(np.float64))).sum(1)
+        err = np.abs(sc[b] - o)
+        assert (err <= 1e-5 * bound + 1e-30).all(), (b, int(err.argmax()), err.max())
+        assert abs(sc[b, p] - o[p]) <= 1e-5 * bound[p] + 1e-30
