@@ -55,24 +55,88 @@ def kv_bytes_per_query(w) -> dict:
 
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle (as it stands) on one sequence of the workload, repeated
-    for about `budget_s` seconds on this host's cores."""
+    for about `budget_s` seconds on all of this host's cores, then for about
+    `budget_s` / 2 seconds on one core."""
     import oracle
     from oracle.group import SeqGroup
     oracle.lib()
     t_set = time.perf_counter()
     g = SeqGroup(w, 0)
     setup = time.perf_counter() - t_set
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        g.step()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
-            break
-    return {"value": n / el, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"sequence 0 of {w.B}, {n} full group steps ({len(w.modes)} layers), "
-                      f"{el:.1f} s (set-up {setup:.1f} s untimed)"}
+
+    def run(budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            g.step()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n >= 50:
+                return n, el
+
+    cores = oracle.num_threads()
+    n, el = run(budget_s)
+    oracle.set_num_threads(1)
+    n1, el1 = run(budget_s / 2)
+    oracle.set_num_threads(cores)
+    return {"value": n / el, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "single_thread": {"value": n1 / el1, "unit": "queries/s", "cores": 1},
+            "sample": f"sequence 0 of {w.B}, {n} full group steps ({len(w.modes)} layers) in "
+                      f"{el:.1f} s on {cores} threads, {n1} in {el1:.1f} s on 1 thread "
+                      f"(set-up {setup:.1f} s untimed)"}
+
+
+def stream_read_peak(nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """The library's plain streaming-read kernel over `nbytes` (beyond the
+    256 MB last-level cache), HIP events around `reps` launches, for a few
+    grid sizes; the best rate is the measured HBM read reference."""
+    import torch
+    from sparse_attention_decode_e2m1_amd import api
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best, per = 0.0, {}
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        api.stream_read(src, sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            api.stream_read(src, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        per[str(blocks)] = round(gbps, 1)
+        best = max(best, gbps)
+    del src
+    return {"GBps": round(best, 1), "bytes": nbytes, "by_blocks": per,
+            "kernel": "stream_read_kernel (csa2_stream_read)"}
+
+
+def hierarchical_recall(w, dw) -> list:
+    """For a workload whose Full layer keeps a pool: recall of each later
+    indexing layer's Top-K (searched inside the pool) against the same layer
+    searching the whole context (the workload with no pool), per layer, mean
+    over query rows."""
+    import dataclasses
+
+    import torch
+    from sparse_attention_decode_e2m1_amd import harness
+    from sparse_attention_decode_e2m1_amd import inputs as I
+    flat = harness.DeviceWorkload(dataclasses.replace(w, P=0), copies=1)
+    flat.step()
+    dw.step(copy=0)
+    torch.cuda.synchronize()
+    out = []
+    for li, m in enumerate(w.modes):
+        if m != I.REINDEX:
+            continue
+        h = dw.layers[li].idx_out.cpu().numpy()
+        f = flat.layers[li].idx_out.cpu().numpy()
+        rec = [len(set(h[r][h[r] >= 0]) & set(f[r][f[r] >= 0])) / max(1, int((f[r] >= 0).sum()))
+               for r in range(h.shape[0])]
+        out.append({"layer": li, "recall": round(float(sum(rec) / len(rec)), 4)})
+    del flat
+    return out
 
 
 def time_rope_quantize(rows: int, reps: int = 50) -> dict:
@@ -182,7 +246,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="skip the instrumented passes (roofline, per-layer, warm, stream peak)")
     ap.add_argument("--rope-quantize-rows", type=int, default=0,
                     help="only time the fused rotary + quantize-on-write of this many bf16 rows "
                          "(576 channels, 64 rotary) against the plain quantize-on-write, and exit")
@@ -258,6 +323,34 @@ def main():
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} queries/s, {kv_gbps:.0f} GB/s",
           file=sys.stderr, flush=True)
 
+    # ---- warm steps (one cache copy, so the index cache stays in the
+    # last-level cache between steps), and per-layer time (events on the
+    # launch stream between the layers of each step)
+    warm_ms = None
+    layer_us = None
+    if not args.no_profile:
+        for _ in range(3):
+            dw.step(copy=0)
+        torch.cuda.synchronize()
+        t4 = time.perf_counter()
+        for _ in range(args.steps):
+            dw.step(copy=0)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t4) * 1e3 / args.steps
+        nl = len(dw.layers)
+        acc = [0.0] * nl
+        for k in range(args.steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
+            ev[0].record()
+            for li in range(nl):
+                dw.run_layer(li, copy=k % args.copies)
+                ev[li + 1].record()
+            torch.cuda.synchronize()
+            for li in range(nl):
+                acc[li] += ev[li].elapsed_time(ev[li + 1])
+        layer_us = [{"layer": li, "mode": I.MODE_NAMES[w.modes[li]],
+                     "us": round(acc[li] * 1e3 / args.steps, 2)} for li in range(nl)]
+
     # ---- instrumented pass: HIP events around every launch, same steps
     roofline = None
     prof = None
@@ -288,6 +381,16 @@ def main():
                 for k, (c, t) in prof.items()}
         prof["instrumented_ms_per_step"] = round((t3 - t2) * 1e3 / args.steps, 4)
 
+    stream = None
+    recall = None
+    if not args.no_profile:
+        stream = stream_read_peak()
+        if roofline is not None:
+            roofline["measured_read_peak_GBps"] = stream["GBps"]
+            roofline["frac_of_measured_peak"] = round(roofline["achieved"] / stream["GBps"], 4)
+        if w.P > 0 and w.T == 1:
+            recall = hierarchical_recall(w, dw)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline ...", file=sys.stderr, flush=True)
@@ -310,6 +413,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": prof,
+        "per_layer_us": layer_us,
+        "warm_ms_per_step": None if warm_ms is None else round(warm_ms, 4),
+        "stream_read_peak": stream,
+        "hierarchical_recall_vs_flat": recall,
     }
     print(json.dumps(line), flush=True)
 

@@ -396,6 +396,15 @@ csa2_status csa2_profile_end(int32_t* counts, double* total_ms);
 size_t csa2_layer_args_size(void);
 size_t csa2_fp4_cache_size(void);
 
+/* Measurement reference: a plain streaming read of `bytes` (a multiple of
+ * 16) at `src` by `blocks` blocks of 256 threads (16-byte non-temporal
+ * loads), each block writing one folded word to sink[block] so that no load
+ * can be dropped.  Its rate is the achievable HBM read bandwidth the hot
+ * path's streaming kernels are compared with.  Errors: NULL pointers, bytes
+ * not a positive multiple of 16, blocks outside [1, 2^20]. */
+csa2_status csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             void* stream);
+
 /* Reports whether a one-wait launch on this workspace gave up waiting
  * (see the Top-K variants above and csa2_sparse_attn_one_launch).  Waits
  * for `stream`, reads the wait-failure flags of the control words of

@@ -66,6 +66,7 @@ def lib():
         L.csa2o_sparse_attn.argtypes = [P, i32, i32, i32, P, P, P, i32, P, f64, i32, f64, P, P]
         L.csa2o_sparse_attn.restype = None
         L.csa2o_num_threads.argtypes, L.csa2o_num_threads.restype = [], i32
+        L.csa2o_set_num_threads.argtypes, L.csa2o_set_num_threads.restype = [i32], None
         _lib = L
     return _lib
 
@@ -76,6 +77,11 @@ def _p(a: np.ndarray):
 
 def num_threads() -> int:
     return int(lib().csa2o_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (timing only)."""
+    lib().csa2o_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- codec

@@ -237,3 +237,11 @@ int32_t csa2o_num_threads(void) {
   return 1;
 #endif
 }
+
+void csa2o_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads((int)n);
+#else
+  (void)n;
+#endif
+}

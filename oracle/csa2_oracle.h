@@ -80,6 +80,8 @@ void csa2o_sparse_attn(const float* q, int32_t H, int32_t D, int32_t dv,
 
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int32_t csa2o_num_threads(void);
+/* Threads for the oracle's later parallel loops (n >= 1). */
+void csa2o_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }

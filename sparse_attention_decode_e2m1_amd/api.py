@@ -106,6 +106,7 @@ def lib():
             "csa2_profile_end": (c_i32, [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]),
             "csa2_workspace_check": (c_i32, [c_p, c_sz, c_i32, c_p]),
             "csa2_layer_step_static": (c_i32, [c_i32, ctypes.POINTER(LayerArgs), c_p]),
+            "csa2_stream_read": (c_i32, [c_p, c_sz, c_p, c_i32, c_p]),
             "csa2_set_topk_variant": (c_i32, [c_i32]),
             "csa2_topk_last_variant": (c_i32, []),
             "csa2_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
@@ -325,6 +326,12 @@ def workspace_check(ws: torch.Tensor, rows: int, stream=None):
     """csa2_workspace_check: raises Csa2Error (status ERR_INCOMPLETE) if a
     one-wait launch on this workspace gave up waiting."""
     _check(lib().csa2_workspace_check(_ptr(ws), ws.numel(), rows, _stream(stream)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, blocks: int, stream=None):
+    """csa2_stream_read: a plain streaming read of src (the HBM reference)."""
+    _check(lib().csa2_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), blocks,
+                                  _stream(stream)))
 
 
 def set_topk_variant(variant: int) -> int:

@@ -309,6 +309,16 @@ csa2_status csa2_workspace_check(void* ws, size_t ws_bytes, int32_t rows, void* 
               nbad, first);
 }
 
+csa2_status csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                             void* stream) {
+  g_last_error.clear();
+  CSA2_REQUIRE(src && sink, CSA2_ERR_NULL, "src and sink are required");
+  CSA2_REQUIRE(bytes >= 16 && bytes % 16 == 0, CSA2_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  CSA2_REQUIRE(blocks >= 1 && blocks <= (1 << 20), CSA2_ERR_SHAPE, "blocks must be in [1, 2^20]");
+  CSA2_TRY(launch_stream_read(src, (int64_t)bytes, sink, blocks, as_stream(stream)), "stream read launch");
+  return CSA2_OK;
+}
+
 int32_t csa2_set_topk_variant(int32_t variant) {
   if (variant < kTopkAuto || variant >= kTopkVariants) variant = kTopkAuto;
   return g_topk_forced.exchange(variant);
@@ -730,11 +740,14 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
                                     pcount, L.tw, st),
                  "pool select launch");
+        // the pool's scores gathered into a dense row (with the histogram its
+        // selection starts from, unless it takes one block per row)
+        const bool prow = topk_row_pass(nr, a->P);
         CSA2_LAUNCH(4, PROF_STREAM, launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
-                                      L.tw.hist, L.tw.hist_stride, L.tw.hist_copies, st),
+                                      prow ? nullptr : L.tw.hist, L.tw.hist_stride, L.tw.hist_copies, st),
                  "pool gather launch");
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
-                                    nullptr, L.tw, st),
+                                    nullptr, L.tw, st, prow),
                  "top-k select launch");
       } else {
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,

@@ -9,7 +9,8 @@
 
 namespace csa2 {
 
-constexpr int32_t kScoreChunk = 2048;  // positions per scoring block
+constexpr int32_t kScoreChunk = 2048;  // positions per scoring block (fewer when the scan is small)
+constexpr int64_t kScanMinBlocks = 512; // ... so that a scan has at least this many blocks
 constexpr int kScoreGroup = 4;         // consecutive 16-position tiles per wave load
 constexpr int32_t kTopkChunk = 4096;        // scores per select block (4 per thread)
 constexpr int32_t kTopkChunkLarge = 16384;  // ... when a pass has many rows (16 per thread)
@@ -140,11 +141,13 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
                             int32_t hist_copies, hipStream_t st, bool first = true);
-// Passes of at least kRowTopkMinRows rows of at most kRowTopkMaxN slots can
-// select with one block per row (topk_row_pass); that path reads no score
-// histogram, so a caller that takes it (row_ok = true) builds none.
+// Passes of at least kRowTopkMinRows rows of at most kRowTopkMaxN slots, and
+// passes of any number of rows of at most kRowTopkSmallN slots, select with
+// one block per row (topk_row_pass); that path reads no score histogram, so
+// a caller that takes it (row_ok = true) builds none.
 constexpr int32_t kRowTopkMinRows = 64;
 constexpr int64_t kRowTopkMaxN = 262144;
+constexpr int64_t kRowTopkSmallN = 65536;
 bool topk_row_pass(int32_t rows, int64_t n_max);
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
@@ -170,6 +173,8 @@ hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* p
                                 uint32_t* hist, int64_t hist_stride, int32_t hist_copies,
                                 hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks,
+                              hipStream_t st);
 // Quantize-on-write of one decode/prefill step: rows r of x1 (dim1) and x2
 // (dim2) go to cache row (r / T) * cap + q_pos[r] of their planes.
 hipError_t launch_quantize_step(const void* x1, const void* x2, bool bf16, int32_t rows,

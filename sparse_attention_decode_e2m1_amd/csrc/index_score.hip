@@ -627,7 +627,11 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
     return launch_topk_hist(scores, rows, n_out, n_valid, nv_add, n_max, hist, hist_stride,
                             hist_copies, st, false);
   }
-  const int32_t chunk = kScoreChunk;
+  // 2048 positions per block, halved (down to 64) until the launch has at
+  // least two blocks per compute unit: a 16K-slot pool or a 4K context would
+  // otherwise scan with a handful of blocks
+  int32_t chunk = kScoreChunk;
+  while (chunk > 64 && ((n_max + chunk - 1) / chunk) * rows < kScanMinBlocks) chunk >>= 1;
   const int64_t nchunks = (n_max + chunk - 1) / chunk;
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
 #define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \

@@ -20,7 +20,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 // Scores of the pool members (slots s < count[r]) gathered into a dense row,
-// with the 12-bit key histogram the Top-K select pass starts from.
+// with the 12-bit key histogram the Top-K select pass starts from (none when
+// hist is null: the one-block-per-row selection needs none).
 __global__ __launch_bounds__(256) void gather_scores_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ pool, int32_t P,
     const int32_t* __restrict__ count, float* __restrict__ out, uint32_t* __restrict__ hist,
@@ -31,8 +32,10 @@ __global__ __launch_bounds__(256) void gather_scores_kernel(
   const int32_t start = blockIdx.x * 4096;
   if (start >= c) return;
   const int32_t end = min(c, start + 4096);
-  for (int k = threadIdx.x; k < kHistBins; k += 256) lhist[k] = 0u;
-  __syncthreads();
+  if (hist) {
+    for (int k = threadIdx.x; k < kHistBins; k += 256) lhist[k] = 0u;
+    __syncthreads();
+  }
   const float* srow = scores + (int64_t)r * n;
   const int32_t* prow = pool + (int64_t)r * P;
   float* orow = out + (int64_t)r * P;
@@ -48,13 +51,52 @@ __global__ __launch_bounds__(256) void gather_scores_kernel(
     const int32_t s = start + u * 256 + threadIdx.x;
     if (s < end) {
       orow[s] = v[u];
-      atomicAdd(&lhist[score_key(v[u]) >> kHistShift], 1u);
+      if (hist) atomicAdd(&lhist[score_key(v[u]) >> kHistShift], 1u);
     }
   }
+  if (!hist) return;
   __syncthreads();
   uint32_t* gh = hist + (int64_t)r * hist_stride + (blockIdx.x % hist_copies) * kHistBins;
   for (int k = threadIdx.x; k < kHistBins; k += 256)
     if (lhist[k]) atomicAdd(gh + k, lhist[k]);
+}
+
+// A plain streaming read of `words16` 16-byte words, the reference for the
+// achievable HBM read rate: each thread reads 8 words per step with
+// non-temporal loads (all requested before any is used) and folds them into
+// one word; one word per block goes to `sink` so nothing can be dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                          int64_t words16,
+                                                          uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  uint32_t acc = 0u;
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < words16; base += stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_nontemporal_load(src + min(base + (int64_t)u * 256, words16 - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  __shared__ uint32_t red[4];
+  acc ^= __shfl_xor(acc, 1, kWave);
+  acc ^= __shfl_xor(acc, 2, kWave);
+  acc ^= __shfl_xor(acc, 4, kWave);
+  acc ^= __shfl_xor(acc, 8, kWave);
+  acc ^= __shfl_xor(acc, 16, kWave);
+  acc ^= __shfl_xor(acc, 32, kWave);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks,
+                              hipStream_t st) {
+  if (bytes < 16 || blocks < 1) return hipSuccess;
+  CSA2_KERNEL(true, true, stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+              static_cast<const u32x4*>(src), bytes / 16, sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* pool, int32_t P,

@@ -25,6 +25,9 @@
 // (Merging in the same launch, with the splits exchanging partials through
 // device-coherent memory, measured slower on MI355X than the kernel boundary:
 // partials written by one XCD and read by another make a slow round trip.)
+#include <mutex>
+#include <vector>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -136,16 +139,14 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     return (WIN || a.K == 0) ? 0 : a.idx[(int64_t)r * a.K + min(e, a.K - 1)];
   };
   int ix = load_ix(e0);
-  uint32_t rq[NM][8];
+  // the query row (16 heads x D bf16), loaded once by the whole block: each
+  // thread takes QPT of its 16-byte words (the last clamped)
+  constexpr int QW = 16 * D / 8, QPT = (QW + 255) / 256;
+  uint4 qraw[QPT];
   {
-    const uint16_t* qr = a.q + ((int64_t)r * 16 + i) * D;
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t)r * 16 * D);
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g);
-      const uint4 c = *reinterpret_cast<const uint4*>(qr + 64 * m + 16 * g + 8);
-      rq[m][0] = u.x; rq[m][1] = u.y; rq[m][2] = u.z; rq[m][3] = u.w;
-      rq[m][4] = c.x; rq[m][5] = c.y; rq[m][6] = c.z; rq[m][7] = c.w;
-    }
+    for (int k = 0; k < QPT; ++k) qraw[k] = qsrc[min(tid + 256 * k, QW - 1)];
   }
   uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
   bool valid;
@@ -217,35 +218,61 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   // otherwise sink them below it, after the query has arrived)
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- query fragments (head i), scaled per head into fp16 range
+  // ---- query fragments (head i), scaled per head into fp16 range.  The
+  // block converts the row once: each head's largest magnitude (LDS max over
+  // the threads holding its words), then every value as fp16 times the
+  // head's power of two into an LDS copy of the row (in the V tile's space,
+  // which is written only after every wave holds its fragments); lane (i, g)
+  // then reads head i's channels 64m + 16g + [0, 16).
   f16x8 qa[NM][2];
-  int qexp;
+  int er[4];
   {
-    float amax = 0.0f;
+    constexpr int WPH = D / 8;      // 16-byte words per head
+    constexpr int QST = D + 8;      // fp16 row stride: the 16 heads' reads spread over banks
+    __shared__ uint32_t s_qmax[16];
+    _Float16* q16 = Vs;             // [16][QST], aliases the V tile
+    static_assert(16 * QST <= 64 * vs_stride<DV>(), "query copy fits the V tile");
+    if (tid < 16) s_qmax[tid] = 0u;
+    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int k = 0; k < QPT; ++k) {
+      const int j = tid + 256 * k;
+      if (j < QW) {
+        const uint32_t wd[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+        float am = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32(rq[m][j] & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(rq[m][j] >> 16)));
+        for (int t = 0; t < 4; ++t)
+          am = fmaxf(am, fmaxf(fabsf(bf16_to_f32(wd[t] & 0xFFFFu)), fabsf(bf16_to_f32(wd[t] >> 16))));
+        atomicMax(&s_qmax[j / WPH], __float_as_uint(am));  // non-negative: ordered as integers
       }
-    amax = fmaxf(amax, shfl_xor(amax, 16));
-    amax = fmaxf(amax, shfl_xor(amax, 32));
-    qexp = fp16_exponent_for(amax);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int j = tid + 256 * k;
+      if (j < QW) {
+        const int h = j / WPH, c0 = (j % WPH) * 8;
+        const int e = fp16_exponent_for(__uint_as_float(s_qmax[h]));
+        const uint32_t wd[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+        f16x8 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] = (_Float16)ldexpf(bf16_to_f32(wd[t] & 0xFFFFu), e);
+          v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(wd[t] >> 16), e);
+        }
+        *reinterpret_cast<f16x8*>(q16 + h * QST + c0) = v;
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
+        qa[m][hf] = *reinterpret_cast<const f16x8*>(q16 + i * QST + 64 * m + 16 * g + 8 * hf);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t wd = rq[m][4 * hf + j];
-          qa[m][hf][2 * j] = (_Float16)ldexpf(bf16_to_f32(wd & 0xFFFFu), qexp);
-          qa[m][hf][2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(wd >> 16), qexp);
-        }
+    for (int rr = 0; rr < 4; ++rr) er[rr] = fp16_exponent_for(__uint_as_float(s_qmax[4 * g + rr]));
+    __syncthreads();  // every wave holds its fragments: the V tile may be written
   }
-  int er[4];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) er[rr] = __shfl(qexp, 4 * g + rr, kWave);
   const float lscale = a.sm_scale * wscale;
 
   // running softmax state of head i (every lane of the block holds its
@@ -579,19 +606,32 @@ size_t attn_lds_bytes(int32_t dv) {
   return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
 }
 
-// Blocks of the split kernel that fit on the device at once.
+// Blocks of a split kernel instantiation that fit on the current device at
+// once: cached per (kernel, LDS size, device), since every instantiation
+// has the same function type.
 template <typename F>
 static int64_t resident_blocks(F kernel, size_t lds) {
-  static int64_t cached = -1;
-  if (cached < 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess)
-      return 0;
-    cached = (int64_t)cus * per_cu;
+  struct Entry {
+    const void* k;
+    size_t lds;
+    int dev;
+    int64_t blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.k == (const void*)kernel && e.lds == lds && e.dev == dev) return e.blocks;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
   }
-  return cached;
+  cache.push_back({(const void*)kernel, lds, dev, (int64_t)cus * per_cu});
+  return cache.back().blocks;
 }
 
 // Launches the one-launch kernel if its grid fits the device at once

@@ -1462,7 +1462,7 @@ bool topk_row_pass(int32_t rows, int64_t n_max) {
   const int32_t f = topk_variant_forced();
   if (f == kTopkRow) return n_max <= kRowTopkMaxN;
   if (f != kTopkAuto) return false;
-  return rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN;
+  return (rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN) || n_max <= kRowTopkSmallN;
 }
 
 static int32_t topk_blocks(int64_t n_max, int32_t chunk) {

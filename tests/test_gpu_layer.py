@@ -174,3 +174,34 @@ def test_full_decode_writes_and_scores_the_new_rows(new_dtype):
         err = np.abs(sc[b] - o)
         assert (err <= 1e-5 * bound + 1e-30).all(), (b, int(err.argmax()), err.max())
         assert abs(sc[b, p] - o[p]) <= 1e-5 * bound[p] + 1e-30
+
+
+def test_cache_save_and_reload_reproduces_the_step(tmp_path):
+    """Checkpoint and resume of the persistent global cache (helmcode.com/
+    deepseek-v41-flash, section "05 · cache hierarchy": the global KV is kept
+    for later reuse): the FP4 planes of both caches are written to files and
+    read back into a fresh set of caches (zeroed first).  Every layer that
+    reads them -- Reindex scoring and selection, Reuse attention -- gives
+    bit-identical indices, outputs and lse."""
+    w = I.small("t_ckpt", 69, B=2, N=20000, K=512, modes=(I.FULL, I.REINDEX, I.REUSE))
+    a = Hn.DeviceWorkload(w)
+    a.step()
+    torch.cuda.synchronize()
+    names = ("kv_codes", "kv_scales", "ix_codes", "ix_scales")
+    for n, t in zip(names, a.caches[0]):
+        np.save(tmp_path / f"{n}.npy", host(t))
+    b = Hn.DeviceWorkload(w)
+    for t in b.caches[0]:
+        t.zero_()
+    for n, t in zip(names, b.caches[0]):
+        t.copy_(torch.from_numpy(np.load(tmp_path / f"{n}.npy")))
+    for li in (1, 2):  # Reindex and Reuse read only the reloaded caches
+        b.run_layer(li)
+    torch.cuda.synchronize()
+    for x, y in zip(a.caches[0], b.caches[0]):
+        assert torch.equal(x, y)
+    for li in (1, 2):
+        La, Lb = a.layers[li], b.layers[li]
+        if La.mode == I.REINDEX:
+            assert torch.equal(La.idx_out, Lb.idx_out), li
+        assert torch.equal(La.out, Lb.out) and torch.equal(La.lse, Lb.lse), li
