@@ -147,7 +147,7 @@ hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const 
 // a caller that takes it (row_ok = true) builds none.
 constexpr int32_t kRowTopkMinRows = 64;
 constexpr int64_t kRowTopkMaxN = 262144;
-constexpr int64_t kRowTopkSmallN = 65536;
+constexpr int64_t kRowTopkSmallN = 16384;
 bool topk_row_pass(int32_t rows, int64_t n_max);
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
