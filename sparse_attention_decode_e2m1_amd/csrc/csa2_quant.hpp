@@ -21,21 +21,26 @@ __device__ __forceinline__ float e4m3_pos(int b) {
 
 // Scale byte = E4M3 value nearest to amax/6, ties to the even mantissa,
 // saturating at 448.  Threshold b lies halfway between bytes b and b+1,
-// times 6: 3*(v_b + v_{b+1}) has at most 8 significant bits, so it is exact.
-// The byte is the number of thresholds amax passes (a tie passes when the
-// upper neighbour b+1 has an even mantissa).
+// times 6: 3*(v_b + v_{b+1}) has at most 8 significant bits, so it is exact;
+// amax passes it when above it, or on it when byte b+1 has an even mantissa.
+__device__ __forceinline__ bool scale_passes(float amax, int b) {
+  const float t = 3.0f * (e4m3_pos(b) + e4m3_pos(b + 1));
+  return amax > t || (amax == t && ((b + 1) & 1) == 0);
+}
+// The hardware conversion rounds the fp32 quotient amax/6 to its nearest
+// E4M3 byte.  Every halfway point between E4M3 values is an fp32 number and
+// rounding to fp32 is monotone, so the quotient never crosses one; it can
+// only land on one, where the conversion's tie may pick the neighbour of the
+// exact answer.  One comparison with the exact threshold on each side of
+// the converted byte therefore gives the byte of the exact amax/6.
 __device__ __forceinline__ int scale_byte(float amax) {
-  int lo = 0, hi = 126;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const float t = 3.0f * (e4m3_pos(mid) + e4m3_pos(mid + 1));
-    const bool pass = amax > t || (amax == t && ((mid + 1) & 1) == 0);
-    if (pass)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return lo;
+  const float qt = fminf(amax / 6.0f, 448.0f);
+  int b = min(__builtin_amdgcn_cvt_pk_fp8_f32(qt, 0.0f, 0, false) & 0x7F, 126);
+  if (b < 126 && scale_passes(amax, b))
+    ++b;
+  else if (b > 0 && !scale_passes(amax, b - 1))
+    --b;
+  return b;
 }
 
 // E2M1 magnitude code of |x| under scale s: nearest of {0,.5,1,1.5,2,3,4,6}*s
@@ -83,6 +88,34 @@ __device__ __forceinline__ void quantize_values(const float (&v)[16], uint8_t* c
   }
   *reinterpret_cast<uint64_t*>(code_dst) = packed;
   *scale_dst = (uint8_t)sb;
+}
+
+// E2M1 magnitude code to its grid value (0, .5, 1, 1.5, 2, 3, 4, 6):
+// mantissa bit over exponent bits (bias 1).
+__device__ __forceinline__ float e2m1_grid(uint32_t mg) {
+  return mg < 2u ? 0.5f * (float)mg : (1.0f + 0.5f * (float)(mg & 1u)) * (float)(1u << ((mg >> 1) - 1u));
+}
+
+// Element-parallel quantisation by one wave: each row of 16 lanes holds one
+// 16-channel block (lane e holds channel e of it).  Every lane gets its
+// exact dequantized value; lanes e = 0 and e = 8 get the 32-bit words of
+// codes for channels 0..7 and 8..15 of their block, and every lane the
+// block's scale byte.  Same codes and scale as quantize_values.
+__device__ __forceinline__ void quantize_lane(float x, float* deq, uint32_t* word, uint32_t* sb) {
+  const int e = threadIdx.x & 15;
+  const float a = fabsf(x);
+  const int b = scale_byte(row16_max(a));
+  const float s = e4m3_pos(b);
+  const uint32_t mg = e2m1_mag(a, s);
+  const uint32_t code = ((__float_as_uint(x) >> 31) << 3) | mg;
+  const float m = e2m1_grid(mg) * s;
+  *deq = (code & 8u) ? -m : m;
+  uint32_t v = code << (4 * (e & 7));
+  v |= __shfl_xor(v, 1, 64);
+  v |= __shfl_xor(v, 2, 64);
+  v |= __shfl_xor(v, 4, 64);
+  *word = v;
+  *sb = (uint32_t)b;
 }
 
 // Quantize one 16-channel block read from memory.

@@ -42,159 +42,141 @@ __device__ __forceinline__ f16x2 scale_pair2(uint32_t word) {
 }
 
 // A Full layer's decode step writes its new rows inside the scan launch
-// (1, 2 or 4 indexer heads, H_I * D_I <= 512, D/16 + D_I/16 <= 64): wave 3 of
-// the first block of query row r quantizes them into both caches (lane j <
-// D/16 takes block j of the main-KV row, the next D_I/16 lanes the index
-// key's blocks; exactly as the quantize-on-write kernels do) and scores the
-// new position p = q_pos[r] from the index key it has just quantized.  No
-// block of the launch reads a cache row while it is being written: every
-// block of the row scans positions [0, p).  The wave issues these loads
-// first, ahead of its scan loads, uses them once its query is in, and never
-// waits on the rest of its block.  The score is sum_h w_h * max(0, q_h . k)
-// with the bf16 query and the exact dequantized key, summed in fp32; it
-// joins the row's histogram.
-
-// Raw registers of that wave between its loads and their use: nothing
-// consumes them before its scan loads are issued, so no wait sits between.
-struct FreshRegs {
-  uint4 raw[4];  // this lane's 16-channel block: 64 bytes (f32) or 32 (bf16)
-  uint32_t q[4]; // H_I*D_I/128 words of the query row [H_I][D_I] (bf16)
-  float wq;      // ... and the weight of the head those words belong to
-};
+// (128-channel index keys, 1, 2 or 4 indexer heads): the last wave of some
+// of the query row's blocks quantizes them, one element per lane (exactly
+// as the quantize-on-write kernels do).  The first block's wave takes the
+// index key (two passes of 64 channels) and scores the new position p =
+// q_pos[r] from the key it has just quantized; pass j of the main-KV row
+// (64 channels) goes to block (1 + j) mod (the row's blocks).  No block of
+// the launch reads a cache row while it is being written: every block of
+// the row scans positions [0, p).  A wave issues these loads first, ahead
+// of its scan loads, computes once its query is in, stores after its scan
+// (stores share the load counter and would hold up its later waits), and
+// never waits on the rest of its block.  The score is
+// sum_h w_h * max(0, q_h . k) with the bf16 query and the exact dequantized
+// key, summed in fp32; it joins the row's histogram.
 constexpr int kFreshWave = 3;
+constexpr int kFreshMaxKvPasses = 2;  // main-KV passes a block's wave keeps in registers
 
-// Sixteen input elements from raw registers, as floats.
+struct FreshRegs {
+  uint32_t xk[2];                  // index key channels lane, 64 + lane (raw f32 / bf16 bits)
+  uint32_t q[4];                   // head h's channel pair (2 lane, 2 lane + 1), bf16
+  float wq;                        // lane h < H_I: weight of head h
+  uint32_t xv[kFreshMaxKvPasses];  // main-KV channel 64 j + lane of this block's passes j
+};
+struct FreshOut {
+  uint32_t kw[2], ks[2];           // index key: code words and scale bytes of the two passes
+  uint32_t vw[kFreshMaxKvPasses], vs[kFreshMaxKvPasses];  // main KV, per pass
+  float sc;                        // score (lane 0)
+};
+
 template <typename In>
-__device__ __forceinline__ void raw16(const uint4 (&raw)[4], float (&v)[16]);
-template <>
-__device__ __forceinline__ void raw16<float>(const uint4 (&raw)[4], float (&v)[16]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[4 * k] = __uint_as_float(raw[k].x);
-    v[4 * k + 1] = __uint_as_float(raw[k].y);
-    v[4 * k + 2] = __uint_as_float(raw[k].z);
-    v[4 * k + 3] = __uint_as_float(raw[k].w);
-  }
+__device__ __forceinline__ uint32_t raw_elem(const void* base, int64_t i) {
+  if constexpr (sizeof(In) == 4) return static_cast<const uint32_t*>(base)[i];
+  else return (uint32_t) static_cast<const uint16_t*>(base)[i];
 }
-template <>
-__device__ __forceinline__ void raw16<uint16_t>(const uint4 (&raw)[4], float (&v)[16]) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * k + 2 * j] = bf16_to_f32(wd[j] & 0xFFFFu);
-      v[8 * k + 2 * j + 1] = bf16_to_f32(wd[j] >> 16);
-    }
-  }
+template <typename In>
+__device__ __forceinline__ float raw_value(uint32_t v) {
+  if constexpr (sizeof(In) == 4) return __uint_as_float(v);
+  else return bf16_to_f32(v);
 }
 
-// Loads only, for the whole wave (lanes past the blocks reload the last one,
-// and the query words past the row its last word; those registers go unused).
+// pass j of the main-KV row belongs to block (1 + j) % nblk; the k-th of
+// this block's passes (k < kFreshMaxKvPasses) is j = blk - 1 + k * nblk
+__device__ __forceinline__ int fresh_kv_pass(int blk, int nblk, int k) {
+  return (blk == 0 ? nblk - 1 : blk - 1) + k * nblk;
+}
+
+// Loads only (every branch is wave-uniform; lanes read in-range addresses).
 template <typename In>
-__device__ __forceinline__ void fresh_load(const NewRows& nw, int r, int32_t DI,
+__device__ __forceinline__ void fresh_load(const NewRows& nw, int r, int32_t HI,
                                            const uint16_t* __restrict__ q_idx,
-                                           const float* __restrict__ w, int32_t HI,
+                                           const float* __restrict__ w, bool index_part,
                                            FreshRegs& f) {
   const int lane = threadIdx.x & 63;
-  constexpr int NW = (int)(16 * sizeof(In) / 16);  // 16-byte words of a block
-  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
-  const In* src = (lane < nkv)
-                      ? static_cast<const In*>(nw.kv) + (int64_t)r * nw.kv_dim + 16 * lane
-                      : static_cast<const In*>(nw.ikey) + (int64_t)r * DI +
-                            16 * min(lane - nkv, nix - 1);
+  if (index_part) {
+    const void* ik = static_cast<const In*>(nw.ikey) + (int64_t)r * 128;
+    f.xk[0] = raw_elem<In>(ik, lane);
+    f.xk[1] = raw_elem<In>(ik, 64 + lane);
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q_idx + (int64_t)r * HI * 128);
 #pragma unroll
-  for (int k = 0; k < NW; ++k) f.raw[k] = reinterpret_cast<const uint4*>(src)[k];
-  const int nwq = (HI * DI) >> 7;  // 32-bit query words per lane (<= 4)
-  const int last = ((HI * DI) >> 1) - 1;
-  const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q_idx + (int64_t)r * HI * DI);
+    for (int h = 0; h < 4; ++h) f.q[h] = qrow[min(h, HI - 1) * 64 + lane];
+    f.wq = w[(int64_t)r * HI + min(lane, HI - 1)];
+  }
+  const void* kv = static_cast<const In*>(nw.kv) + (int64_t)r * nw.kv_dim;
+  const int npass = nw.kv_dim >> 6;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) f.q[m] = qrow[min(lane * nwq + m, last)];
-  f.wq = w[(int64_t)r * HI + lane / (64 / HI)];
+  for (int k = 0; k < kFreshMaxKvPasses; ++k) {
+    const int j = fresh_kv_pass(blockIdx.x, gridDim.x, k);
+    f.xv[k] = raw_elem<In>(kv, min(64 * j, 64 * (npass - 1)) + lane);
+  }
 }
 
-// What the wave stores once its scan's loads are all issued (stores share
-// the load counter, so stores issued earlier would hold up its waits for the
-// scan's later loads): this lane's block of codes and its scale, and the
-// new position's score.
-struct FreshOut {
-  uint32_t lo, hi;  // 16 codes
-  uint32_t sb;      // scale byte
-  float sc;         // score (lane 0)
-};
-
 template <typename In>
-__device__ FreshOut fresh_compute(const NewRows& nw, int64_t p, int64_t cap, int32_t DI,
-                                  int32_t HI, int64_t nv, const FreshRegs& f) {
-  __shared__ float kdeq[512];  // dequantized new index key (DI <= 512), this wave's only
+__device__ FreshOut fresh_compute(const NewRows& nw, int32_t HI, bool index_part,
+                                  const FreshRegs& f) {
+  __shared__ float kdeq[128];  // the new index key's exact values (this wave's only)
   const int lane = threadIdx.x & 63;
-  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
-  const bool ix_lane = lane >= nkv && lane < nkv + nix;
-  FreshOut o{0u, 0u, 0u, 0.0f};
-  if (lane < nkv + nix) {
-    float v[16];
-    raw16<In>(f.raw, v);
-    uint8_t code8[8];
-    uint8_t sb;
-    quantize_values(v, code8, &sb);
-    o.lo = *reinterpret_cast<const uint32_t*>(code8);
-    o.hi = *reinterpret_cast<const uint32_t*>(code8 + 4);
-    o.sb = sb;
-    if (ix_lane) {  // exact values: grid(code) * e4m3(scale)
-      const int j = lane - nkv;
-      const float s = e4m3_pos(sb);
+  FreshOut o{};
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const uint32_t nib = (code8[c >> 1] >> (4 * (c & 1))) & 0xFu;
-        const uint32_t mg = nib & 7u;  // E2M1 magnitude code: 0, .5, 1, 1.5, 2, 3, 4, 6
-        // mantissa bit over exponent bits (bias 1): 0.5 * mg below 2, else (1 + m/2) 2^(e-1)
-        const float m = (mg < 2u ? 0.5f * (float)mg
-                                 : (1.0f + 0.5f * (float)(mg & 1u)) * (float)(1u << ((mg >> 1) - 1u))) * s;
-        kdeq[16 * j + c] = (nib & 8u) ? -m : m;
-      }
-    }
+  for (int k = 0; k < kFreshMaxKvPasses; ++k) {
+    float d;
+    quantize_lane(raw_value<In>(f.xv[k]), &d, &o.vw[k], &o.vs[k]);
+  }
+  if (!index_part) return o;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float d;
+    quantize_lane(raw_value<In>(f.xk[p]), &d, &o.kw[p], &o.ks[p]);
+    kdeq[64 * p + lane] = d;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the key's values are in LDS
-  // lane l holds query elements [l*E, (l+1)*E) of [HI][DI], E = HI*DI/64:
-  // one head per group of 64/HI lanes
-  const int nwq = (HI * DI) >> 7, G = 64 / HI;
-  const int c0 = (lane * 2 * nwq) % DI;
-  float acc = 0.0f;
+  const float k0 = kdeq[2 * lane], k1 = kdeq[2 * lane + 1];
+  float sc = 0.0f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    if (m < nwq) {
-      acc += bf16_to_f32(f.q[m] & 0xFFFFu) * kdeq[c0 + 2 * m];
-      acc += bf16_to_f32(f.q[m] >> 16) * kdeq[c0 + 2 * m + 1];
-    }
-  for (int m = G >> 1; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
-  const float term = f.wq * fmaxf(acc, 0.0f);  // every lane of a group holds its head's term
-  for (int h = 0; h < HI; ++h) o.sc += __shfl(term, h * G, kWave);
-  (void)p; (void)cap; (void)nv;
+  for (int h = 0; h < 4; ++h) {
+    if (h >= HI) break;
+    float acc = bf16_to_f32(f.q[h] & 0xFFFFu) * k0 + bf16_to_f32(f.q[h] >> 16) * k1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+    sc += __shfl(f.wq, h, kWave) * fmaxf(acc, 0.0f);
+  }
+  o.sc = sc;
   return o;
 }
 
 __device__ __forceinline__ void fresh_store(const NewRows& nw, int64_t p, int b,
                                             uint8_t* __restrict__ icodes,
                                             uint8_t* __restrict__ iscales, int64_t cap,
-                                            int32_t DI, int64_t nv, float* __restrict__ srow,
-                                            uint32_t* __restrict__ hist, const FreshOut& o) {
-  const int lane = threadIdx.x & 63;
-  const int nkv = nw.kv_dim >> 4, nix = DI >> 4;
-  const uint64_t codes8 = ((uint64_t)o.hi << 32) | o.lo;
-  if (lane < nkv) {
-    if (p >= 0 && p < nw.kv_cap) {
-      const int64_t dr = (int64_t)b * nw.kv_cap + p;
-      *reinterpret_cast<uint64_t*>(nw.kv_codes + dr * (nw.kv_dim >> 1) + 8 * lane) = codes8;
-      nw.kv_scales[dr * nkv + lane] = (uint8_t)o.sb;
+                                            int64_t nv, float* __restrict__ srow,
+                                            uint32_t* __restrict__ hist, bool index_part,
+                                            const FreshOut& o) {
+  const int lane = threadIdx.x & 63, e = lane & 15;
+  const int npass = nw.kv_dim >> 6;
+  // lane e == 0 / 8 of each 16-lane row holds a code word, e == 0 the scale
+  if (p >= 0 && p < nw.kv_cap) {
+    const int64_t dr = (int64_t)b * nw.kv_cap + p;
+#pragma unroll
+    for (int k = 0; k < kFreshMaxKvPasses; ++k) {
+      const int j = fresh_kv_pass(blockIdx.x, gridDim.x, k);
+      if (j < npass) {
+        const int c = 64 * j + lane;  // this lane's channel
+        if ((e & 7) == 0)
+          *reinterpret_cast<uint32_t*>(nw.kv_codes + dr * (nw.kv_dim >> 1) + (c >> 1)) = o.vw[k];
+        if (e == 0) nw.kv_scales[dr * (nw.kv_dim >> 4) + (c >> 4)] = (uint8_t)o.vs[k];
+      }
     }
-  } else if (lane < nkv + nix && p >= 0 && p < cap) {
-    const int j = lane - nkv;
-    const int64_t dr = (int64_t)b * cap + p;
-    *reinterpret_cast<uint64_t*>(icodes + dr * (DI >> 1) + 8 * j) = codes8;
-    iscales[dr * nix + j] = (uint8_t)o.sb;
   }
-  if (lane == 0 && p >= 0 && p < cap && p < nv) {  // the position is visible to this row
+  if (!index_part || p < 0 || p >= cap) return;
+  const int64_t dr = (int64_t)b * cap + p;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = 64 * q + lane;
+    if ((e & 7) == 0) *reinterpret_cast<uint32_t*>(icodes + dr * 64 + (c >> 1)) = o.kw[q];
+    if (e == 0) iscales[dr * 8 + (c >> 4)] = (uint8_t)o.ks[q];
+  }
+  if (lane == 0 && p < nv) {  // the position is visible to this row
     srow[p] = o.sc;
     if (hist) atomicAdd(hist + (score_key(o.sc) >> kHistShift), 1u);
   }
@@ -228,7 +210,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   if (fresh_on) nv = min(nv, max(p_new, (int64_t)0));  // scanned: [0, q_pos)
   const int64_t start = (int64_t)blockIdx.x * chunk;
   // blocks past the scanned range still take their part of the new rows
-  if (start >= nv && !(fresh_on && blockIdx.x == 0)) return;  // uniform for the whole block
+  if (start >= nv && !(fresh_on && (int)blockIdx.x <= (fresh.kv_dim >> 6)))
+    return;  // uniform for the whole block
   const int64_t end = min(nv, start + chunk);
 
   // the wave index is uniform: kept in a scalar register, the whole-group
@@ -298,11 +281,13 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // the first group is requested before the query is prepared, so the
   // scan's first HBM round trip overlaps the query's
   // the new rows' loads go first, ahead of this wave's scan loads
-  const bool fresh_wave = fresh_on && blockIdx.x == 0 && wave == kFreshWave;  // wave-uniform
+  const bool fresh_wave = fresh_on && wave == kFreshWave &&
+                          (blockIdx.x == 0 || (int)blockIdx.x <= (fresh.kv_dim >> 6));  // wave-uniform
+  const bool idx_part = fresh_on && blockIdx.x == 0;
   FreshRegs fr;
   if (fresh_wave) {
-    if (fresh.bf16) fresh_load<uint16_t>(fresh, r, DI, q_idx, w, HI, fr);
-    else fresh_load<float>(fresh, r, DI, q_idx, w, HI, fr);
+    if (fresh.bf16) fresh_load<uint16_t>(fresh, r, HI, q_idx, w, idx_part, fr);
+    else fresh_load<float>(fresh, r, HI, q_idx, w, idx_part, fr);
   }
   if (nrounds > 0) {
     if (whole) load_group(std::false_type{}, 0, cwA, swA);
@@ -359,15 +344,15 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const bool owner = (g % GPS) == 0;
   // the new rows (one wave of the row's first block), once the wave's loads
   // and its query are in; stored after its scan
-  FreshOut fo{0u, 0u, 0u, 0.0f};
+  FreshOut fo{};
   if (fresh_wave) {
-    if (fresh.bf16) fo = fresh_compute<uint16_t>(fresh, p_new, cap, DI, HI, nv_all, fr);
-    else fo = fresh_compute<float>(fresh, p_new, cap, DI, HI, nv_all, fr);
+    if (fresh.bf16) fo = fresh_compute<uint16_t>(fresh, HI, idx_part, fr);
+    else fo = fresh_compute<float>(fresh, HI, idx_part, fr);
   }
   auto fresh_done = [&]() {
     if (fresh_wave)
       fresh_store(fresh, p_new, b, const_cast<uint8_t*>(codes), const_cast<uint8_t*>(scales), cap,
-                  DI, nv_all, srow, hist ? hist + (int64_t)r * hist_stride : nullptr, fo);
+                  nv_all, srow, hist ? hist + (int64_t)r * hist_stride : nullptr, idx_part, fo);
   };
   if (fresh_on && start >= nv) {
     fresh_done();
@@ -598,8 +583,8 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
 }
 
 bool fresh_rows_supported(bool pool, int32_t T, int32_t HI, int32_t DI, int32_t kv_dim) {
-  return !pool && T == 1 && (HI == 1 || HI == 2 || HI == 4) && HI * DI <= 512 && kv_dim > 0 &&
-         kv_dim % 16 == 0 && kv_dim / 16 + DI / 16 <= 64;
+  return !pool && T == 1 && (HI == 1 || HI == 2 || HI == 4) && DI == 128 && kv_dim > 0 &&
+         kv_dim % 64 == 0;
 }
 
 hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32_t DI,
@@ -632,7 +617,10 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   // otherwise scan with a handful of blocks
   int32_t chunk = kScoreChunk;
   while (chunk > 64 && ((n_max + chunk - 1) / chunk) * rows < kScanMinBlocks) chunk >>= 1;
-  const int64_t nchunks = (n_max + chunk - 1) / chunk;
+  int64_t nchunks = (n_max + chunk - 1) / chunk;
+  // every 64-channel pass of a new main-KV row needs a block of its row
+  if (nw.ikey)
+    nchunks = std::max<int64_t>(nchunks, ((nw.kv_dim >> 6) + kFreshMaxKvPasses - 1) / kFreshMaxKvPasses);
   const dim3 grid((unsigned)nchunks, (unsigned)rows), block(256);
 #define CSA2_IS_LAUNCH(NCH, TPA, GT)                                                           \
   do {                                                                                         \

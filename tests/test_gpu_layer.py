@@ -138,19 +138,50 @@ def test_forty_layer_plan_small():
 
 
 
-@pytest.mark.parametrize("new_dtype", ["f32", "bf16"])
+def _edge_rows(rows, dim, seed):
+    """Rows whose 16-channel blocks sit on rounding boundaries: blocks with
+    amax exactly on a scale threshold (6 x the halfway point between E4M3
+    neighbours, or an fp32 neighbour of it) and blocks whose elements lie
+    exactly on the E2M1 halfway points of an E4M3 scale."""
+    rng = np.random.default_rng(seed)
+    e4 = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mids = (e4[:-1] + e4[1:]) / 2
+    t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    x = np.zeros((rows, dim), np.float32)
+    for r in range(rows):
+        for k in range(dim // 16):
+            n = seed + r * (dim // 16) + k
+            blk = np.empty(16, np.float32)
+            if n % 2 == 0:
+                j = (n // 2 * 5) % 126
+                blk[:] = rng.standard_normal(16) * 0.1 * mids[j]
+                a = np.float32(6 * mids[j])
+                a = [a, np.nextafter(a, np.float32(np.inf)), np.nextafter(a, np.float32(0))][n % 3]
+                blk[rng.integers(16)] = a if n % 4 else -a
+            else:
+                s = e4[(n * 11) % 127]
+                blk[:] = np.concatenate([t, -t])[rng.permutation(16)] * s
+            x[r, 16 * k:16 * k + 16] = blk
+    return x
+
+
+@pytest.mark.parametrize("new_dtype", ["f32", "bf16", "f32_edges"])
 def test_full_decode_writes_and_scores_the_new_rows(new_dtype):
     """A Full decode step writes its new rows inside the scan launch: the
     written rows equal the oracle's quantization of the new rows bit for bit,
     and the layer's score row (left in the workspace: it follows the control
     block) equals the oracle's indexer scores at every visible position,
-    the new one included, within the fp32 accumulation bound."""
+    the new one included, within the fp32 accumulation bound.  The edge
+    variant puts every block of the new rows on a rounding boundary."""
     w = I.small("t_fresh", 68, B=3, N=7000, K=256, modes=(I.FULL,))
     dw = Hn.DeviceWorkload(w)
     if new_dtype == "bf16":
         dw.new_kv = dw.new_kv.to(torch.bfloat16)
         dw.new_ikey = dw.new_ikey.to(torch.bfloat16)
         dw._args = [dw._layer_args(0, 0)]
+    elif new_dtype == "f32_edges":
+        dw.new_kv.copy_(torch.from_numpy(_edge_rows(w.B, dw.new_kv.shape[-1], 3)).view_as(dw.new_kv))
+        dw.new_ikey.copy_(torch.from_numpy(_edge_rows(w.B, dw.new_ikey.shape[-1], 4)).view_as(dw.new_ikey))
     dw.step()
     torch.cuda.synchronize()
     kvc, kvs, ixc, ixs = (host(t) for t in dw.caches[0])
