@@ -208,7 +208,19 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
  * csa2_workspace_check reports it as CSA2_ERR_INCOMPLETE and clears the
  * flag.  Records carry the launch's generation, so a record left behind by
  * such a launch is never taken by a later one, and later calls on the same
- * workspace are correct. */
+ * workspace are correct.
+ *
+ * Prefill passes of csa2_layer_step over long contexts (32 or more tokens
+ * per sequence, 128-channel index keys, 1 to 4 indexer heads, K <= 2048,
+ * 2^15 to 2^18 cache slots, no pool) select without a score matrix
+ * (CSA2_TOPK_SAMPLED): every 16th position is scored first and each row's
+ * threshold is set from those samples so that about 2K positions pass it;
+ * the full scan keeps only the positions at or above it, and the exact
+ * Top-K is taken among them.  A row whose kept positions come short of K
+ * or overflow their room is scored in full and selected by the ROW kernel,
+ * so the result is the same index set, in the same order, as the other
+ * variants give.  CSA2_TOPK_ROW or any score-matrix variant forced for such
+ * a pass runs it the older way. */
 typedef enum {
   CSA2_TOPK_AUTO = 0,             /* chosen from the shape */
   CSA2_TOPK_ROW = 1,              /* one block per row, in LDS (rows of <= 2^18 slots) */
@@ -216,7 +228,9 @@ typedef enum {
   CSA2_TOPK_SELECT = 3,           /* 4096-score blocks; the row's last block finishes */
   CSA2_TOPK_SELECT_CUT = 4,       /* ... after a kernel that finds each row's cut bin */
   CSA2_TOPK_SELECT_LARGE = 5,     /* 16384-score blocks; the row's last block finishes */
-  CSA2_TOPK_SELECT_LARGE_CUT = 6  /* ... after the cut kernel */
+  CSA2_TOPK_SELECT_LARGE_CUT = 6, /* ... after the cut kernel */
+  CSA2_TOPK_SAMPLED = 7,          /* prefill passes: sampled threshold, candidates only */
+  CSA2_TOPK_SAMPLED_FALLBACK = 8  /* ... with every row sent to the exact path */
 } csa2_topk_variant;
 /* Flag in csa2_topk_last_variant(): the finishing block merged two sorted
  * lists (rows over 2^19 slots) instead of reading back a bitmap. */

@@ -728,12 +728,50 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
         fresh.kv_cap = a->kv.cap;
         fresh.kv_dim = a->D;
       }
+      int32_t* idx = a->idx_out + (size_t)r0 * a->K;
+      // Prefill passes over long contexts select without a score matrix: a
+      // sampled threshold, the candidates above it, the exact Top-K among
+      // them, and the exact path for any row that needs it (the sample
+      // lives in the kept-position region, the candidates in the candidate
+      // region and the per-row words in the count region of the Top-K
+      // workspace, none of which the exact path of these passes touches).
+      if (!pooled_in && !(mode == CSA2_MODE_FULL && a->P > 0) &&
+          sampled_select_pass(nr, a->T, a->H_I, a->D_I, r0, a->K, n_max) &&
+          L.tw.above_stride >= kCandCap && L.tw.counts_stride >= 3) {
+        SampledSel sel;
+        sel.samp = reinterpret_cast<float*>(L.tw.above);
+        sel.ns_stride = L.tw.above_stride;
+        sel.cand = reinterpret_cast<uint2*>(L.tw.cand);
+        sel.thr = L.tw.counts;
+        sel.count = L.tw.counts + nr;
+        sel.fail = L.tw.counts + 2 * (size_t)nr;
+        const bool force_fail = topk_variant_forced() == kTopkSampledFallback;
+        const uint8_t* ic = a->icache.codes;
+        const uint8_t* isc = a->icache.scales;
+        CSA2_LAUNCH(1, PROF_STREAM, launch_index_sample(ic, isc, a->D_I, a->icache.cap, nr, a->T, qi, wi,
+                                                        a->H_I, nvp, nv_add, n_max, sel, st, r0),
+                    "index sample launch");
+        CSA2_LAUNCH(2, PROF_STREAM, launch_sample_threshold(nr, nvp, nv_add, n_max, a->K, sel, force_fail, st),
+                    "sample threshold launch");
+        CSA2_LAUNCH(1, PROF_STREAM, launch_index_candidates(ic, isc, a->D_I, a->icache.cap, nr, a->T, qi, wi,
+                                                            a->H_I, nvp, nv_add, n_max, sel, st, r0),
+                    "index candidates launch");
+        CSA2_LAUNCH(2, PROF_STREAM, launch_sampled_final(nr, nvp, nv_add, n_max, a->K, idx, sel, st),
+                    "candidate select launch");
+        CSA2_LAUNCH(1, PROF_STREAM, launch_index_score_failed(ic, isc, a->D_I, a->icache.cap, nr, a->T, qi, wi,
+                                                              a->H_I, nvp, nv_add, n_max, L.scores,
+                                                              L.n_out, sel.fail, st, r0),
+                    "index score launch (exact path)");
+        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_row_failed(L.scores, nr, L.n_out, nvp, nv_add, a->K, idx,
+                                                           sel.fail, st),
+                    "top-k select launch (exact path)");
+        set_topk_last(force_fail ? kTopkSampledFallback : kTopkSampled);
+      } else {
       CSA2_LAUNCH(1, PROF_STREAM, launch_index_score(a->icache.codes, a->icache.scales, a->D_I, a->icache.cap, nr, a->T,
                                   qi, wi, a->H_I, nvp, nv_add, pool, pooled_in ? a->P_in : 0, n_max,
                                   L.scores, L.n_out, row ? nullptr : L.tw.hist, L.tw.hist_stride,
                                   L.tw.hist_copies, st, r0, fresh_in_scan ? &fresh : nullptr),
                "index score launch");
-      int32_t* idx = a->idx_out + (size_t)r0 * a->K;
       if (mode == CSA2_MODE_FULL && a->P > 0) {
         int32_t* pool_out = a->pool_out + (size_t)r0 * a->P;
         int32_t* pcount = a->pool_count_out + r0;
@@ -753,6 +791,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, nvp, nv_add, n_max,
                                     pooled_in ? pool : nullptr, a->K, idx, nullptr, L.tw, st, row),
                  "top-k select launch");
+      }
       }
     }
     const int32_t* idx_att = (mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out) + (size_t)r0 * a->K;

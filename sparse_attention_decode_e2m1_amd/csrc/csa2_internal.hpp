@@ -72,7 +72,9 @@ enum TopkVariant : int32_t {
   kTopkSelectCut = 4,    // ... after a per-row cut kernel
   kTopkSelectLarge = 5,  // 16384-score blocks; the row's last block finishes
   kTopkSelectLargeCut = 6,
-  kTopkVariants = 7,
+  kTopkSampled = 7,          // prefill: a sampled threshold, then the candidates above it only
+  kTopkSampledFallback = 8,  // ... with every row sent to the exact path (a test of that path)
+  kTopkVariants = 9,
 };
 constexpr int32_t kTopkListFinish = 16;  // flag: the finishing block merged sorted lists
 int32_t topk_variant_forced();
@@ -149,6 +151,56 @@ constexpr int32_t kRowTopkMinRows = 64;
 constexpr int64_t kRowTopkMaxN = 262144;
 constexpr int64_t kRowTopkSmallN = 16384;
 bool topk_row_pass(int32_t rows, int64_t n_max);
+
+// Prefill selection without a score matrix.  Every kSampleStride-th
+// position is scored first; each row's threshold is read off those samples
+// low enough that, in expectation, twice the row's K positions pass it; the
+// full scan then keeps only the positions at or above it (about 2K per row
+// instead of every score), and the exact Top-K is taken among them.  A row
+// whose candidates come short of K, or overflow the room for them, is
+// scored in full again and selected by the one-block-per-row kernel, so the
+// result never depends on the sample.
+constexpr int kSampleStride = 16;
+constexpr int kCandCap = 8192;    // candidates kept per row
+constexpr int kCandStage = 64;    // candidates a scoring block stages per token
+struct SampledSel {
+  float* samp;        // row r: sample m (position kSampleStride * m) at samp + r * ns_stride + m
+  int64_t ns_stride;
+  uint32_t* thr;      // per row: the candidates' key threshold
+  uint32_t* count;    // per row: candidates written
+  uint32_t* fail;     // per row: nonzero sends the row to the exact path
+  uint2* cand;        // row r: kCandCap (score key, slot) pairs at cand + r * kCandCap
+};
+// The prefill passes that can take it (flat scan, tokens x positions kernel,
+// K <= 2048, at least 32 K positions, at most kRowTopkMaxN).
+bool sampled_select_pass(int32_t rows, int32_t T, int32_t HI, int32_t DI, int32_t row0,
+                         int32_t K, int64_t n_max);
+hipError_t launch_index_sample(const uint8_t* codes, const uint8_t* scales, int32_t DI,
+                               int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
+                               const float* w, int32_t HI, const int32_t* n_valid,
+                               int32_t nv_add, int64_t n_max, const SampledSel& sel,
+                               hipStream_t st, int32_t row0);
+hipError_t launch_index_candidates(const uint8_t* codes, const uint8_t* scales, int32_t DI,
+                                   int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
+                                   const float* w, int32_t HI, const int32_t* n_valid,
+                                   int32_t nv_add, int64_t n_max, const SampledSel& sel,
+                                   hipStream_t st, int32_t row0);
+// The full score rows of the rows whose fail word is set (others untouched).
+hipError_t launch_index_score_failed(const uint8_t* codes, const uint8_t* scales, int32_t DI,
+                                     int64_t cap, int32_t rows, int32_t T, const uint16_t* q_idx,
+                                     const float* w, int32_t HI, const int32_t* n_valid,
+                                     int32_t nv_add, int64_t n_max, float* scores, int64_t n_out,
+                                     const uint32_t* fail, hipStream_t st, int32_t row0);
+hipError_t launch_sample_threshold(int32_t rows, const int32_t* n_valid, int32_t nv_add,
+                                   int64_t n_max, int32_t k, const SampledSel& sel,
+                                   bool force_fail, hipStream_t st);
+hipError_t launch_sampled_final(int32_t rows, const int32_t* n_valid, int32_t nv_add,
+                                int64_t n_max, int32_t k, int32_t* idx_out,
+                                const SampledSel& sel, hipStream_t st);
+// topk_row_kernel over the rows whose fail word is set.
+hipError_t launch_topk_row_failed(const float* scores, int32_t rows, int64_t n,
+                                  const int32_t* n_valid, int32_t nv_add, int32_t k,
+                                  int32_t* idx_out, const uint32_t* fail, hipStream_t st);
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,

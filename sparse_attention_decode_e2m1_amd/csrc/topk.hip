@@ -1287,8 +1287,9 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* h, int nbins, uint
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, int32_t nwp) {
+    int32_t* __restrict__ count_out, int32_t nwp, const uint32_t* __restrict__ only) {
   constexpr int NT = kRowThreads, NW = NT / 64, UN = 8;
+  if (only && only[blockIdx.x] == 0u) return;  // a row the sampled selection has finished
   extern __shared__ uint32_t lds[];
   uint32_t* hist = lds;               // kHistBins
   uint32_t* keep = hist + kHistBins;  // nwp words: slots kept
@@ -1458,8 +1459,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   if (count_out && tid == 0) count_out[r] = k;
 }
 
-bool topk_row_pass(int32_t rows, int64_t n_max) {
+// The forced variant as the score-matrix selection sees it (the sampled
+// prefill variants leave these passes their own choice).
+static int32_t forced_select_variant() {
   const int32_t f = topk_variant_forced();
+  return f >= kTopkSampled ? (int32_t)kTopkAuto : f;
+}
+
+bool topk_row_pass(int32_t rows, int64_t n_max) {
+  const int32_t f = forced_select_variant();
   if (f == kTopkRow) return n_max <= kRowTopkMaxN;
   if (f != kTopkAuto) return false;
   return (rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN) || n_max <= kRowTopkSmallN;
@@ -1501,6 +1509,229 @@ hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const 
   return hipGetLastError();
 }
 
+// ------------------------------------------------ sampled prefill selection
+// Threshold of row r from its samples (one block of kThrThreads per row,
+// the samples held in registers): the key at which the count of visible
+// samples from the top reaches M = 2 need / kSampleStride + 16 (need =
+// min(k, visible slots)), to 20 bits (the 12-bit bin, then 12 more bits
+// inside it); every sample at or above the M-th largest is at or above it.
+// A row with at most M visible samples takes every visible slot (threshold
+// 0).  force_fail sets an unreachable threshold, so every row with something
+// to select takes the exact path.  Also clears the row's candidate count
+// and fail word.
+constexpr int kThrThreads = 512;
+constexpr int kThrPer = 32;  // samples per thread: rows of up to 2^18 slots
+static_assert(kThrThreads * kThrPer * kSampleStride >= kRowTopkMaxN, "samples fit the block");
+__global__ __launch_bounds__(kThrThreads) void sample_threshold_kernel(
+    const int32_t* __restrict__ n_valid, int32_t nv_add, int64_t n_max, int32_t k,
+    SampledSel sel, uint32_t force_fail) {
+  constexpr int NT = kThrThreads;
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t tmp[NT / 64];
+  __shared__ uint32_t s_bin, s_above;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n_max), (int64_t)0);
+  const int nsv = (int)((nv + kSampleStride - 1) / kSampleStride);  // visible samples
+  const int64_t need = min((int64_t)k, nv);
+  const int M = (int)min((int64_t)nsv, 2 * need / kSampleStride + 16);
+  const float* sr = sel.samp + (int64_t)r * sel.ns_stride;
+  uint32_t thr = 0u;
+  if (force_fail) {
+    thr = 0xFFFFFFFFu;
+  } else if (nsv > M) {
+    // every load issued before any is used
+    uint32_t key[kThrPer];
+#pragma unroll
+    for (int q = 0; q < kThrPer; ++q) {
+      const int m = tid + q * NT;
+      key[q] = (m < nsv) ? score_key(sr[m]) : 0u;
+    }
+    for (int j = tid; j < kHistBins; j += NT) hist[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kThrPer; ++q)
+      if (tid + q * NT < nsv) atomicAdd(&hist[key[q] >> kHistShift], 1u);
+    __syncthreads();
+    find_bin_desc<NT>(hist, kHistBins, (uint32_t)M, tmp, &s_bin, &s_above);
+    const uint32_t b1 = s_bin, rem = (uint32_t)M - s_above;
+    for (int j = tid; j < kHistBins; j += NT) hist[j] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kThrPer; ++q)
+      if (tid + q * NT < nsv && (key[q] >> kHistShift) == b1)
+        atomicAdd(&hist[(key[q] >> 8) & (kHistBins - 1)], 1u);
+    __syncthreads();
+    find_bin_desc<NT>(hist, kHistBins, rem, tmp, &s_bin, &s_above);
+    thr = (b1 << kHistShift) | (s_bin << 8);
+  }
+  if (tid == 0) {
+    sel.thr[r] = thr;
+    sel.count[r] = 0u;
+    sel.fail[r] = 0u;
+  }
+}
+
+// Exact Top-K of row r among its candidates (one block of 1024 per row, the
+// candidates in registers): the key T of the need-th largest from 12-, 12-
+// and 8-bit histograms; keys above T are kept, keys equal to T go to a tie
+// bitmap whose lowest slots fill the rest (the lower slot wins a tie), and
+// the kept slots are written in slot order, -1 after them.  A row whose
+// list is short, overflowed, or was flagged is left to the exact path (its
+// fail word set).
+constexpr int kFinThreads = 1024;
+constexpr int kFinPer = kCandCap / kFinThreads;
+__global__ __launch_bounds__(kFinThreads) void sampled_final_kernel(
+    const int32_t* __restrict__ n_valid, int32_t nv_add, int64_t n_max, int32_t k,
+    int32_t* __restrict__ idx_out, SampledSel sel) {
+  constexpr int NT = kFinThreads;
+  extern __shared__ uint32_t fin_lds[];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t tmp[NT / 64];
+  __shared__ uint32_t s_bin, s_above;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n_max), (int64_t)0);
+  const uint32_t need = (uint32_t)min((int64_t)k, nv);
+  const uint32_t c = sel.count[r];
+  if (sel.fail[r] != 0u || c > (uint32_t)kCandCap || c < need) {
+    if (tid == 0) sel.fail[r] = 1u;
+    return;
+  }
+  int32_t* orow = idx_out + (int64_t)r * k;
+  const int nwords = (int)((nv + 31) >> 5);
+  uint32_t* keep = fin_lds;        // nwords
+  uint32_t* tie = keep + nwords;   // nwords
+  const uint2* cr = sel.cand + (int64_t)r * kCandCap;
+  uint32_t ck[kFinPer], cs[kFinPer];
+#pragma unroll
+  for (int q = 0; q < kFinPer; ++q) {
+    const uint32_t x = tid + q * NT;
+    const uint2 e = (x < c) ? cr[x] : make_uint2(0u, 0u);
+    ck[q] = e.x;
+    cs[q] = e.y;
+  }
+  for (int x = tid; x < nwords; x += NT) keep[x] = tie[x] = 0u;
+  uint32_t T = 0u, above = 0u;
+  if (need > 0u) {
+    // three levels: bits 31..20, 19..8, 7..0 of the need-th largest key
+    uint32_t pre = 0u;  // the key bits fixed so far
+    for (int lvl = 0; lvl < 3; ++lvl) {
+      const int shift = lvl == 0 ? 20 : (lvl == 1 ? 8 : 0);
+      const int nb = lvl == 2 ? 256 : kHistBins;
+      const int hi = lvl == 0 ? 32 : (lvl == 1 ? 20 : 8);  // bits above `hi` are fixed
+      for (int j = tid; j < kHistBins; j += NT) hist[j] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kFinPer; ++q)
+        if (tid + q * NT < c && (hi == 32 || (ck[q] >> hi) == pre))
+          atomicAdd(&hist[(ck[q] >> shift) & (uint32_t)(nb - 1)], 1u);
+      __syncthreads();
+      find_bin_desc<NT>(hist, nb, need - above, tmp, &s_bin, &s_above);
+      above += s_above;
+      pre = (hi == 32 ? 0u : (pre << (hi - shift))) | s_bin;
+    }
+    T = pre;
+  }
+  // keys above T kept; keys equal to T listed as ties
+#pragma unroll
+  for (int q = 0; q < kFinPer; ++q) {
+    if (tid + q * NT < c && need > 0u) {
+      if (ck[q] > T) atomicOr(&keep[cs[q] >> 5], 1u << (cs[q] & 31));
+      else if (ck[q] == T) atomicOr(&tie[cs[q] >> 5], 1u << (cs[q] & 31));
+    }
+  }
+  __syncthreads();
+  // thread t takes words [t*wpt, (t+1)*wpt): the lowest need - above ties
+  // join the kept slots, then every kept slot is written in slot order
+  const int wpt = (nwords + NT - 1) / NT;
+  const uint32_t tneed = need - above;
+  uint32_t tc = 0;
+  for (int q = 0; q < wpt; ++q) {
+    const int wi = tid * wpt + q;
+    if (wi < nwords) tc += (uint32_t)__popc(tie[wi]);
+  }
+  uint32_t tot;
+  uint32_t tb = block_scan<NT>(tc, tmp, &tot);
+  uint32_t kc = 0;
+  for (int q = 0; q < wpt; ++q) {
+    const int wi = tid * wpt + q;
+    if (wi >= nwords) break;
+    uint32_t m = tie[wi], kw = keep[wi];
+    while (m && tb < tneed) {
+      kw |= m & (~m + 1u);  // lowest tie of the word
+      m &= m - 1u;
+      ++tb;
+    }
+    keep[wi] = kw;  // this thread's own words
+    kc += (uint32_t)__popc(kw);
+  }
+  uint32_t o = block_scan<NT>(kc, tmp, &tot);
+  for (int q = 0; q < wpt; ++q) {
+    const int wi = tid * wpt + q;
+    if (wi >= nwords) break;
+    uint32_t m = keep[wi];
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      if (o < (uint32_t)k) orow[o] = wi * 32 + bit;
+      ++o;
+      m &= m - 1u;
+    }
+  }
+  for (uint32_t x = need + tid; x < (uint32_t)k; x += NT) orow[x] = -1;
+}
+
+hipError_t launch_sample_threshold(int32_t rows, const int32_t* n_valid, int32_t nv_add,
+                                   int64_t n_max, int32_t k, const SampledSel& sel,
+                                   bool force_fail, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  CSA2_KERNEL(true, true, sample_threshold_kernel, dim3((unsigned)rows), dim3(kThrThreads), 0, st,
+              n_valid, nv_add, n_max, k, sel, force_fail ? 1u : 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_sampled_final(int32_t rows, const int32_t* n_valid, int32_t nv_add,
+                                int64_t n_max, int32_t k, int32_t* idx_out,
+                                const SampledSel& sel, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (n_max > kRowTopkMaxN) return hipErrorInvalidValue;
+  const size_t lds = (size_t)2 * ((n_max + 31) / 32) * 4;  // kept and tie bitmaps
+  static bool raised = false;
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute((const void*)sampled_final_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(2 * (kRowTopkMaxN / 32) * 4));
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  CSA2_KERNEL(true, true, sampled_final_kernel, dim3((unsigned)rows), dim3(kFinThreads), lds, st,
+              n_valid, nv_add, n_max, k, idx_out, sel);
+  return hipGetLastError();
+}
+
+static hipError_t raise_row_lds() {
+  static bool raised = false;
+  if (raised) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) +
+                                            2 * kRowCand) * sizeof(uint32_t)));
+  if (e == hipSuccess) raised = true;
+  return e;
+}
+
+hipError_t launch_topk_row_failed(const float* scores, int32_t rows, int64_t n,
+                                  const int32_t* n_valid, int32_t nv_add, int32_t k,
+                                  int32_t* idx_out, const uint32_t* fail, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (n > kRowTopkMaxN) return hipErrorInvalidValue;
+  const int32_t nwp = (int32_t)(((n + 31) / 32 + 3) & ~3);
+  const size_t lds = (size_t)(kHistBins + 2 * nwp + 2 * kRowCand) * sizeof(uint32_t);
+  hipError_t e = raise_row_lds();
+  if (e != hipSuccess) return e;
+  CSA2_KERNEL(true, true, topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), lds, st,
+              scores, n, n_valid, nv_add, nullptr, k, idx_out, nullptr, nwp, fail);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
@@ -1510,23 +1741,16 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   if (row_ok && topk_row_pass(rows, n_max)) {
     const int32_t nwp = (int32_t)(((n + 31) / 32 + 3) & ~3);
     const size_t lds = (size_t)(kHistBins + 2 * nwp + 2 * kRowCand) * sizeof(uint32_t);
-    static bool raised = false;
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) +
-                                                2 * kRowCand) * sizeof(uint32_t)));
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+    hipError_t e = raise_row_lds();
+    if (e != hipSuccess) return e;
     CSA2_KERNEL(true, true, topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), lds, st,
-                scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp);
+                scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, nullptr);
     set_topk_last(kTopkRow);
     return hipGetLastError();
   }
   // A variant forced by csa2_set_topk_variant runs when the pass allows it;
   // otherwise the choice falls back to the shape's own.
-  const int32_t forced = topk_variant_forced();
+  const int32_t forced = forced_select_variant();
   // Passes whose blocks can all be resident at once take the one-wait variant.
   if (forced == kTopkAuto || forced == kTopkOneWait) {
     const int32_t nblk = topk_blocks(n_max, kTopkChunk);
