@@ -103,6 +103,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// max(x, 0) in one integer instruction: a negative float (sign bit set)
+// compares below 0 as a signed integer, and +0 is the integer 0.  (fmaxf
+// would first quiet its operands, one more instruction each.)
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ------------------------------------------------------------ score keys
 // Order-preserving unsigned key of an fp32 score: larger score -> larger
 // key; -0 and +0 map to the same key.

@@ -140,7 +140,7 @@ __device__ FreshOut fresh_compute(const NewRows& nw, int32_t HI, bool index_part
     float acc = bf16_to_f32(f.q[h] & 0xFFFFu) * k0 + bf16_to_f32(f.q[h] >> 16) * k1;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
-    sc += __shfl(f.wq, h, kWave) * fmaxf(acc, 0.0f);
+    sc += __shfl(f.wq, h, kWave) * relu(acc);
   }
   o.sc = sc;
   return o;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       }
       float part = 0.0f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part += wq[rr] * fmaxf(acc[rr], 0.0f);
+      for (int rr = 0; rr < 4; ++rr) part += wq[rr] * relu(acc[rr]);
       if constexpr (GPS >= 2) part += shfl_xor(part, 16);
       if constexpr (GPS >= 4) part += shfl_xor(part, 32);
       const int64_t s = start + (int64_t)((rnd * 4 + wave) * GT + a * TPA + my_slot) * 16 + i;
@@ -578,10 +578,11 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
     int64_t s = start + (int64_t)tile * 16 + i;
     if (s >= end) s = end - 1;
     const int64_t pr = s * PSTEP;  // cache row of the slot
+    // ordinary loads: the block's four waves and the other row groups'
+    // blocks read the same rows, so they should stay in the caches
 #pragma unroll
     for (int c2 = 0; c2 < NCH; ++c2) {
-      cw[c2] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(cbase + pr * ROWB + 64 * c2 + 16 * g));
+      cw[c2] = *reinterpret_cast<const u32x4*>(cbase + pr * ROWB + 64 * c2 + 16 * g);
       sw[c2] = *reinterpret_cast<const uint32_t*>(sbase + pr * ROWS + 8 * c2 + 4 * (g >> 1));
     }
   };
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
           for (int kk = 0; kk < 4; ++kk) acc = mfma16x16x32(qv[j][c2][kk], kb[c2][kk], acc);
         float part = 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) part += wq[j][rr] * fmaxf(acc[rr], 0.0f);
+        for (int rr = 0; rr < 4; ++rr) part += wq[j][rr] * relu(acc[rr]);
         const int64_t tr = min(rbase + 4 * j + g, rows - 1);
         if constexpr (MODE == kTokAll) {
           // Unconditional (clamped) store, as in index_score_kernel: tokens
