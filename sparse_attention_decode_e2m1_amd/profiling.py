@@ -125,6 +125,11 @@ def cmd_mfma(a):
     print(f"simds: {a.simds}")
     print(f"mfma_busy_fraction: {util:.4f}")
     print(f"mfma_f16_flop_per_dispatch: {flops:.4g}")
+    if "SQ_INSTS_VALU" in c:
+        # 16x16x32 f16 MFMAs: 16384 flops each; SQ_INSTS_VALU counts them too
+        n_mfma = flops / 16384
+        print(f"SQ_INSTS_VALU_per_dispatch: {c['SQ_INSTS_VALU']:.0f}")
+        print(f"other_valu_per_mfma: {(c['SQ_INSTS_VALU'] - n_mfma) / max(n_mfma, 1):.2f}")
 
 
 def read_traffic(path: str, kernel: str):
