@@ -256,13 +256,15 @@ def test_topk_many_rows():
     _check_topk(s, nv, 256)
 
 
+@pytest.mark.parametrize("n", [40007, 12005])
 @pytest.mark.parametrize("kind", ["normal", "ties", "three_values", "slot_map"])
-def test_topk_one_block_per_row(kind):
+def test_topk_one_block_per_row(kind, n):
     """64 or more rows of at most 2^18 slots: one block per row selects in LDS
     (the cut bin's candidates listed there, or, past 4096 of them, further
-    passes over the row).  Rows at and below k visible slots included."""
-    rng = np.random.default_rng(len(kind))
-    rows, n = 72, 40000 + 7
+    passes over the row).  Rows at and below k visible slots included.  Rows
+    of 8K to 16K slots keep their keys in registers."""
+    rng = np.random.default_rng(len(kind) + n)
+    rows = 72
     if kind == "ties":
         s = np.round(rng.standard_normal((rows, n)), 1)
         s[3] = np.where(rng.random(n) < 0.5, -0.0, 0.0)   # -0 == +0
