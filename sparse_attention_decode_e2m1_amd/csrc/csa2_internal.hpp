@@ -225,6 +225,11 @@ hipError_t launch_gather_scores(const float* scores, int64_t n, const int32_t* p
                                 uint32_t* hist, int64_t hist_stride, int32_t hist_copies,
                                 hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// Blocks of `kernel` (with `threads` threads and `lds` bytes of dynamic LDS)
+// that the current device holds at once, from the occupancy query; cached
+// per (kernel, threads, LDS, device) and safe to call from several threads.
+// 0 if the query fails.
+int64_t device_resident_blocks(const void* kernel, int threads, size_t lds);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t blocks,
                               hipStream_t st);
 // Quantize-on-write of one decode/prefill step: rows r of x1 (dim1) and x2

@@ -1,8 +1,40 @@
-// misc.hip -- small helper kernels: workspace fill and pool score gather.
+// misc.hip -- small helper kernels: workspace fill and pool score gather;
+// the per-device occupancy cache the launchers share.
+#include <mutex>
+#include <vector>
+
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
 namespace csa2 {
+
+int64_t device_resident_blocks(const void* kernel, int threads, size_t lds) {
+  struct Entry {
+    const void* k;
+    int threads;
+    size_t lds;
+    int dev;
+    int64_t blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.k == kernel && e.threads == threads && e.lds == lds && e.dev == dev) return e.blocks;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache.push_back({kernel, threads, lds, dev, (int64_t)cus * per});
+  return cache.back().blocks;
+}
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t words) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;

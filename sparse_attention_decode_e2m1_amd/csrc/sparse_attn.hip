@@ -25,9 +25,6 @@
 // (Merging in the same launch, with the splits exchanging partials through
 // device-coherent memory, measured slower on MI355X than the kernel boundary:
 // partials written by one XCD and read by another make a slow round trip.)
-#include <mutex>
-#include <vector>
-
 #include "csa2_device.hpp"
 #include "csa2_internal.hpp"
 
@@ -606,34 +603,6 @@ size_t attn_lds_bytes(int32_t dv) {
   return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
 }
 
-// Blocks of a split kernel instantiation that fit on the current device at
-// once: cached per (kernel, LDS size, device), since every instantiation
-// has the same function type.
-template <typename F>
-static int64_t resident_blocks(F kernel, size_t lds) {
-  struct Entry {
-    const void* k;
-    size_t lds;
-    int dev;
-    int64_t blocks;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& e : cache)
-    if (e.k == (const void*)kernel && e.lds == lds && e.dev == dev) return e.blocks;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  cache.push_back({(const void*)kernel, lds, dev, (int64_t)cus * per_cu});
-  return cache.back().blocks;
-}
-
 // Launches the one-launch kernel if its grid fits the device at once
 // (blocks per compute unit from the occupancy query, per device); sets
 // *launched accordingly.
@@ -641,29 +610,15 @@ template <int D, int DV, int KB>
 static hipError_t try_one_launch(const AttnArgs& args, int32_t rows, size_t lds, uint32_t* ctl,
                                  float* out, float* lse, hipStream_t st, bool* launched) {
   *launched = false;
-  static bool lds_raised = false;
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_one_launch_kernel<D, DV, KB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
-  static int64_t cap[64];
-  static bool known[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipSuccess;
-  if (!known[dev]) {
-    int cus = 0, per = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, sparse_attn_one_launch_kernel<D, DV, KB>,
-                                                     256, lds) != hipSuccess) {
-      (void)hipGetLastError();
-      return hipSuccess;  // unknown capacity: the split + merge kernels run instead
-    }
-    cap[dev] = (int64_t)cus * per;
-    known[dev] = true;
-  }
-  if ((int64_t)args.nsplit * rows > cap[dev]) return hipSuccess;
+  // raised once per process (thread-safe static initialisation)
+  static const hipError_t raised =
+      hipFuncSetAttribute((const void*)sparse_attn_one_launch_kernel<D, DV, KB>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (raised != hipSuccess) return raised;
+  // unknown capacity (0): the split + merge kernels run instead
+  const int64_t cap =
+      device_resident_blocks((const void*)sparse_attn_one_launch_kernel<D, DV, KB>, 256, lds);
+  if ((int64_t)args.nsplit * rows > cap) return hipSuccess;
   const dim3 grid((unsigned)args.nsplit, (unsigned)rows);
   CSA2_KERNEL(true, true, (sparse_attn_one_launch_kernel<D, DV, KB>), grid, dim3(256), lds, st,
               args, ctl, (int64_t)kCtlWordsPerRow, out, lse, wait_limit());
@@ -680,16 +635,17 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
                               const AttnWs& w, hipStream_t st, int32_t row0,
                               const float* row_scale, uint32_t* one_launch_ctl) {
   const size_t lds = attn_lds_bytes(DV);
-  static bool lds_raised = false;
-  if (!lds_raised) {
+  // raised once per process (thread-safe static initialisation)
+  static const hipError_t raised = [lds]() {
     for (const void* k : {(const void*)sparse_attn_kernel<D, DV, false, false>,
                           (const void*)sparse_attn_kernel<D, DV, true, false>,
                           (const void*)sparse_attn_kernel<D, DV, false, true>}) {
       hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    lds_raised = true;
-  }
+    return hipSuccess;
+  }();
+  if (raised != hipSuccess) return raised;
   // An empty window array contributes no entries (its pointers may be null).
   if (S == 0) W = 0;
   // One round (64 entries) per split unless the grid would be more than four
@@ -698,7 +654,8 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   // variant always takes one round).  For a 256-row prefill pass this gives
   // 8 rounds: 115.8 us against 120.4 (4 rounds), 127.9 (16) and 166 (2).
   const bool kv8 = row_scale != nullptr;
-  const int64_t cap_blocks = resident_blocks(sparse_attn_kernel<D, DV, true, false>, lds);
+  const int64_t cap_blocks =
+      device_resident_blocks((const void*)sparse_attn_kernel<D, DV, true, false>, 256, lds);
   int32_t rounds = 1;
   AttnSplit sp = attn_split(K, W, rounds);
   while (!kv8 && (int64_t)sp.nsplit * rows > 4 * cap_blocks && sp.nsplit > 2 && rounds < 64) {

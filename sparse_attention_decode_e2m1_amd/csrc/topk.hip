@@ -1513,22 +1513,7 @@ static int32_t topk_blocks(int64_t n_max, int32_t chunk) {
 // Blocks of topk_coop_kernel the current device holds at once (0 if the
 // query fails, which disables that variant).
 static int64_t coop_capacity() {
-  static int64_t cap[64];
-  static bool known[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (!known[dev]) {
-    int cus = 0, per = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, topk_coop_kernel, kCoopThreads,
-                                                     kCoopLds) != hipSuccess) {
-      (void)hipGetLastError();
-      return 0;
-    }
-    cap[dev] = (int64_t)cus * per;
-    known[dev] = true;
-  }
-  return cap[dev];
+  return device_resident_blocks((const void*)topk_coop_kernel, kCoopThreads, kCoopLds);
 }
 
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
@@ -1726,31 +1711,28 @@ hipError_t launch_sampled_final(int32_t rows, const int32_t* n_valid, int32_t nv
   if (rows <= 0) return hipSuccess;
   if (n_max > kRowTopkMaxN) return hipErrorInvalidValue;
   const size_t lds = (size_t)2 * ((n_max + 31) / 32) * 4;  // kept and tie bitmaps
-  static bool raised = false;
-  if (!raised) {
-    hipError_t e = hipFuncSetAttribute((const void*)sampled_final_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(2 * (kRowTopkMaxN / 32) * 4));
-    if (e != hipSuccess) return e;
-    raised = true;
-  }
+  static const hipError_t raised = hipFuncSetAttribute(
+      (const void*)sampled_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(2 * (kRowTopkMaxN / 32) * 4));
+  if (raised != hipSuccess) return raised;
   CSA2_KERNEL(true, true, sampled_final_kernel, dim3((unsigned)rows), dim3(kFinThreads), lds, st,
               n_valid, nv_add, n_max, k, idx_out, sel);
   return hipGetLastError();
 }
 
+// Raised once per process (thread-safe static initialisation).
 static hipError_t raise_row_lds() {
-  static bool raised = false;
-  if (raised) return hipSuccess;
-  const int bytes = (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) + 2 * kRowCand) *
-                          sizeof(uint32_t));
-  hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel<false>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)topk_row_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) raised = true;
-  return e;
+  static const hipError_t raised = []() {
+    const int bytes = (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) + 2 * kRowCand) *
+                            sizeof(uint32_t));
+    hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)topk_row_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
+  }();
+  return raised;
 }
 
 hipError_t launch_topk_row_failed(const float* scores, int32_t rows, int64_t n,
@@ -1819,16 +1801,15 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   int32_t lds_cand = fixed < kBudget ? (int32_t)((kBudget - fixed) / 8) : 0;
   if (lds_cand > 16384) lds_cand = 16384;
   const size_t lds = fixed + (size_t)lds_cand * 8;
-  static bool lds_raised = false;
-  if (!lds_raised) {
+  static const hipError_t raised = []() {
     hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<4>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)topk_select_kernel<16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+    return e;
+  }();
+  if (raised != hipSuccess) return raised;
   // many blocks per row: find each row's cut once instead of in every block
   bool use_cut = (int64_t)rows * nblk > 1024;
   if (forced >= kTopkSelect && forced <= kTopkSelectLargeCut)

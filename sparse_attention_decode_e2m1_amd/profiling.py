@@ -33,7 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # sources that define the indexer-scoring kernel's machine code
 KERNEL_SOURCES = {
     "index_score_kernel": ["csrc/index_score.hip", "csrc/csa2_device.hpp",
-                           "csrc/csa2_internal.hpp", "build.py"],
+                           "csrc/csa2_quant.hpp", "csrc/csa2_internal.hpp", "build.py"],
 }
 
 
