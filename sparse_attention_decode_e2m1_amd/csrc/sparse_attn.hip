@@ -136,14 +136,17 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     return (WIN || a.K == 0) ? 0 : a.idx[(int64_t)r * a.K + min(e, a.K - 1)];
   };
   int ix = load_ix(e0);
-  // the query row (16 heads x D bf16), loaded once by the whole block: each
-  // thread takes QPT of its 16-byte words (the last clamped)
-  constexpr int QW = 16 * D / 8, QPT = (QW + 255) / 256;
+  // the query row (16 heads x D bf16), loaded once by the whole block: the 16
+  // threads 16h .. 16h + 15 (16 consecutive lanes of one wave) take head h,
+  // thread 16h + c its 16-byte words c, c + 16, ... (the last clamped)
+  constexpr int WPH = D / 8;                 // 16-byte words per head
+  constexpr int QPT = (WPH + 15) / 16;       // words per thread
+  const int qh = tid >> 4, qc = tid & 15;    // head and word column of this thread
   uint4 qraw[QPT];
   {
-    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t)r * 16 * D);
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + ((int64_t)r * 16 + qh) * D);
 #pragma unroll
-    for (int k = 0; k < QPT; ++k) qraw[k] = qsrc[min(tid + 256 * k, QW - 1)];
+    for (int k = 0; k < QPT; ++k) qraw[k] = qsrc[min(qc + 16 * k, WPH - 1)];
   }
   uint32_t w0[NM], w1[NM], w2[NM], w3[NM], sc[NM];
   bool valid;
@@ -215,41 +218,35 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   // otherwise sink them below it, after the query has arrived)
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- query fragments (head i), scaled per head into fp16 range.  The
-  // block converts the row once: each head's largest magnitude (LDS max over
-  // the threads holding its words), then every value as fp16 times the
-  // head's power of two into an LDS copy of the row (in the V tile's space,
-  // which is written only after every wave holds its fragments); lane (i, g)
-  // then reads head i's channels 64m + 16g + [0, 16).
+  // ---- query fragments (head i), scaled per head into fp16 range.  Each
+  // head's largest magnitude comes from its 16 threads by a DPP row maximum;
+  // they write the row as fp16 times the head's power of two into an LDS
+  // copy (in the V tile's space, which is written only after every wave
+  // holds its fragments); lane (i, g) then reads head i's channels
+  // 64m + 16g + [0, 16).  Two barriers.
   f16x8 qa[NM][2];
   int er[4];
   {
-    constexpr int WPH = D / 8;      // 16-byte words per head
     constexpr int QST = D + 8;      // fp16 row stride: the 16 heads' reads spread over banks
-    __shared__ uint32_t s_qmax[16];
+    __shared__ int s_qexp[16];
     _Float16* q16 = Vs;             // [16][QST], aliases the V tile
     static_assert(16 * QST <= 64 * vs_stride<DV>(), "query copy fits the V tile");
-    if (tid < 16) s_qmax[tid] = 0u;
-    __syncthreads();
+    float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-      const int j = tid + 256 * k;
-      if (j < QW) {
+      if (qc + 16 * k < WPH) {
         const uint32_t wd[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
-        float am = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           am = fmaxf(am, fmaxf(fabsf(bf16_to_f32(wd[t] & 0xFFFFu)), fabsf(bf16_to_f32(wd[t] >> 16))));
-        atomicMax(&s_qmax[j / WPH], __float_as_uint(am));  // non-negative: ordered as integers
       }
     }
-    __syncthreads();
+    const int e = fp16_exponent_for(row16_max(am));
+    if (qc == 0) s_qexp[qh] = e;
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-      const int j = tid + 256 * k;
-      if (j < QW) {
-        const int h = j / WPH, c0 = (j % WPH) * 8;
-        const int e = fp16_exponent_for(__uint_as_float(s_qmax[h]));
+      const int j = qc + 16 * k;
+      if (j < WPH) {
         const uint32_t wd[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
         f16x8 v;
 #pragma unroll
@@ -257,7 +254,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
           v[2 * t] = (_Float16)ldexpf(bf16_to_f32(wd[t] & 0xFFFFu), e);
           v[2 * t + 1] = (_Float16)ldexpf(bf16_to_f32(wd[t] >> 16), e);
         }
-        *reinterpret_cast<f16x8*>(q16 + h * QST + c0) = v;
+        *reinterpret_cast<f16x8*>(q16 + qh * QST + 8 * j) = v;
       }
     }
     __syncthreads();
@@ -267,7 +264,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       for (int hf = 0; hf < 2; ++hf)
         qa[m][hf] = *reinterpret_cast<const f16x8*>(q16 + i * QST + 64 * m + 16 * g + 8 * hf);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) er[rr] = fp16_exponent_for(__uint_as_float(s_qmax[4 * g + rr]));
+    for (int rr = 0; rr < 4; ++rr) er[rr] = s_qexp[4 * g + rr];
     __syncthreads();  // every wave holds its fragments: the V tile may be written
   }
   const float lscale = a.sm_scale * wscale;
