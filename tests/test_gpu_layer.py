@@ -26,6 +26,20 @@ def test_group_decode_small():
     assert chk.rows == expected_rows(w) and chk.same_sets >= 3
 
 
+@pytest.mark.parametrize("hi", [1, 2])
+def test_group_decode_fewer_index_heads(hi):
+    """A decode group whose indexer has 1 or 2 heads (the scan packs more
+    tiles per MFMA) against the oracle."""
+    w = I.small(f"t_group_hi{hi}", 66 + hi, B=2, N=20000, K=512, modes=(I.FULL, I.REINDEX, I.REUSE),
+                HI=hi)
+    dw = Hn.DeviceWorkload(w)
+    dw.step()
+    torch.cuda.synchronize()
+    ores, oc = run_group(w, keep_scores=True)
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w) and chk.same_sets >= 3
+
+
 def test_group_reuse_layers_in_one_launch():
     """The decode group with its Reuse layers run by the one-launch attention
     gives every layer's output and lse bit for bit as csa2_layer_step does."""
@@ -165,15 +179,17 @@ def _edge_rows(rows, dim, seed):
     return x
 
 
-@pytest.mark.parametrize("new_dtype", ["f32", "bf16", "f32_edges"])
-def test_full_decode_writes_and_scores_the_new_rows(new_dtype):
+@pytest.mark.parametrize("new_dtype,hi", [("f32", 4), ("bf16", 4), ("f32_edges", 4), ("f32", 2),
+                                          ("f32", 1)])
+def test_full_decode_writes_and_scores_the_new_rows(new_dtype, hi):
     """A Full decode step writes its new rows inside the scan launch: the
     written rows equal the oracle's quantization of the new rows bit for bit,
     and the layer's score row (left in the workspace: it follows the control
     block) equals the oracle's indexer scores at every visible position,
     the new one included, within the fp32 accumulation bound.  The edge
-    variant puts every block of the new rows on a rounding boundary."""
-    w = I.small("t_fresh", 68, B=3, N=7000, K=256, modes=(I.FULL,))
+    variant puts every block of the new rows on a rounding boundary; 1 and 2
+    indexer heads take the same fused write."""
+    w = I.small("t_fresh", 68, B=3, N=7000, K=256, modes=(I.FULL,), HI=hi)
     dw = Hn.DeviceWorkload(w)
     if new_dtype == "bf16":
         dw.new_kv = dw.new_kv.to(torch.bfloat16)

@@ -41,9 +41,9 @@ def _three_ways(dw):
     return a
 
 
-@pytest.mark.parametrize("K", [256, 2048])
-def test_sampled_prefill_equals_score_matrix_path(K):
-    w = I.small("t_samp", 70 + K % 7, B=1, N=40000, T=64, K=K, modes=(I.FULL,))
+@pytest.mark.parametrize("K,hi", [(256, 4), (2048, 4), (256, 2), (256, 1)])
+def test_sampled_prefill_equals_score_matrix_path(K, hi):
+    w = I.small("t_samp", 70 + K % 7 + hi, B=1, N=40000, T=64, K=K, modes=(I.FULL,), HI=hi)
     dw = Hn.DeviceWorkload(w)
     a = _three_ways(dw)
     # every row keeps K distinct visible positions, in ascending order
