@@ -41,7 +41,7 @@ def _three_ways(dw):
     return a
 
 
-@pytest.mark.parametrize("K,hi", [(256, 4), (2048, 4), (256, 2), (256, 1)])
+@pytest.mark.parametrize("K,hi", [(256, 4), (2048, 4), (256, 2), (256, 1), (1, 4), (33, 4)])
 def test_sampled_prefill_equals_score_matrix_path(K, hi):
     w = I.small("t_samp", 70 + K % 7 + hi, B=1, N=40000, T=64, K=K, modes=(I.FULL,), HI=hi)
     dw = Hn.DeviceWorkload(w)
