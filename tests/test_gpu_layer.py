@@ -26,6 +26,23 @@ def test_group_decode_small():
     assert chk.rows == expected_rows(w) and chk.same_sets >= 3
 
 
+def test_group_decode_context_shorter_than_k():
+    """Contexts of fewer positions than K: every visible position is kept,
+    the rest of each index row is -1, and the attention skips the padding."""
+    w = I.small("t_short", 59, B=2, N=150, K=256, modes=(I.FULL, I.REINDEX, I.REUSE))
+    dw = Hn.DeviceWorkload(w)
+    dw.step()
+    torch.cuda.synchronize()
+    for li in (0, 1):
+        idx = host(dw.layers[li].idx_out)
+        for row in idx:
+            nv = w.N  # decode: the query sits at position N - 1 and sees [0, N)
+            assert list(row[:nv]) == list(range(nv)) and (row[nv:] == -1).all()
+    ores, oc = run_group(w, keep_scores=True)
+    chk = compare_group(w, dw, ores, oc)
+    assert chk.rows == expected_rows(w)
+
+
 @pytest.mark.parametrize("hi", [1, 2])
 def test_group_decode_fewer_index_heads(hi):
     """A decode group whose indexer has 1 or 2 heads (the scan packs more
