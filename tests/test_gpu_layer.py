@@ -74,31 +74,37 @@ def test_group_reuse_layers_in_one_launch():
     assert int(torch.count_nonzero(words)) == 0
 
 
-def test_group_pool_small():
-    w = I.small("t_pool", 61, B=1, N=60000, K=512, P=4096,
+@pytest.mark.parametrize("P,B", [(4096, 1), (12000, 2)])
+def test_group_pool_small(P, B):
+    """Pools of 4096 slots and of 12000 (whose selections keep the keys in
+    registers), one and two sequences."""
+    w = I.small("t_pool", 61, B=B, N=60000, K=512, P=P,
                 modes=(I.FULL, I.REINDEX, I.REINDEX), salient=True)
     dw = Hn.DeviceWorkload(w)
     dw.step()
     torch.cuda.synchronize()
-    assert int(host(dw.layers[0].pool_count)[0]) == 4096
-    idx0 = set(host(dw.layers[0].idx_out)[0].tolist())
-    assert idx0 <= set(host(dw.layers[0].pool_out)[0].tolist())
+    assert (host(dw.layers[0].pool_count) == P).all()
+    for b in range(B):
+        idx0 = set(host(dw.layers[0].idx_out)[b].tolist())
+        assert idx0 <= set(host(dw.layers[0].pool_out)[b].tolist())
     ores, oc = run_group(w, keep_scores=True)
     chk = compare_group(w, dw, ores, oc)
-    assert chk.rows == expected_rows(w) and chk.pools == 1
+    assert chk.rows == expected_rows(w) and chk.pools == B
 
 
-def test_pool_larger_than_context_equals_flat():
-    """P >= n: the pool is every position and Top-K equals the flat result."""
-    wp = I.small("t_poolbig", 62, B=1, N=3000, K=256, P=4096, modes=(I.FULL,))
-    wf = I.small("t_poolbig", 62, B=1, N=3000, K=256, P=0, modes=(I.FULL,))
+@pytest.mark.parametrize("N,P", [(3000, 4096), (10000, 12000)])
+def test_pool_larger_than_context_equals_flat(N, P):
+    """P >= n: the pool is every position (the rest of the pool row -1) and
+    Top-K equals the flat result."""
+    wp = I.small("t_poolbig", 62, B=1, N=N, K=256, P=P, modes=(I.FULL,))
+    wf = I.small("t_poolbig", 62, B=1, N=N, K=256, P=0, modes=(I.FULL,))
     a, b = Hn.DeviceWorkload(wp), Hn.DeviceWorkload(wf)
     a.step()
     b.step()
     torch.cuda.synchronize()
-    assert int(host(a.layers[0].pool_count)[0]) == 3000
-    assert list(host(a.layers[0].pool_out)[0][:3000]) == list(range(3000))
-    assert (host(a.layers[0].pool_out)[0][3000:] == -1).all()
+    assert int(host(a.layers[0].pool_count)[0]) == N
+    assert list(host(a.layers[0].pool_out)[0][:N]) == list(range(N))
+    assert (host(a.layers[0].pool_out)[0][N:] == -1).all()
     assert np.array_equal(host(a.layers[0].idx_out), host(b.layers[0].idx_out))
     assert np.array_equal(host(a.layers[0].out), host(b.layers[0].out))
 
