@@ -15,7 +15,11 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcsa2.so")
 OBJDIR = os.path.join(ROOT, "_build", "csa2")
 
-SOURCES = ["quantize.hip", "index_score.hip", "topk.hip", "sparse_attn.hip", "misc.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "index_score.hip", "index_tokens.hip", "topk.hip", "sparse_attn.hip",
+           "misc.hip", "api.cpp"]
+# The prefill scoring kernel keeps its MFMA results in ordinary vector
+# registers (no accumulator-register reads in its per-score epilogue).
+EXTRA_FLAGS = {"index_tokens.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for all device code.
@@ -26,7 +30,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -140,6 +140,15 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
                               float* scores, int64_t n_out, uint32_t* hist, int64_t hist_stride,
                               int32_t hist_copies, hipStream_t st, int32_t row0 = 0,
                               const NewRows* fresh = nullptr);
+// Prefill passes (32 or more tokens per sequence in whole waves of one
+// sequence, 128-channel keys, at most 4 indexer heads, no pool) score with
+// the tokens x positions kernel, which writes every visible score.
+bool index_tokens_pass(bool pool, int32_t T, int32_t HI, int32_t DI, int32_t row0);
+hipError_t launch_index_tokens(const uint8_t* codes, const uint8_t* scales, int64_t cap,
+                               int32_t rows, int32_t T, const uint16_t* q_idx, const float* w,
+                               int32_t HI, const int32_t* n_valid, int32_t nv_add, int64_t n_max,
+                               float* scores, int64_t n_out, hipStream_t st, int32_t row0,
+                               bool last);
 hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const int32_t* n_valid,
                             int32_t nv_add, int64_t n_max, uint32_t* hist, int64_t hist_stride,
                             int32_t hist_copies, hipStream_t st, bool first = true);
