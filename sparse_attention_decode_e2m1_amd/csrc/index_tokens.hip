@@ -42,6 +42,16 @@ static_assert(kPrefillChunk <= 65536, "a candidate's slot in its block fits 16 b
 //                list with one claim per token and block.
 enum { kTokAll = 0, kTokSample = 1, kTokCand = 2 };
 
+// Compare predicates of the lane-mask compare builtins (LLVM's numbering).
+constexpr int kCmpOge = 3, kCmpUlt = 36, kCmpSlt = 40;
+
+// a if this lane's bit of `mask` is set, else b (one v_cndmask on the mask)
+__device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+  return r;
+}
+
 template <int NCH, int NG, int MODE>
 __global__ __launch_bounds__(256) void index_score_tokens_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t cap,
@@ -236,12 +246,17 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
           // past the list's end it is dropped and counted, which sends the
           // wave's tokens to the exact path.  (-0 passes a threshold of +0,
           // as its key equals that of +0.)
-          const bool hit = rel < lim[j] && part >= thrf[j];
-          const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-          const uint32_t p = wcnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          // The lane masks come straight from the compares (signed rel <
+          // lim, ordered part >= threshold, unsigned p < WCAP) and select
+          // each lane's entry, so no condition is turned into a value and
+          // back.
+          const uint64_t m = __builtin_amdgcn_sicmp(rel, lim[j], kCmpSlt) &
+                             __builtin_amdgcn_fcmpf(part, thrf[j], kCmpOge);
+          const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, wcnt));
+          const uint64_t put = m & __builtin_amdgcn_uicmp(p, (uint32_t)WCAP, kCmpUlt);
           const uint32_t tokb = (uint32_t)(wave * TPW + 4 * j + g);
-          wbuf[wave][(hit && p < (uint32_t)WCAP) ? p : (uint32_t)(WCAP + lane)] =
+          wbuf[wave][lane_select(put, p, (uint32_t)(WCAP + lane))] =
               make_uint2(__float_as_uint(part), (uint32_t)rel | (tokb << 16));
           wcnt += (uint32_t)__popcll(m);
         }
