@@ -534,6 +534,91 @@ __device__ __forceinline__ void merge_units(const float* __restrict__ part, int3
   }
 }
 
+// Merge of whole rows, one block per row, for passes of many rows with few
+// splits each (a prefill pass): thread t takes unit t + 256 k of the row
+// (k < 16 DV / 512), with the splits' maxima and sums staged in LDS
+// ([split][32]: the 16 maxima, then the 16 sums), and keeps KH units x SC
+// splits of loads in flight.  Consecutive threads read consecutive pairs, so
+// each load instruction covers 512 contiguous bytes of a partial; the merge
+// kernel's groups of four threads per unit would load every split of a
+// short list several times over.  Per unit the arithmetic is the merge
+// kernel's, summed over the splits in order.
+template <int DV>
+__global__ __launch_bounds__(256) void attn_merge_rows_kernel(const float* __restrict__ part,
+                                                              int32_t nsplit,
+                                                              float* __restrict__ out,
+                                                              float* __restrict__ lse) {
+  extern __shared__ float s_ml[];  // nsplit x 32
+  constexpr int PSTRIDE = 16 * DV + 32;
+  constexpr int UPH = DV / 2;              // units per head
+  constexpr int UPT = 16 * UPH / 256;      // units per thread
+  constexpr int KH = UPT < 8 ? UPT : 8;    // units in flight
+  constexpr int SC = 8;                    // splits in flight
+  static_assert(UPT % KH == 0, "unit groups");
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* prow = part + (int64_t)r * nsplit * PSTRIDE;
+  for (int x = tid; x < nsplit * 32; x += 256)
+    s_ml[x] = prow[(int64_t)(x >> 5) * PSTRIDE + 16 * DV + (x & 31)];
+  __syncthreads();
+  for (int k0 = 0; k0 < UPT; k0 += KH) {
+    float Mrun[KH], L[KH], nx[KH], ny[KH];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      Mrun[kh] = -INFINITY;
+      L[kh] = nx[kh] = ny[kh] = 0.0f;
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += SC) {
+      float2 ov[SC][KH];
+#pragma unroll
+      for (int sc = 0; sc < SC; ++sc) {
+        if (s0 + sc < nsplit) {  // the same for the whole block
+#pragma unroll
+          for (int kh = 0; kh < KH; ++kh) {
+            const int u = tid + 256 * (k0 + kh);
+            ov[sc][kh] = ld_pair(prow + (int64_t)(s0 + sc) * PSTRIDE + (u / UPH) * DV + 2 * (u % UPH));
+          }
+        }
+      }
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) {
+        const int h = (tid + 256 * (k0 + kh)) / UPH;
+        float cm = -INFINITY;
+#pragma unroll
+        for (int sc = 0; sc < SC; ++sc)
+          if (s0 + sc < nsplit) cm = fmaxf(cm, s_ml[(s0 + sc) * 32 + h]);
+        const float Mnew = fmaxf(Mrun[kh], cm);
+        const float a = (Mnew == -INFINITY) ? 1.0f : __expf(Mrun[kh] - Mnew);
+        L[kh] *= a;
+        nx[kh] *= a;
+        ny[kh] *= a;
+#pragma unroll
+        for (int sc = 0; sc < SC; ++sc) {
+          if (s0 + sc < nsplit) {
+            const float m = s_ml[(s0 + sc) * 32 + h];
+            const float wv = (m == -INFINITY) ? 0.0f : __expf(m - Mnew);
+            L[kh] += wv * s_ml[(s0 + sc) * 32 + 16 + h];
+            nx[kh] += wv * ov[sc][kh].x;
+            ny[kh] += wv * ov[sc][kh].y;
+          }
+        }
+        Mrun[kh] = Mnew;
+      }
+    }
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      const int u = tid + 256 * (k0 + kh);
+      const int h = u / UPH, pp = 2 * (u % UPH);
+      const float inv = (L[kh] > 0.0f) ? 1.0f / L[kh] : 0.0f;
+      const int ch = partial_channel<DV>(pp);  // slot pp + 1 holds channel ch + 16
+      float* orow = out + (int64_t)r * 16 * DV + h * DV;
+      orow[ch] = nx[kh] * inv;
+      orow[ch + 16] = ny[kh] * inv;
+      if (lse && pp == 0)
+        lse[(int64_t)r * 16 + h] = (L[kh] > 0.0f) ? Mrun[kh] + logf(L[kh]) : -INFINITY;
+    }
+  }
+}
+
 template <int DV, int SUB, int KB>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
                                                            int32_t nsplit, float* __restrict__ out,
@@ -595,6 +680,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_one_launch_kernel(AttnArgs
     }
   }
 }
+
+// Passes merged one block per row (at least this many rows, at most this
+// many splits per row).
+constexpr int32_t kMergeRowsMin = 128;
+constexpr int32_t kMergeRowsMaxSplits = 64;
 
 size_t attn_lds_bytes(int32_t dv) {
   return (size_t)64 * (dv == 512 ? vs_stride<512>() : vs_stride<128>()) * sizeof(_Float16);
@@ -684,6 +774,12 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
                 args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // many rows of few splits: one block per row
+  if (rows >= kMergeRowsMin && sp.nsplit <= kMergeRowsMaxSplits) {
+    CSA2_KERNEL(false, true, attn_merge_rows_kernel<DV>, dim3((unsigned)rows), dim3(256),
+                (size_t)sp.nsplit * 32 * sizeof(float), st, w.part, sp.nsplit, out, lse);
+    return hipGetLastError();
+  }
   // four threads per output unit; each pass takes 4 KB splits
   constexpr int NU = 16 * DV / 2;
   const dim3 cgrid(NU / 64, (unsigned)rows);

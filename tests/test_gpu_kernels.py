@@ -503,6 +503,43 @@ def test_sparse_attn_one_launch(B, T, N, K, W, npad, D):
         assert np.allclose(gl[r], l, atol=1e-4, rtol=1e-5)
 
 
+@pytest.mark.parametrize("B,T,N,K,W,npad,D", [
+    (32, 4, 3000, 2048, 128, 0, 576),    # 128 rows: splits of 4 rounds
+    (32, 4, 3000, 2048, 0, 300, 576),    # no window, every row padded
+    (64, 4, 3000, 2048, 64, 0, 128),     # the 128-channel kernel, 8 rounds
+])
+def test_sparse_attn_multi_round(B, T, N, K, W, npad, D):
+    """Grids of more than four times the blocks the device holds run splits
+    of several rounds (each prefetching the next round's rows): every row
+    matches the oracle, a second call on the same workspace gives the same
+    bits, and the control words are left zero."""
+    codes, scales, swa, swa_s, idx, q, q_pos, pos0, S = _attn_batch(B, T, N, K, npad, D,
+                                                                    K + B + W + npad)
+    dv = 512 if D == 576 else 128
+    rows = B * T
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    args = (q.cuda(), B, T, api.cache(dev(codes), dev(scales), D, N), dev(idx), K, dev(swa),
+            dev(swa_s), dev(pos0), S, W, dev(q_pos), sm, dv)
+    ws = api.workspace(api.sparse_attn_workspace_bytes(rows, K, W, dv))
+    res = []
+    for _ in range(2):
+        out = torch.full((rows, 16, dv), np.nan, device="cuda")
+        lse = torch.full((rows, 16), np.nan, device="cuda")
+        api.sparse_attn(*args, out, lse, ws)
+        torch.cuda.synchronize()
+        assert ctl_words_zero(ws, rows)
+        res.append((out, lse))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    go, gl = host(res[0][0]), host(res[0][1])
+    for r in range(rows):
+        b = r // T
+        wrows = oracle.window_rows(swa[b], int(pos0[b]), int(q_pos[r]), W)
+        o, l = oracle.sparse_attn(q[r].float().numpy(), codes[b * N:(b + 1) * N],
+                                  scales[b * N:(b + 1) * N], idx[r], wrows, float(swa_s[b]), sm, dv)
+        assert_attention_close(go[r], o, what=(B, T, K, W, r))
+        assert np.allclose(gl[r], l, atol=1e-4, rtol=1e-5)
+
+
 def test_sparse_attn_small_dims_and_batch():
     """D = dv = 128 kernel variant, several sequences."""
     B, N, K = 3, 2000, 300
