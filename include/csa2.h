@@ -386,9 +386,13 @@ csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_layer_args* a, voi
 int64_t csa2_fp4_bytes_per_token(int32_t dim);
 /* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream);
-/* Bytes at the start of a workspace that hold control words for `rows`
- * query rows: they must be zero when a call starts, and every successful
- * call leaves them zero. */
+/* Every call works through its query rows in passes of at most
+ * CSA2_PASS_ROWS rows (a 4096-token prefill chunk: two passes); the
+ * workspace holds one pass's buffers. */
+#define CSA2_PASS_ROWS 2048
+/* Bytes at the start of a workspace that hold control words for
+ * min(rows, CSA2_PASS_ROWS) query rows: they must be zero when a call
+ * starts, and every successful call leaves them zero. */
 size_t csa2_workspace_control_bytes(int32_t rows);
 const char* csa2_status_string(csa2_status s);
 /* Message of the last failing call on this host thread ("" if none). */
@@ -422,8 +426,8 @@ csa2_status csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, int3
 /* Reports whether a one-wait launch on this workspace gave up waiting
  * (see the Top-K variants above and csa2_sparse_attn_one_launch).  Waits
  * for `stream`, reads the wait-failure flags of the control words of
- * min(rows, 256) query rows (rows = the largest B*T used with the
- * workspace), and returns CSA2_ERR_INCOMPLETE if any is set, after zeroing
+ * min(rows, CSA2_PASS_ROWS) query rows (rows = the largest B*T used with
+ * the workspace), and returns CSA2_ERR_INCOMPLETE if any is set, after zeroing
  * the whole control block (every call on the workspace has finished, so
  * nothing is still writing to it).  The outputs of the calls since the last
  * check are then incomplete.  Returns CSA2_OK when no flag is set.

@@ -109,7 +109,7 @@ struct ProfScope {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-constexpr int32_t kRowChunk = 256;  // query rows scored / selected / attended per pass
+constexpr int32_t kRowChunk = CSA2_PASS_ROWS;  // query rows scored / selected / attended per pass
 
 // A bump allocator over the caller's workspace.  The per-row control block
 // (kCtlWordsPerRow words) always comes first, so every kind of call finds
