@@ -67,6 +67,8 @@ __device__ __forceinline__ f16x8 v_operand(const _Float16* lo, const _Float16* h
 // Row stride (floats) of the round's logits: 64 entries + 4, so the 16 head
 // rows of a 16-byte read fall on different banks.
 constexpr int kLgStride = 68;
+constexpr float kLog2e = 1.44269504088896341f;  // log2 e
+constexpr float kLn2 = 0.693147180559945309f;   // ln 2
 
 template <int DV>
 constexpr int vs_stride() {
@@ -267,7 +269,14 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     for (int rr = 0; rr < 4; ++rr) er[rr] = s_qexp[4 * g + rr];
     __syncthreads();  // every wave holds its fragments: the V tile may be written
   }
+  // Logits are kept in base-2 units (natural logit x log2 e): the softmax
+  // weights are then plain powers of two, 2^(l - m), one v_exp each, and the
+  // partial's maximum is stored in the same units.  The query's power of two
+  // folds into the per-head scale.
   const float lscale = a.sm_scale * wscale;
+  float esc[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) esc[rr] = ldexpf(lscale * kLog2e, -er[rr]);
 
   // running softmax state of head i (every lane of the block holds its
   // head's), and this wave's P.V tiles
@@ -342,11 +351,12 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     // one barrier, lane (i, g) reads head i's logits at its P.V operand slots
     // (entries 32ks + 8g + [0, 8)), and the four lanes of head i agree on its
     // maximum and sum with lane exchanges.  Every wave thus builds P itself.
-    const float escale = (!WIN && KV8) ? lscale * sj : lscale;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      Lg[(4 * g + rr) * kLgStride + wave * 16 + i] =
-          valid ? ldexpf(acc0[rr] + acc1[rr], -er[rr]) * escale : -INFINITY;
+    for (int rr = 0; rr < 4; ++rr) {
+      float lg = (acc0[rr] + acc1[rr]) * esc[rr];
+      if constexpr (!WIN && KV8) lg *= sj;
+      Lg[(4 * g + rr) * kLgStride + wave * 16 + i] = valid ? lg : -INFINITY;
+    }
     if constexpr (!WIN && KV8) {
       if (g == 0) Sg[wave * 16 + i] = sj;
       const float wm = row16_max(sj);
@@ -369,7 +379,9 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     mr = fmaxf(mr, shfl_xor(mr, 16));
     mr = fmaxf(mr, shfl_xor(mr, 32));
     const float mnew = fmaxf(mrun, mr);
-    const float alpha = (mnew == -INFINITY) ? 1.0f : __expf(mrun - mnew);
+    const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
+    // with no finite logit yet every lv is -inf, and 2^(-inf - 0) = 0
+    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
     f16x8 pa[2];
     float ps = 0.0f;  // the sum uses the unrounded probabilities
     float ew[2][8];   // KV8: s_j / s_max of the lane's entries
@@ -385,7 +397,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pr = (mnew == -INFINITY) ? 0.0f : __expf(lv[ks][j] - mnew);
+        const float pr = __builtin_amdgcn_exp2f(lv[ks][j] - msafe);
         ps += pr;
         if constexpr (!WIN && KV8)
           pa[ks][j] = (_Float16)(pr * ew[ks][j]);
@@ -505,13 +517,13 @@ __device__ __forceinline__ void merge_units(const float* __restrict__ part, int3
     cm = fmaxf(cm, dpp_move<kDppXor1>(cm));
     cm = fmaxf(cm, dpp_move<kDppXor2>(cm));
     const float Mnew = fmaxf(Mrun, cm);
-    const float a = (Mnew == -INFINITY) ? 1.0f : __expf(Mrun - Mnew);
+    const float a = (Mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(Mrun - Mnew);
     L *= a;
     nx *= a;
     ny *= a;
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const float wv = (mv[k] == -INFINITY) ? 0.0f : __expf(mv[k] - Mnew);
+      const float wv = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - Mnew);
       L += wv * lv[k];
       nx += wv * ov[k].x;
       ny += wv * ov[k].y;
@@ -530,7 +542,7 @@ __device__ __forceinline__ void merge_units(const float* __restrict__ part, int3
     float* orow = out + (int64_t)r * 16 * DV + h * DV;
     orow[ch] = nx * inv;
     orow[ch + 16] = ny * inv;
-    if (lse && pp == 0) lse[(int64_t)r * 16 + h] = (L > 0.0f) ? Mrun + logf(L) : -INFINITY;
+    if (lse && pp == 0) lse[(int64_t)r * 16 + h] = (L > 0.0f) ? Mrun * kLn2 + logf(L) : -INFINITY;
   }
 }
 
@@ -587,7 +599,7 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(const float* __res
         for (int sc = 0; sc < SC; ++sc)
           if (s0 + sc < nsplit) cm = fmaxf(cm, s_ml[(s0 + sc) * 32 + h]);
         const float Mnew = fmaxf(Mrun[kh], cm);
-        const float a = (Mnew == -INFINITY) ? 1.0f : __expf(Mrun[kh] - Mnew);
+        const float a = (Mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(Mrun[kh] - Mnew);
         L[kh] *= a;
         nx[kh] *= a;
         ny[kh] *= a;
@@ -595,7 +607,7 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(const float* __res
         for (int sc = 0; sc < SC; ++sc) {
           if (s0 + sc < nsplit) {
             const float m = s_ml[(s0 + sc) * 32 + h];
-            const float wv = (m == -INFINITY) ? 0.0f : __expf(m - Mnew);
+            const float wv = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - Mnew);
             L[kh] += wv * s_ml[(s0 + sc) * 32 + 16 + h];
             nx[kh] += wv * ov[sc][kh].x;
             ny[kh] += wv * ov[sc][kh].y;
@@ -614,7 +626,7 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(const float* __res
       orow[ch] = nx[kh] * inv;
       orow[ch + 16] = ny[kh] * inv;
       if (lse && pp == 0)
-        lse[(int64_t)r * 16 + h] = (L[kh] > 0.0f) ? Mrun[kh] + logf(L[kh]) : -INFINITY;
+        lse[(int64_t)r * 16 + h] = (L[kh] > 0.0f) ? Mrun[kh] * kLn2 + logf(L[kh]) : -INFINITY;
     }
   }
 }
