@@ -171,7 +171,7 @@ bool topk_row_pass(int32_t rows, int64_t n_max);
 // result never depends on the sample.
 constexpr int kSampleStride = 16;
 constexpr int kCandCap = 8192;    // candidates kept per row
-constexpr int kCandStage = 64;    // candidates a scoring block stages per token
+constexpr int kCandStage = 128;   // list room per token of a scoring block (1 in 8 positions)
 struct SampledSel {
   float* samp;        // row r: sample m (position kSampleStride * m) at samp + r * ns_stride + m
   int64_t ns_stride;

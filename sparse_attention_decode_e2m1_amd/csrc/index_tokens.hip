@@ -19,8 +19,13 @@ namespace csa2 {
 // Row groups of 4 tokens per wave, and positions per block (4 groups: at
 // most 256 registers, two waves per SIMD; 8 groups need 448 and leave one).
 constexpr int kPrefillGroups = 4;
-constexpr int32_t kPrefillChunk = 512;
-static_assert(kPrefillChunk <= 65536, "a candidate's slot in its block fits 16 bits");
+constexpr int32_t kPrefillChunk = 1024;
+// A listed candidate's second word: its slot in the block (kEntTokShift
+// bits), its token in the block (6 bits), then its rank among the token's
+// entries of the block.
+constexpr int kEntTokShift = 12, kEntRankShift = kEntTokShift + 6;
+static_assert(kPrefillChunk <= (1 << kEntTokShift), "a candidate's slot in its block fits");
+static_assert(kCandStage * 8 == kPrefillChunk, "list room: one in eight positions per token");
 
 // Many query tokens of one sequence score the same positions, so the scan
 // becomes a tokens x positions contraction: MFMA rows = 4 tokens x 4 heads,
@@ -71,11 +76,13 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
   const int rbase = blockIdx.y * TPB + wave * TPW;  // first token row of this wave
   // The candidate mode has block-wide barriers: a wave without work skips
   // the scan instead of returning.  Each wave lists its kept scores as
-  // (score bits, slot in the block | token in the block << 16 | rank among
-  // the token's entries << 22); lanes that keep nothing write a sink entry
+  // (score bits, slot in the block | token in the block << kEntTokShift |
+  // rank among the token's entries << kEntRankShift); lanes that keep
+  // nothing write a sink entry
   // of their own past the list, so the scan has no branch.
   constexpr int WCAP = TPW * kCandStage;  // list entries per wave
-  static_assert(MODE != kTokCand || (TPB <= 64 && WCAP <= 1024), "list entry fields");
+  static_assert(MODE != kTokCand || (TPB <= 64 && WCAP <= (1 << (32 - kEntRankShift))),
+                "list entry fields");
   __shared__ uint2 wbuf[MODE == kTokCand ? 4 : 1][MODE == kTokCand ? WCAP + 64 : 1];
   __shared__ uint32_t wtot[MODE == kTokCand ? 4 : 1];
   __shared__ uint32_t lcnt[MODE == kTokCand ? TPB : 1];
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
           const uint64_t put = m & __builtin_amdgcn_uicmp(p, (uint32_t)WCAP, kCmpUlt);
           const uint32_t tokb = (uint32_t)(wave * TPW + 4 * j + g);
           wbuf[wave][lane_select(put, p, (uint32_t)(WCAP + lane))] =
-              make_uint2(__float_as_uint(part), (uint32_t)rel | (tokb << 16));
+              make_uint2(__float_as_uint(part), (uint32_t)rel | (tokb << kEntTokShift));
           wcnt += (uint32_t)__popcll(m);
         }
       }
@@ -272,8 +279,8 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
       const int wv = x / WCAP, e = x - wv * WCAP;
       if ((uint32_t)e < min(wtot[wv], (uint32_t)WCAP)) {
         const uint32_t y = wbuf[wv][e].y;
-        const uint32_t rank = atomicAdd(&lcnt[(y >> 16) & 63u], 1u);
-        wbuf[wv][e].y = y | (rank << 22);
+        const uint32_t rank = atomicAdd(&lcnt[(y >> kEntTokShift) & 63u], 1u);
+        wbuf[wv][e].y = y | (rank << kEntRankShift);
       }
     }
     __syncthreads();
@@ -295,11 +302,12 @@ __global__ __launch_bounds__(256) void index_score_tokens_kernel(
       const int wv = x / WCAP, e = x - wv * WCAP;
       if ((uint32_t)e < min(wtot[wv], (uint32_t)WCAP)) {
         const uint2 v = wbuf[wv][e];
-        const uint32_t tk = (v.y >> 16) & 63u;
-        const uint32_t pos = lbase[tk] + (v.y >> 22);
+        const uint32_t tk = (v.y >> kEntTokShift) & 63u;
+        const uint32_t pos = lbase[tk] + (v.y >> kEntRankShift);
         if (trow0 + (int)tk < rows && pos < (uint32_t)kCandCap)
           sel.cand[(int64_t)(trow0 + (int)tk) * kCandCap + pos] =
-              make_uint2(score_key(__uint_as_float(v.x)), (uint32_t)(start + (v.y & 0xFFFFu)));
+              make_uint2(score_key(__uint_as_float(v.x)),
+                         (uint32_t)(start + (v.y & ((1u << kEntTokShift) - 1u))));
       }
     }
   }
