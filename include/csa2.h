@@ -386,10 +386,12 @@ csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_layer_args* a, voi
 int64_t csa2_fp4_bytes_per_token(int32_t dim);
 /* Zero-fill a workspace on `stream` with a kernel (safe inside graph capture). */
 csa2_status csa2_workspace_init(void* ws, size_t ws_bytes, void* stream);
-/* Every call works through its query rows in passes of at most
- * CSA2_PASS_ROWS rows (a 4096-token prefill chunk: two passes); the
- * workspace holds one pass's buffers. */
-#define CSA2_PASS_ROWS 2048
+/* Calls work through their query rows in passes of at most CSA2_PASS_ROWS
+ * rows, and a prefill layer step that selects without a score matrix
+ * (CSA2_TOPK_SAMPLED) in passes of at most CSA2_PREFILL_PASS_ROWS (a
+ * 4096-token chunk: two passes); the workspace holds one pass's buffers. */
+#define CSA2_PASS_ROWS 256
+#define CSA2_PREFILL_PASS_ROWS 2048
 /* Bytes at the start of a workspace that hold control words for
  * min(rows, CSA2_PASS_ROWS) query rows: they must be zero when a call
  * starts, and every successful call leaves them zero. */

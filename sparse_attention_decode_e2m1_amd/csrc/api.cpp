@@ -110,6 +110,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int32_t kRowChunk = CSA2_PASS_ROWS;  // query rows scored / selected / attended per pass
+// Passes of a prefill step that selects without a score matrix: its
+// per-row buffers are small (samples, a candidate list, the exact path's
+// score row), and passes this long fill the device in every launch.
+constexpr int32_t kPrefillPassRows = CSA2_PREFILL_PASS_ROWS;
 
 // A bump allocator over the caller's workspace.  The per-row control block
 // (kCtlWordsPerRow words) always comes first, so every kind of call finds
@@ -158,9 +162,19 @@ void carve_topk(Carve& c, int32_t rows, int64_t n, int32_t k, TopkWs* tw) {
   tw->counts = c.take<uint32_t>((size_t)rows * tw->counts_stride);
 }
 
-void carve_attn(Carve& c, int32_t rows, int32_t K, int32_t W, int32_t dv, AttnWs* aw) {
-  const AttnSplit sp = attn_split(K, W);
-  aw->part = c.take<float>((size_t)rows * sp.nsplit * (16 * (size_t)dv + 32));
+// Attention partials of passes of rc rows over `rows` rows.  exact: the
+// passes' own split counts (attn_rounds of each pass's rows, FP4 cache);
+// otherwise room for one round per split, which serves either cache.
+void carve_attn(Carve& c, int32_t rows, int32_t rc, int32_t K, int32_t W, int32_t dv, AttnWs* aw,
+                bool exact = false) {
+  int64_t units = (int64_t)rc * attn_split(K, W).nsplit;
+  if (exact) {
+    const int32_t last = rows % rc;
+    units = (int64_t)rc * attn_split(K, W, attn_rounds(rc, K, W, false)).nsplit;
+    if (last > 0)
+      units = std::max<int64_t>(units, (int64_t)last * attn_split(K, W, attn_rounds(last, K, W, false)).nsplit);
+  }
+  aw->part = c.take<float>((size_t)units * (16 * (size_t)dv + 32));
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -462,7 +476,7 @@ size_t csa2_sparse_attn_workspace_bytes(int32_t rows, int32_t K, int32_t W, int3
   Carve c(nullptr);
   AttnWs aw;
   carve_ctl(c, rc, nullptr);
-  carve_attn(c, rc, K, W, dv, &aw);
+  carve_attn(c, rows, rc, K, W, dv, &aw);
   return c.off;
 }
 
@@ -507,7 +521,7 @@ static csa2_status sparse_attn_impl(const uint16_t* q, int32_t B, int32_t T, int
   Carve c(ws);
   AttnWs aw;
   carve_ctl(c, rc, nullptr);
-  carve_attn(c, rc, K, Weff, dv, &aw);
+  carve_attn(c, rows, rc, K, Weff, dv, &aw);
   const int32_t D = kv->dim;
   for (int32_t r0 = 0; r0 < rows; r0 += rc) {
     const int32_t nr = std::min(rc, rows - r0);
@@ -583,7 +597,7 @@ csa2_status csa2_sparse_attn_fp8(const uint16_t* q, int32_t B, int32_t T, int32_
   Carve c(ws);
   AttnWs aw;
   carve_ctl(c, rc, nullptr);
-  carve_attn(c, rc, K, Weff, dv, &aw);
+  carve_attn(c, rows, rc, K, Weff, dv, &aw);
   const int32_t D = kv->dim;
   for (int32_t r0 = 0; r0 < rows; r0 += rc) {
     const int32_t nr = std::min(rc, rows - r0);
@@ -603,6 +617,7 @@ namespace {
 
 struct StepLayout {
   int32_t rc;         // rows per pass
+  bool sampled;       // a prefill step selecting without a score matrix
   int64_t n_out;      // score row length
   TopkWs tw;
   AttnWs aw;
@@ -611,24 +626,58 @@ struct StepLayout {
   size_t bytes;
 };
 
-StepLayout step_layout(csa2_mode mode, const csa2_layer_args* a, void* ws) {
+// Whether a step's passes select without a score matrix (its shapes, and
+// unless shapes_only the forced Top-K variant; every pass of such a step
+// qualifies, since passes start at multiples of 32 rows).
+bool sampled_step(csa2_mode mode, const csa2_layer_args* a, bool shapes_only) {
+  if (mode == CSA2_MODE_REUSE || (mode == CSA2_MODE_FULL && a->P > 0) ||
+      (mode == CSA2_MODE_REINDEX && a->pool_in))
+    return false;
+  return shapes_only ? sampled_select_shapes(1, a->T, a->H_I, a->D_I, 0, a->K, a->icache.cap)
+                     : sampled_select_pass(1, a->T, a->H_I, a->D_I, 0, a->K, a->icache.cap);
+}
+
+// sampled: -1 from the step and the forced Top-K variant now, else 0 / 1.
+StepLayout step_layout(csa2_mode mode, const csa2_layer_args* a, void* ws, int sampled = -1) {
   StepLayout L{};
   const int32_t rows = a->B * a->T;
-  L.rc = std::min(rows, kRowChunk);
+  L.sampled = sampled < 0 ? sampled_step(mode, a, false) : sampled == 1;
+  L.rc = std::min(rows, L.sampled ? kPrefillPassRows : kRowChunk);
   const bool pooled_in = (mode == CSA2_MODE_REINDEX && a->pool_in);
   L.n_out = (mode == CSA2_MODE_REUSE) ? 1 : (pooled_in ? a->P_in : a->icache.cap);
   const int32_t Weff = (a->S > 0) ? a->W : 0;
   Carve c(ws);
-  carve_ctl(c, L.rc, &L.tw);
-  if (mode != CSA2_MODE_REUSE) {
+  // the control block always covers min(rows, kRowChunk) rows (the sampled
+  // selection uses none of its words)
+  carve_ctl(c, std::min(L.rc, kRowChunk), &L.tw);
+  if (L.sampled) {
+    // the exact path's score rows, then the position samples, the
+    // candidate lists and the per-row threshold, count and fail words
+    L.scores = c.take<float>((size_t)L.rc * L.n_out);
+    L.tw.above_stride = (L.n_out + kSampleStride - 1) / kSampleStride;
+    L.tw.above = c.take<uint32_t>((size_t)L.rc * L.tw.above_stride);
+    L.tw.cand_stride = kCandCap;
+    L.tw.cand = c.take<uint64_t>((size_t)L.rc * kCandCap);
+    L.tw.counts_stride = 3;
+    L.tw.counts = c.take<uint32_t>((size_t)L.rc * 3);
+  } else if (mode != CSA2_MODE_REUSE) {
     L.scores = c.take<float>((size_t)L.rc * L.n_out);
     const int32_t kmax = (mode == CSA2_MODE_FULL && a->P > 0) ? std::max(a->P, a->K) : a->K;
     if (mode == CSA2_MODE_FULL && a->P > 0) L.pscores = c.take<float>((size_t)L.rc * a->P);
     carve_topk(c, L.rc, std::max<int64_t>(L.n_out, a->P), kmax, &L.tw);
   }
-  carve_attn(c, L.rc, a->K, Weff, a->dv, &L.aw);
+  carve_attn(c, rows, L.rc, a->K, Weff, a->dv, &L.aw, true);
   L.bytes = c.off;
   return L;
+}
+
+// Workspace bytes of a step: the larger of the layouts it can take (a
+// prefill step's passes select without a score matrix unless a forced Top-K
+// variant says otherwise, so a workspace sized once serves every variant).
+size_t step_bytes(csa2_mode mode, const csa2_layer_args* a) {
+  size_t b = step_layout(mode, a, nullptr, 0).bytes;
+  if (sampled_step(mode, a, true)) b = std::max(b, step_layout(mode, a, nullptr, 1).bytes);
+  return b;
 }
 
 csa2_status check_step(csa2_mode mode, const csa2_layer_args* a) {
@@ -674,7 +723,7 @@ csa2_status check_step(csa2_mode mode, const csa2_layer_args* a) {
 
 size_t csa2_workspace_bytes(csa2_mode mode, const csa2_layer_args* a) {
   if (check_step(mode, a) != CSA2_OK) return 0;
-  return step_layout(mode, a, nullptr).bytes;
+  return step_bytes(mode, a);
 }
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, size_t ws_bytes,
@@ -682,7 +731,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
   g_last_error.clear();
   csa2_status s = check_step(mode, a);
   if (s) return s;
-  const size_t need = step_layout(mode, a, nullptr).bytes;
+  const size_t need = step_bytes(mode, a);
   CSA2_REQUIRE(ws && ws_bytes >= need, CSA2_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)",
                need, ws_bytes);
   const StepLayout L = step_layout(mode, a, ws);
@@ -735,9 +784,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       // lives in the kept-position region, the candidates in the candidate
       // region and the per-row words in the count region of the Top-K
       // workspace, none of which the exact path of these passes touches).
-      if (!pooled_in && !(mode == CSA2_MODE_FULL && a->P > 0) &&
-          sampled_select_pass(nr, a->T, a->H_I, a->D_I, r0, a->K, n_max) &&
-          L.tw.above_stride >= kCandCap && L.tw.counts_stride >= 3) {
+      if (L.sampled) {
         SampledSel sel;
         sel.samp = reinterpret_cast<float*>(L.tw.above);
         sel.ns_stride = L.tw.above_stride;
@@ -809,7 +856,7 @@ csa2_status csa2_layer_step_static(csa2_mode mode, const csa2_layer_args* a, voi
   g_last_error.clear();
   csa2_status s = check_step(mode, a);
   if (s) return s;
-  const size_t need = step_layout(mode, a, nullptr).bytes;
+  const size_t need = step_bytes(mode, a);
   CSA2_REQUIRE(need <= kStaticScratchBytes, CSA2_ERR_WORKSPACE,
                "this step needs %zu bytes of scratch, more than the static scratch's %zu; "
                "call csa2_layer_step with a workspace instead",

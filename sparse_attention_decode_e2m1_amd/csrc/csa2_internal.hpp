@@ -61,6 +61,22 @@ inline AttnSplit attn_split(int32_t K, int32_t W, int32_t rounds = 1) {
   s.nsplit = s.nsg + s.nsw;
   return s;
 }
+// Rounds (of 64 entries) per attention split for a pass of `rows` rows: one,
+// unless the grid would exceed kAttnGridBlocks blocks (four times the split
+// kernel's blocks an MI355X holds at once); then doubled, up to 8, keeping
+// at least 2 splits per row (FP4 main cache only: the FP8 variant takes one
+// round).  A function of the shape alone, so the workspace query sizes the
+// partials of every pass exactly.
+constexpr int64_t kAttnGridBlocks = 2048;
+inline int32_t attn_rounds(int64_t rows, int32_t K, int32_t W, bool kv8) {
+  int32_t rounds = 1;
+  AttnSplit sp = attn_split(K, W, rounds);
+  while (!kv8 && (int64_t)sp.nsplit * rows > kAttnGridBlocks && sp.nsplit > 2 && rounds < 8) {
+    rounds *= 2;
+    sp = attn_split(K, W, rounds);
+  }
+  return rounds;
+}
 
 // Process-wide diagnostic controls (set through csa2_set_topk_variant and
 // csa2_set_wait_limit) and what the last Top-K launch of this thread ran.
@@ -180,8 +196,11 @@ struct SampledSel {
   uint32_t* fail;     // per row: nonzero sends the row to the exact path
   uint2* cand;        // row r: kCandCap (score key, slot) pairs at cand + r * kCandCap
 };
-// The prefill passes that can take it (flat scan, tokens x positions kernel,
-// K <= 2048, at least 32 K positions, at most kRowTopkMaxN).
+// The prefill passes whose shapes allow it (flat scan, tokens x positions
+// kernel, K <= 2048, at least 32 K positions, at most kRowTopkMaxN), and
+// those that take it (the shapes, and a forced Top-K variant that allows it).
+bool sampled_select_shapes(int32_t rows, int32_t T, int32_t HI, int32_t DI, int32_t row0,
+                           int32_t K, int64_t n_max);
 bool sampled_select_pass(int32_t rows, int32_t T, int32_t HI, int32_t DI, int32_t row0,
                          int32_t K, int64_t n_max);
 hipError_t launch_index_sample(const uint8_t* codes, const uint8_t* scales, int32_t DI,

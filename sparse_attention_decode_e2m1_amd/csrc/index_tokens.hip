@@ -332,12 +332,17 @@ hipError_t launch_index_tokens(const uint8_t* codes, const uint8_t* scales, int6
 }
 
 // ------------------------------------------------ sampled prefill selection
+bool sampled_select_shapes(int32_t rows, int32_t T, int32_t HI, int32_t DI, int32_t row0,
+                           int32_t K, int64_t n_max) {
+  return HI <= 4 && T >= 32 && T % 32 == 0 && row0 % 32 == 0 && DI == 128 && K >= 1 &&
+         K <= 2048 && n_max >= 32768 && n_max <= kRowTopkMaxN && rows >= 1;
+}
+
 bool sampled_select_pass(int32_t rows, int32_t T, int32_t HI, int32_t DI, int32_t row0,
                          int32_t K, int64_t n_max) {
   const int32_t f = topk_variant_forced();
   if (f != kTopkAuto && f != kTopkSampled && f != kTopkSampledFallback) return false;
-  return HI <= 4 && T >= 32 && T % 32 == 0 && row0 % 32 == 0 && DI == 128 && K >= 1 &&
-         K <= 2048 && n_max >= 32768 && n_max <= kRowTopkMaxN && rows >= 1;
+  return sampled_select_shapes(rows, T, HI, DI, row0, K, n_max);
 }
 
 static hipError_t launch_tokens_mode(int mode, const uint8_t* codes, const uint8_t* scales,

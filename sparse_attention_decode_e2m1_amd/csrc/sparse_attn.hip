@@ -747,22 +747,14 @@ static hipError_t launch_attn(const uint16_t* q, int32_t rows, int32_t T, const 
   if (raised != hipSuccess) return raised;
   // An empty window array contributes no entries (its pointers may be null).
   if (S == 0) W = 0;
-  // One round (64 entries) per split unless the grid would be more than four
-  // times the device: then splits of several rounds (each prefetching the
-  // next round's rows) keep the partials few (FP4 main cache only; the FP8
-  // variant always takes one round), up to 8 rounds.  For a 256-row prefill
-  // pass 8 rounds took 115.8 us (split + merge) against 120.4 (4 rounds),
-  // 127.9 (16) and 166 (2); a 4096-token chunk in passes of 2048 rows took
-  // 2.66 ms with at most 8 rounds against 2.77 (4) and 2.72 (16).
+  // Splits of several rounds (each prefetching the next round's rows) keep
+  // the partials few when the grid would be large (attn_rounds).  For a
+  // 256-row prefill pass 8 rounds took 115.8 us (split + merge) against
+  // 120.4 (4 rounds), 127.9 (16) and 166 (2); a 4096-token chunk in passes
+  // of 2048 rows took 2.66 ms with 8 rounds against 2.77 (4) and 2.72 (16).
   const bool kv8 = row_scale != nullptr;
-  const int64_t cap_blocks =
-      device_resident_blocks((const void*)sparse_attn_kernel<D, DV, true, false>, 256, lds);
-  int32_t rounds = 1;
-  AttnSplit sp = attn_split(K, W, rounds);
-  while (!kv8 && (int64_t)sp.nsplit * rows > 4 * cap_blocks && sp.nsplit > 2 && rounds < 8) {
-    rounds *= 2;
-    sp = attn_split(K, W, rounds);
-  }
+  const int32_t rounds = attn_rounds(rows, K, W, kv8);
+  const AttnSplit sp = attn_split(K, W, rounds);
   const AttnArgs args{q, T, codes, scales, cap, idx, K, swa, swa_scale, swa_pos0, S, W, q_pos,
                       sm_scale, w.part, sp.nsg, sp.nsplit, rounds, row0, row_scale};
   if (one_launch_ctl && !kv8 && rounds == 1) {

@@ -168,9 +168,8 @@ def test_workspace_check_rejects(L):
     assert f(FAKE, ctl, 0, None) == 2                 # rows < 1
     assert f(FAKE, ctl - 1, 4, None) == 4             # smaller than the control block
     assert b"control bytes" in L.csa2_last_error()
-    # the control block covers at most one pass of 2048 rows
-    assert L.csa2_workspace_control_bytes(10_000) == L.csa2_workspace_control_bytes(2048)
-    assert L.csa2_workspace_control_bytes(2048) == 8 * L.csa2_workspace_control_bytes(256)
+    # the control block covers at most one pass of 256 rows
+    assert L.csa2_workspace_control_bytes(10_000) == L.csa2_workspace_control_bytes(256)
 
 
 def test_topk_variant_and_wait_limit_controls(L):
