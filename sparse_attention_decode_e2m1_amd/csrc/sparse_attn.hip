@@ -77,6 +77,33 @@ constexpr int vs_stride() {
   return DV + 16;
 }
 
+// The NW scale words of an FP4 row (one word per 64-channel group, byte j
+// for channels 16j..16j+15 of the group), read with as few loads as the
+// row's 4-byte alignment allows: every lane of the row takes the whole row
+// (the same cache lines) and later shifts out its own byte, instead of one
+// byte load per group.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+template <int NW>
+__device__ __forceinline__ void load_scale_words(const uint8_t* sr, uint32_t (&out)[NW]) {
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(sr);
+#pragma unroll
+  for (int q = 0; q + 4 <= NW; q += 4) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(s32 + q);
+    out[q] = v.x;
+    out[q + 1] = v.y;
+    out[q + 2] = v.z;
+    out[q + 3] = v.w;
+  }
+  constexpr int R = NW & ~3;
+  if constexpr (NW - R >= 2) {
+    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(s32 + R);
+    out[R] = v.x;
+    out[R + 1] = v.y;
+  }
+  if constexpr ((NW - R) & 1) out[NW - 1] = s32[NW - 1];
+}
+
 struct AttnArgs {
   const uint16_t* q;
   int32_t T;
@@ -172,14 +199,13 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       valid = e < a.K && ix >= 0 && ix < a.cap;
       const int64_t row = (int64_t)b * a.cap + (valid ? ix : 0);
       const uint8_t* cr = a.codes + row * (D / 2);
-      const uint8_t* sr = a.scales + row * (D / 16);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
         w0[m] = cw.x;
         w1[m] = cw.y;
-        sc[m] = sr[4 * m + g];
       }
+      load_scale_words<NM>(a.scales + row * (D / 16), sc);
     } else {
       valid = e < nw;
       const int64_t row = (int64_t)b * a.S + (valid ? (wlo - pos0 + e) : 0);
@@ -205,14 +231,13 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       pvalid = e < a.K && ix >= 0 && ix < a.cap;
       const int64_t row = (int64_t)b * a.cap + (pvalid ? ix : 0);
       const uint8_t* cr = a.codes + row * (D / 2);
-      const uint8_t* sr = a.scales + row * (D / 16);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
         p0[m] = cw.x;
         p1[m] = cw.y;
-        psc[m] = sr[4 * m + g];
       }
+      load_scale_words<NM>(a.scales + row * (D / 16), psc);
     }
   };
   load_row(e0);
@@ -325,7 +350,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
             k[4 * (q4 & 1) + 3] = hi[1];
           }
         } else if constexpr (!WIN) {
-          const f16x2 s2 = scale_pair(sc[m]);
+          const f16x2 s2 = scale_pair(sc[m] >> (8 * g));  // byte g: channels 64m + 16g..
           k0 = fp4x8_to_f16(w0[m], s2);
           k1 = fp4x8_to_f16(w1[m], s2);
         } else {
