@@ -139,6 +139,14 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   static_assert(!(KV8 && MULTI), "FP8 main-cache splits take one round");
   constexpr int NM = D / 64;        // 64-channel groups of a row
   constexpr int NMV = DV / 64;      // groups holding value channels
+  // FP4 main rows are read 16 bytes per lane: in each 128-channel group p
+  // (NP of them) lane (i, g) holds channels 128p + 32g + [0, 32), which
+  // feed the k-slots of MFMA pair (2p, 2p + 1); a last 64-channel group is
+  // read 8 bytes per lane (channels 64m + 16g + [0, 16)), as are all groups
+  // of the window and FP8 rows.  chan(m, hf) is the first of the 8 channels
+  // lane (i, g) holds for operand half hf of group slot m; the query
+  // fragments use the same channels.
+  constexpr int NP = (!WIN && !KV8) ? D / 128 : 0;
   constexpr int VST = vs_stride<DV>();
   constexpr int CPW = DV / 4;       // value channels per wave
   constexpr int NT = CPW / 16;      // P.V output tiles per wave
@@ -146,6 +154,10 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
   const int b = (a.row0 + r) / a.T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
+  const uint32_t ghi = 0u - (uint32_t)(g >> 1);  // all ones for g = 2, 3
+  auto chan = [&](int m, int hf) -> int {
+    return (m < 2 * NP) ? 128 * (m >> 1) + 32 * g + 16 * (m & 1) + 8 * hf : 64 * m + 16 * g + 8 * hf;
+  };
   const int rounds = MULTI ? a.rounds : 1;
   // entry of this lane in round rnd: e0 + 64 * rnd
   const int e0 = (WIN ? sidx - a.nsg : sidx) * 64 * rounds + wave * 16 + i;
@@ -200,7 +212,15 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       const int64_t row = (int64_t)b * a.cap + (valid ? ix : 0);
       const uint8_t* cr = a.codes + row * (D / 2);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
+      for (int q = 0; q < NP; ++q) {
+        const uint4 cw = *reinterpret_cast<const uint4*>(cr + 64 * q + 16 * g);
+        w0[2 * q] = cw.x;
+        w1[2 * q] = cw.y;
+        w0[2 * q + 1] = cw.z;
+        w1[2 * q + 1] = cw.w;
+      }
+#pragma unroll
+      for (int m = 2 * NP; m < NM; ++m) {
         const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
         w0[m] = cw.x;
         w1[m] = cw.y;
@@ -232,7 +252,15 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
       const int64_t row = (int64_t)b * a.cap + (pvalid ? ix : 0);
       const uint8_t* cr = a.codes + row * (D / 2);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
+      for (int q = 0; q < NP; ++q) {
+        const uint4 cw = *reinterpret_cast<const uint4*>(cr + 64 * q + 16 * g);
+        p0[2 * q] = cw.x;
+        p1[2 * q] = cw.y;
+        p0[2 * q + 1] = cw.z;
+        p1[2 * q + 1] = cw.w;
+      }
+#pragma unroll
+      for (int m = 2 * NP; m < NM; ++m) {
         const uint2 cw = *reinterpret_cast<const uint2*>(cr + 32 * m + 8 * g);
         p0[m] = cw.x;
         p1[m] = cw.y;
@@ -289,7 +317,7 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        qa[m][hf] = *reinterpret_cast<const f16x8*>(q16 + i * QST + 64 * m + 16 * g + 8 * hf);
+        qa[m][hf] = *reinterpret_cast<const f16x8*>(q16 + i * QST + chan(m, hf));
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) er[rr] = s_qexp[4 * g + rr];
     __syncthreads();  // every wave holds its fragments: the V tile may be written
@@ -350,7 +378,18 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
             k[4 * (q4 & 1) + 3] = hi[1];
           }
         } else if constexpr (!WIN) {
-          const f16x2 s2 = scale_pair(sc[m] >> (8 * g));  // byte g: channels 64m + 16g..
+          // the scale byte of this lane's 16 channels: byte 2 (g & 1) + (m & 1)
+          // of word 2p + g / 2 in a 128-channel group, byte g of word m after
+          // (a bitwise select: a conditional pick of the two words becomes
+          // an indexed register read, which the compiler puts in scratch)
+          uint32_t sb;
+          if (m < 2 * NP) {
+            const uint32_t lo = sc[m & ~1], hi = sc[(m & ~1) + 1];
+            sb = (lo ^ ((lo ^ hi) & ghi)) >> (16 * (g & 1) + 8 * (m & 1));
+          } else {
+            sb = sc[m] >> (8 * g);
+          }
+          const f16x2 s2 = scale_pair(sb);
           k0 = fp4x8_to_f16(w0[m], s2);
           k1 = fp4x8_to_f16(w1[m], s2);
         } else {
@@ -364,8 +403,8 @@ __device__ __forceinline__ void split_body(const AttnArgs& a, int r, int sidx, _
         acc0 = mfma16x16x32(qa[m][0], k0, acc0);
         acc1 = mfma16x16x32(qa[m][1], k1, acc1);
         if (m < NMV) {
-          *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g) = k0;
-          *reinterpret_cast<f16x8*>(vrow + 64 * m + 16 * g + 8) = k1;
+          *reinterpret_cast<f16x8*>(vrow + chan(m, 0)) = k0;
+          *reinterpret_cast<f16x8*>(vrow + chan(m, 1)) = k1;
         }
       }
     }
