@@ -535,11 +535,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
 // Merge kernel.  Unit u of row r is the value-slot pair (2(u % (dv/2)), +1)
 // of head u / (dv/2); SUB consecutive threads merge one unit, thread `sub`
 // taking splits sub, sub + SUB, ...  Each thread loads, per split, its pair
-// of the partial output and the split's max and sum for the unit's head,
-// all requested before any is used; the SUB threads agree on the running
-// maximum and add their shares with lane moves, so the merge needs no LDS
-// and no barrier:
-//   out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s,  lse = M + log L.
+// of the partial output, all requested before any is used, and the split's
+// max and sum for the unit's head (staged once per block in LDS when the
+// row has at most SUB * KB splits, else loaded by every thread); the SUB
+// threads agree on the running maximum and add their shares with lane
+// moves.  With the maxima m_s in base-2 units:
+//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  lse = M ln 2 + log L.
 // One pass of 256 threads merges units [vb * 256 / SUB, (vb + 1) * 256 / SUB)
 // of row r.  COH: the partials were written by blocks of the same launch.
 template <int DV, int SUB, int KB, bool COH>  // KB: splits per thread per pass
@@ -550,6 +551,13 @@ __device__ __forceinline__ void merge_units(const float* __restrict__ part, int3
   constexpr int PSTRIDE = 16 * DV + 32;
   constexpr int UPH = DV / 2;          // units per head
   constexpr int UPB = 256 / SUB;       // units per pass
+  static_assert(UPH % UPB == 0, "a pass lies inside one head");
+  static_assert(2 * SUB * KB <= 256, "one staged value per thread");
+  // Rows of at most SUB * KB splits (one group of splits per thread): the
+  // maxima and sums of the pass's head (every unit of a pass belongs to one
+  // head) are loaded once per block into LDS instead of by every thread.
+  __shared__ float s_ml[2][SUB * KB];
+  const bool staged = nsplit <= SUB * KB;  // the same for the whole block
   const int tid = threadIdx.x, sub = tid % SUB;
   const int u = vb * UPB + tid / SUB;  // the passes cover the units exactly
   const int h = u / UPH, pp = 2 * (u % UPH);
@@ -562,14 +570,36 @@ __device__ __forceinline__ void merge_units(const float* __restrict__ part, int3
     for (int k = 0; k < KB; ++k) {
       const int sc = min(s0 + sub + SUB * k, nsplit - 1);  // clamped: every load in bounds
       const float* ps = prow + (int64_t)sc * PSTRIDE;
-      if constexpr (COH) {
+      if constexpr (COH)
         ov[k] = __builtin_bit_cast(float2, ld_coh(reinterpret_cast<const uint64_t*>(ps + h * DV + pp)));
-        mv[k] = ld_coh(ps + 16 * DV + h);
-        lv[k] = ld_coh(ps + 16 * DV + 16 + h);
-      } else {
+      else
         ov[k] = ld_pair(ps + h * DV + pp);
-        mv[k] = ps[16 * DV + h];
-        lv[k] = ps[16 * DV + 16 + h];
+    }
+    if (staged) {
+      __syncthreads();  // an earlier pass's reads of s_ml are done
+      if (tid < 2 * nsplit) {
+        const float* pm = prow + (int64_t)(tid >> 1) * PSTRIDE + 16 * DV + 16 * (tid & 1) + h;
+        s_ml[tid & 1][tid >> 1] = COH ? ld_coh(pm) : *pm;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int sc = min(sub + SUB * k, nsplit - 1);
+        mv[k] = s_ml[0][sc];
+        lv[k] = s_ml[1][sc];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int sc = min(s0 + sub + SUB * k, nsplit - 1);
+        const float* ps = prow + (int64_t)sc * PSTRIDE;
+        if constexpr (COH) {
+          mv[k] = ld_coh(ps + 16 * DV + h);
+          lv[k] = ld_coh(ps + 16 * DV + 16 + h);
+        } else {
+          mv[k] = ps[16 * DV + h];
+          lv[k] = ps[16 * DV + 16 + h];
+        }
       }
     }
     float cm = -INFINITY;
