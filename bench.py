@@ -112,6 +112,36 @@ def stream_read_peak(nbytes: int = 1 << 30, reps: int = 5) -> dict:
             "kernel": "stream_read_kernel (csa2_stream_read)"}
 
 
+def stream_read_same_size(nbytes: int, reps: int = 40) -> dict:
+    """The streaming-read kernel over `nbytes` per launch (the roofline
+    kernel's bytes), launched back to back over buffers rotated through more
+    than the 256 MB last-level cache, as the scan's launches run: the rate a
+    read of that size reaches with its own start-up and tail included."""
+    import torch
+    from sparse_attention_decode_e2m1_amd import api
+    words = max(4, (nbytes // 16) * 4)  # whole 16-byte words
+    copies = max(2, -(-(768 << 20) // (words * 4)))
+    bufs = [torch.ones(words, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    best_us, per = None, {}
+    for blocks in (512, 1024, 2048, 4096):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        for i in range(copies):
+            api.stream_read(bufs[i], sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            api.stream_read(bufs[i % copies], sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        per[str(blocks)] = round(us, 2)
+        best_us = us if best_us is None else min(best_us, us)
+    del bufs
+    return {"us": round(best_us, 2), "GBps": round(words * 4 / best_us / 1e3, 1), "bytes": words * 4,
+            "us_by_blocks": per}
+
+
 def hierarchical_recall(w, dw) -> list:
     """For a workload whose Full layer keeps a pool: recall of each later
     indexing layer's Top-K (searched inside the pool) against the same layer
@@ -388,6 +418,9 @@ def main():
         if roofline is not None:
             roofline["measured_read_peak_GBps"] = stream["GBps"]
             roofline["frac_of_measured_peak"] = round(roofline["achieved"] / stream["GBps"], 4)
+            same = stream_read_same_size(roofline["bytes_per_launch"])
+            roofline["same_size_read"] = same
+            roofline["frac_of_same_size_read"] = round(roofline["achieved"] / same["GBps"], 4)
         if w.P > 0 and w.T == 1:
             recall = hierarchical_recall(w, dw)
 
