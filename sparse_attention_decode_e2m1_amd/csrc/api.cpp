@@ -114,6 +114,9 @@ constexpr int32_t kRowChunk = CSA2_PASS_ROWS;  // query rows scored / selected /
 // per-row buffers are small (samples, a candidate list, the exact path's
 // score row), and passes this long fill the device in every launch.
 constexpr int32_t kPrefillPassRows = CSA2_PREFILL_PASS_ROWS;
+// Rows per attention launch within a pass: a 1024-row launch's partials
+// (about 170 MB with 5 splits per row) fit the 256 MB last-level cache.
+constexpr int32_t kAttnPassRows = 1024;
 
 // A bump allocator over the caller's workspace.  The per-row control block
 // (kCtlWordsPerRow words) always comes first, so every kind of call finds
@@ -666,7 +669,7 @@ StepLayout step_layout(csa2_mode mode, const csa2_layer_args* a, void* ws, int s
     if (mode == CSA2_MODE_FULL && a->P > 0) L.pscores = c.take<float>((size_t)L.rc * a->P);
     carve_topk(c, L.rc, std::max<int64_t>(L.n_out, a->P), kmax, &L.tw);
   }
-  carve_attn(c, rows, L.rc, a->K, Weff, a->dv, &L.aw, true);
+  carve_attn(c, rows, std::min(L.rc, kAttnPassRows), a->K, Weff, a->dv, &L.aw, true);
   L.bytes = c.off;
   return L;
 }
@@ -841,13 +844,18 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       }
       }
     }
-    const int32_t* idx_att = (mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out) + (size_t)r0 * a->K;
-    CSA2_LAUNCH(3, PROF_STREAM, launch_sparse_attn(a->q + (size_t)r0 * a->H * a->D, nr, a->T, a->D, a->dv, a->kv.codes,
-                                a->kv.scales, a->kv.cap, idx_att, a->K, a->swa, a->swa_scale,
-                                a->swa_pos0, a->S, Weff, qpos, a->sm_scale,
-                                a->out + (size_t)r0 * a->H * a->dv,
-                                a->lse ? a->lse + (size_t)r0 * a->H : nullptr, L.aw, st, r0),
-             "sparse attention launch");
+    // attention in sub-passes of at most kAttnPassRows rows, so a long
+    // pass's partials stay within the last-level cache for the merge
+    for (int32_t a0 = r0; a0 < r0 + nr; a0 += kAttnPassRows) {
+      const int32_t na = std::min(kAttnPassRows, r0 + nr - a0);
+      const int32_t* idx_att = (mode == CSA2_MODE_REUSE ? a->idx_in : a->idx_out) + (size_t)a0 * a->K;
+      CSA2_LAUNCH(3, PROF_STREAM, launch_sparse_attn(a->q + (size_t)a0 * a->H * a->D, na, a->T, a->D, a->dv, a->kv.codes,
+                                  a->kv.scales, a->kv.cap, idx_att, a->K, a->swa, a->swa_scale,
+                                  a->swa_pos0, a->S, Weff, a->q_pos + a0, a->sm_scale,
+                                  a->out + (size_t)a0 * a->H * a->dv,
+                                  a->lse ? a->lse + (size_t)a0 * a->H : nullptr, L.aw, st, a0),
+               "sparse attention launch");
+    }
   }
   return CSA2_OK;
 }
