@@ -59,7 +59,9 @@ def test_c4_pool_1m():
 def test_c5_prefill_chunk_sampled_tokens():
     w = I.WORKLOADS["C5_prefill_4k_on_128k"]
     rng = np.random.default_rng(5)
-    fixed = {0, 1, 127, 128, 255, 256, w.T - 2, w.T - 1}
+    # the first and last tokens, and those around the 2048-row pass and the
+    # 1024-row attention launch boundaries
+    fixed = {0, 1, 1023, 1024, 2047, 2048, 3071, 3072, w.T - 2, w.T - 1}
     rest = [t for t in rng.permutation(w.T).tolist() if t not in fixed][: 64 - len(fixed)]
     tok = sorted(fixed | set(rest))
     assert len(tok) == 64

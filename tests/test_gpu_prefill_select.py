@@ -93,3 +93,22 @@ def test_sampled_prefill_ties_overflow_to_exact_path():
     # tied slots
     tied = a[w.T:]
     assert (tied[:, 0] == 0).all()
+
+
+def test_sampled_prefill_multi_pass_against_oracle():
+    """2560 query tokens: one pass of 2048 rows and one of 512, each attending
+    in launches of at most 1024 rows (1024 + 1024, then 512); tokens at every
+    pass and launch boundary match the oracle."""
+    w = I.small("t_samp_mp", 74, B=1, N=40000, T=2560, K=256, modes=(I.FULL,))
+    dw = Hn.DeviceWorkload(w)
+    dw.step()
+    torch.cuda.synchronize()
+    assert api.topk_last_variant() == api.TOPK_SAMPLED
+    rng = np.random.default_rng(74)
+    fixed = {0, 1, 1023, 1024, 2047, 2048, 2049, w.T - 2, w.T - 1}
+    rest = [t for t in rng.permutation(w.T).tolist() if t not in fixed][: 16 - len(fixed)]
+    tok = sorted(fixed | set(rest))
+    ores, oc = run_group(w, tokens=tok, keep_scores=True)
+    chk = compare_group(w, dw, ores, oc, tokens=tok)
+    assert chk.rows == expected_rows(w, tokens=tok) and chk.same_sets >= len(tok) // 2
+
