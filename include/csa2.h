@@ -213,7 +213,7 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
  * Prefill passes of csa2_layer_step over long contexts (32 or more tokens
  * per sequence, 128-channel index keys, 1 to 4 indexer heads, K <= 2048,
  * 2^15 to 2^18 cache slots, no pool) select without a score matrix
- * (CSA2_TOPK_SAMPLED): every 16th position is scored first and each row's
+ * (CSA2_TOPK_SAMPLED): every 32nd position is scored first and each row's
  * threshold is set from those samples so that about 2K positions pass it;
  * the full scan keeps only the positions at or above it, and the exact
  * Top-K is taken among them.  A row whose kept positions come short of K

@@ -184,8 +184,11 @@ bool topk_row_pass(int32_t rows, int64_t n_max);
 // instead of every score), and the exact Top-K is taken among them.  A row
 // whose candidates come short of K, or overflow the room for them, is
 // scored in full again and selected by the one-block-per-row kernel, so the
-// result never depends on the sample.
-constexpr int kSampleStride = 16;
+// result never depends on the sample.  With a stride of 32 the threshold
+// sits 6.7 standard deviations (of the sample's rank noise) above K for
+// K = 2048 on independent scores (16: 8.7); 2.310 -> 2.274 ms per 4096-token
+// chunk against 16.
+constexpr int kSampleStride = 32;
 constexpr int kCandCap = 8192;    // candidates kept per row
 constexpr int kCandStage = 128;   // list room per token of a scoring block (1 in 8 positions)
 struct SampledSel {

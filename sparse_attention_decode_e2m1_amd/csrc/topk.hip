@@ -1537,7 +1537,7 @@ hipError_t launch_topk_hist(const float* scores, int32_t rows, int64_t n, const 
 // to select takes the exact path.  Also clears the row's candidate count
 // and fail word.
 constexpr int kThrThreads = 512;
-constexpr int kThrPer = 32;  // samples per thread: rows of up to 2^18 slots
+constexpr int kThrPer = 16;  // samples per thread: rows of up to 2^18 slots
 static_assert(kThrThreads * kThrPer * kSampleStride >= kRowTopkMaxN, "samples fit the block");
 __global__ __launch_bounds__(kThrThreads) void sample_threshold_kernel(
     const int32_t* __restrict__ n_valid, int32_t nv_add, int64_t n_max, int32_t k,

@@ -3,6 +3,7 @@ and rejects invalid arguments on the host before launching anything (these
 calls never reach a kernel, so they run without a GPU)."""
 import ctypes
 import subprocess
+import threading
 
 import pytest
 
@@ -191,4 +192,10 @@ def test_topk_variant_and_wait_limit_controls(L):
         assert api.set_wait_limit(123) == 0
     finally:
         api.set_wait_limit(1 << 20)
-    assert api.topk_last_variant() == -1   # no Top-K pass ran on this thread
+    # per host thread: a thread that ran no Top-K pass reads -1 (a fresh
+    # thread, since GPU tests earlier in the same process may have run some)
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(api.topk_last_variant()))
+    th.start()
+    th.join()
+    assert seen == [-1]
