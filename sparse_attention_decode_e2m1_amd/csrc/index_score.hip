@@ -201,33 +201,17 @@ __global__ __launch_bounds__(256) void index_score_kernel(
 
   const int r = blockIdx.y;
   const int b = (row0 + r) / T;
-  // visible entries, clamped to what the score row and the key list hold
-  int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), POOL ? (int64_t)P : cap);
-  const bool fresh_on = !POOL && fresh.ikey;
-  const int64_t nv_all = nv;  // the new position counts as visible to the fresh score
-  // the new position (loaded once: later loads queue behind the scan's)
-  const int64_t p_new = fresh_on ? (int64_t)fresh.q_pos[r] : -1;
-  if (fresh_on) nv = min(nv, max(p_new, (int64_t)0));  // scanned: [0, q_pos)
   const int64_t start = (int64_t)blockIdx.x * chunk;
-  // blocks past the scanned range still take their part of the new rows
-  if (start >= nv && !(fresh_on && (int)blockIdx.x <= (fresh.kv_dim >> 6)))
-    return;  // uniform for the whole block
-  const int64_t end = min(nv, start + chunk);
-
   // the wave index is uniform: kept in a scalar register, the whole-group
   // test below is a scalar branch
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
-
-  if (hist) {
-    for (int k = tid; k < kHistBins; k += 256) lhist[k] = 0u;
-  }
-
   const uint8_t* cbase = codes + (int64_t)b * cap * ROWB;
   const uint8_t* sbase = scales + (int64_t)b * cap * ROWS;
   const int32_t* prow = POOL ? pool + (int64_t)r * P : nullptr;
   float* srow = scores + (int64_t)r * n_out;
+  int64_t end = 0;  // set below, once the row's visible length is known
 
   // Each wave takes groups of GT consecutive tiles (GT KiB of contiguous
   // codes for 128 channels in flat mode); the four waves of a round cover
@@ -235,8 +219,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // current group is computed, into the other of two register buffers.
   // The scale bytes of lane (i, g) are bytes 2g, 2g+1 of each chunk's
   // scales; they are fetched as the aligned 32-bit word holding them.
-  const int ntiles = (int)((end - start + 15) >> 4);
-  const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
   // Whole chunks of a flat scan read every group at fixed offsets from one
   // address; the last chunk of a row (and pool lists) compute each tile's
   // rows, clamped to the range (lanes past the end reload the last position;
@@ -273,23 +255,49 @@ __global__ __launch_bounds__(256) void index_score_kernel(
         }
     }
   };
+  u32x4 cwA[GT][NCH], cwB[GT][NCH];
+  uint32_t swA[GT][NCH], swB[GT][NCH];
+  // The new rows' loads go first, ahead of this wave's scan loads (one wave
+  // of some of the row's blocks, known from the block and wave alone).
+  const bool fresh_on = !POOL && fresh.ikey;
+  const bool fresh_wave = fresh_on && wave == kFreshWave &&
+                          (blockIdx.x == 0 || (int)blockIdx.x <= (fresh.kv_dim >> 6));  // wave-uniform
+  // A flat scan's chunk that lies inside the cache requests its first group
+  // of a whole chunk before the row's visible length arrives (every such
+  // row is allocated, so the loads are in bounds); it is used if the chunk
+  // turns out whole, and requested again per tile otherwise.
+  const bool guess_whole = !POOL && !fresh_wave && chunk == kScoreChunk && start + chunk <= cap;
+  if (guess_whole) load_group(std::false_type{}, 0, cwA, swA);
+
+  // visible entries, clamped to what the score row and the key list hold
+  int64_t nv = min(min((int64_t)n_valid[r] + nv_add, n_out), POOL ? (int64_t)P : cap);
+  const int64_t nv_all = nv;  // the new position counts as visible to the fresh score
+  // the new position (loaded once: later loads queue behind the scan's)
+  const int64_t p_new = fresh_on ? (int64_t)fresh.q_pos[r] : -1;
+  if (fresh_on) nv = min(nv, max(p_new, (int64_t)0));  // scanned: [0, q_pos)
+  // blocks past the scanned range still take their part of the new rows
+  if (start >= nv && !(fresh_on && (int)blockIdx.x <= (fresh.kv_dim >> 6)))
+    return;  // uniform for the whole block
+  end = min(nv, start + chunk);
+
+  if (hist) {
+    for (int k = tid; k < kHistBins; k += 256) lhist[k] = 0u;
+  }
+
+  const int ntiles = (int)((end - start + 15) >> 4);
+  const int nrounds = (ntiles + 4 * GT - 1) / (4 * GT);
   const int sshift = 16 * (g & 1);
 
   const bool whole = !POOL && chunk == kScoreChunk && end - start == chunk;  // block-uniform
-  u32x4 cwA[GT][NCH], cwB[GT][NCH];
-  uint32_t swA[GT][NCH], swB[GT][NCH];
-  // the first group is requested before the query is prepared, so the
-  // scan's first HBM round trip overlaps the query's
-  // the new rows' loads go first, ahead of this wave's scan loads
-  const bool fresh_wave = fresh_on && wave == kFreshWave &&
-                          (blockIdx.x == 0 || (int)blockIdx.x <= (fresh.kv_dim >> 6));  // wave-uniform
   const bool idx_part = fresh_on && blockIdx.x == 0;
   FreshRegs fr;
   if (fresh_wave) {
     if (fresh.bf16) fresh_load<uint16_t>(fresh, r, HI, q_idx, w, idx_part, fr);
     else fresh_load<float>(fresh, r, HI, q_idx, w, idx_part, fr);
   }
-  if (nrounds > 0) {
+  // the first group is requested before the query is prepared, so the
+  // scan's first HBM round trip overlaps the query's
+  if (nrounds > 0 && !(whole && guess_whole)) {
     if (whole) load_group(std::false_type{}, 0, cwA, swA);
     else load_group(std::true_type{}, 0, cwA, swA);
   }
