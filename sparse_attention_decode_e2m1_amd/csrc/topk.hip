@@ -1255,11 +1255,13 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowCand = 4096;
 
 // The bin (of nbins, counted from the top) where the running count from the
-// top reaches `need` (1 <= need <= total); *bin and *above (count in the bins
-// above it) are written by the thread that finds it.
+// top reaches `need` (1 <= need <= total); *bin, *above (count in the bins
+// above it) and, if given, *count (the bin's own count) are written by the
+// thread that finds it.
 template <int NT>
 __device__ __forceinline__ void find_bin_desc(const uint32_t* h, int nbins, uint32_t need,
-                                              uint32_t* tmp, uint32_t* bin, uint32_t* above) {
+                                              uint32_t* tmp, uint32_t* bin, uint32_t* above,
+                                              uint32_t* count = nullptr) {
   const int tid = threadIdx.x;
   constexpr int BPT = kHistBins / NT;  // at most 4 bins per thread
   const int bpt = nbins >= NT ? nbins / NT : 1;
@@ -1278,6 +1280,7 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* h, int nbins, uint
     if (q < bpt && acc < need && acc + c[q] >= need) {
       *bin = (uint32_t)(nbins - 1 - (tid * bpt + q));
       *above = acc;
+      if (count) *count = c[q];
     }
     acc += c[q];
   }
@@ -1604,7 +1607,7 @@ __global__ __launch_bounds__(kFinThreads) void sampled_final_kernel(
   extern __shared__ uint32_t fin_lds[];
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t tmp[NT / 64];
-  __shared__ uint32_t s_bin, s_above;
+  __shared__ uint32_t s_bin, s_above, s_cnt;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n_max), (int64_t)0);
   const uint32_t need = (uint32_t)min((int64_t)k, nv);
@@ -1642,9 +1645,17 @@ __global__ __launch_bounds__(kFinThreads) void sampled_final_kernel(
         if (tid + q * NT < c && (hi == 32 || (ck[q] >> hi) == pre))
           atomicAdd(&hist[(ck[q] >> shift) & (uint32_t)(nb - 1)], 1u);
       __syncthreads();
-      find_bin_desc<NT>(hist, nb, need - above, tmp, &s_bin, &s_above);
+      find_bin_desc<NT>(hist, nb, need - above, tmp, &s_bin, &s_above, &s_cnt);
       above += s_above;
       pre = (hi == 32 ? 0u : (pre << (hi - shift))) | s_bin;
+      // the bin holds exactly the keys still needed: every key with this
+      // prefix is kept, so the threshold is the key just below the prefix
+      // (no tie left to resolve) and the finer digits are not needed
+      if (lvl < 2 && s_cnt == need - above && (pre << shift) != 0u) {
+        above += s_cnt;
+        pre = (pre << shift) - 1u;
+        break;
+      }
     }
     T = pre;
   }
