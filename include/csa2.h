@@ -220,7 +220,16 @@ csa2_status csa2_topk(const float* scores, int32_t rows, int64_t n, const int32_
  * or overflow their room is scored in full and selected by the ROW kernel,
  * so the result is the same index set, in the same order, as the other
  * variants give.  CSA2_TOPK_ROW or any score-matrix variant forced for such
- * a pass runs it the older way. */
+ * a pass runs it the older way.
+ *
+ * Rows of at most 2^14 slots (a candidate pool's rows, short contexts)
+ * select with one block per row and the row's keys in registers
+ * (CSA2_TOPK_BAND): a 1024-key sample brackets the K-th largest key between
+ * two keys with a wide margin, one pass counts the keys above the bracket
+ * and lists those inside it, and the exact K-th is found among the listed
+ * keys.  When the bracket misses (or too many keys share it, as with many
+ * equal scores) the block runs the exact selection of the ROW kernel
+ * instead: the index set and its order never depend on the sample. */
 typedef enum {
   CSA2_TOPK_AUTO = 0,             /* chosen from the shape */
   CSA2_TOPK_ROW = 1,              /* one block per row, in LDS (rows of <= 2^18 slots) */
@@ -230,7 +239,9 @@ typedef enum {
   CSA2_TOPK_SELECT_LARGE = 5,     /* 16384-score blocks; the row's last block finishes */
   CSA2_TOPK_SELECT_LARGE_CUT = 6, /* ... after the cut kernel */
   CSA2_TOPK_SAMPLED = 7,          /* prefill passes: sampled threshold, candidates only */
-  CSA2_TOPK_SAMPLED_FALLBACK = 8  /* ... with every row sent to the exact path */
+  CSA2_TOPK_SAMPLED_FALLBACK = 8, /* ... with every row sent to the exact path */
+  CSA2_TOPK_BAND = 9,             /* one block per row of <= 2^14 slots: a sampled key band */
+  CSA2_TOPK_BAND_EXACT = 10       /* ... with every row sent to the block's exact selection */
 } csa2_topk_variant;
 /* Flag in csa2_topk_last_variant(): the finishing block merged two sorted
  * lists (rows over 2^19 slots) instead of reading back a bitmap. */

@@ -24,7 +24,7 @@ HEADS = 16
 ERR_INCOMPLETE = 7
 # csa2_topk_variant
 TOPK_AUTO, TOPK_ROW, TOPK_ONE_WAIT, TOPK_SELECT, TOPK_SELECT_CUT, TOPK_SELECT_LARGE, \
-    TOPK_SELECT_LARGE_CUT, TOPK_SAMPLED, TOPK_SAMPLED_FALLBACK = range(9)
+    TOPK_SELECT_LARGE_CUT, TOPK_SAMPLED, TOPK_SAMPLED_FALLBACK, TOPK_BAND, TOPK_BAND_EXACT = range(11)
 TOPK_LIST_FINISH = 16
 
 c_i32, c_i64, c_f32, c_p, c_sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,

@@ -90,7 +90,9 @@ enum TopkVariant : int32_t {
   kTopkSelectLargeCut = 6,
   kTopkSampled = 7,          // prefill: a sampled threshold, then the candidates above it only
   kTopkSampledFallback = 8,  // ... with every row sent to the exact path (a test of that path)
-  kTopkVariants = 9,
+  kTopkBand = 9,             // one block per row, a sampled key band (rows <= kRowTopkSmallN slots)
+  kTopkBandExact = 10,       // ... with every row sent to its exact LDS selection (a test of that path)
+  kTopkVariants = 11,
 };
 constexpr int32_t kTopkListFinish = 16;  // flag: the finishing block merged sorted lists
 int32_t topk_variant_forced();

@@ -1289,14 +1289,17 @@ __device__ __forceinline__ void find_bin_desc(const uint32_t* h, int nbins, uint
 
 // SMALL: rows of at most kRowTopkSmallN slots, whose keys the block loads
 // once into registers (16 per thread) and every pass reads from there.
-template <bool SMALL>
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
-    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
-    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, int32_t nwp, const uint32_t* __restrict__ only) {
-  constexpr int NT = kRowThreads, NW = NT / 64, UN = 8;
-  if (only && only[blockIdx.x] == 0u) return;  // a row the sampled selection has finished
-  extern __shared__ uint32_t lds[];
+// The selection of row r by one block of NT threads (every thread calls
+// it); `lds` is the block's dynamic LDS (kHistBins + 2 nwp + 2 kRowCand words).
+template <bool SMALL, int NT = kRowThreads>
+__device__ __forceinline__ void row_select(int r, const float* __restrict__ scores, int64_t n,
+                                           const int32_t* __restrict__ n_valid, int32_t nv_add,
+                                           const int32_t* __restrict__ slot_pos, int32_t k,
+                                           int32_t* __restrict__ idx_out,
+                                           int32_t* __restrict__ count_out, int32_t nwp,
+                                           uint32_t* lds) {
+  constexpr int NW = NT / 64, UN = 8;
+  static_assert(!SMALL || NT == kRowThreads, "register batches of the row kernel");
   uint32_t* hist = lds;               // kHistBins
   uint32_t* keep = hist + kHistBins;  // nwp words: slots kept
   uint32_t* tie = keep + nwp;         // nwp words: slots whose key equals the threshold
@@ -1304,7 +1307,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   uint32_t* cslot = ckey + kRowCand;  // and their slots
   __shared__ uint32_t tmp[NW];
   __shared__ uint32_t s_bin, s_above, s_ncand;
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n), (int64_t)0);
   const float* srow = scores + (int64_t)r * n;
   const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
@@ -1494,16 +1497,367 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   if (count_out && tid == 0) count_out[r] = k;
 }
 
+template <bool SMALL>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
+    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
+    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, int32_t nwp, const uint32_t* __restrict__ only) {
+  if (only && only[blockIdx.x] == 0u) return;  // a row the sampled selection has finished
+  extern __shared__ uint32_t lds[];
+  row_select<SMALL>(blockIdx.x, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp,
+                    lds);
+}
+
+// ------------------------------------------- one block per row: key band
+// Rows of up to 2^14 slots (a candidate pool's rows, short contexts), one
+// block of kBandThreads per row with the row's keys in registers (key 0,
+// below every score's key, past the visible slots).  The per-key steps are
+// ballots and lane counts, no per-key LDS atomic:
+//   1. a sample of 4096 keys (4 per thread, spread over the row) is histogrammed
+//      in 4096 bins over its own key range; the bins where the sample's
+//      count from the top reaches e -+ (4 sqrt(e) + 8), e = k * samples /
+//      slots the expected sample count above the k-th key, give two keys
+//      1 <= L <= H;
+//   2. one pass counts the keys at or above H and lists the keys in [L, H)
+//      with their slots in LDS (ballots and lane counts);
+//   3. if A = count(>= H) < k <= A + listed, the k-th largest of the row is
+//      the (k - A)-th largest of the list: a 12-bit histogram of the listed
+//      keys relative to L gives its bin, and that bin's members are ranked
+//      directly (key, then the lower slot);
+//   4. the kept slots (key above the threshold's, or equal with a slot not
+//      after its) are written in slot order from one ballot per register.
+// The sample only sets the bracket: when it misses (or the list or the cut
+// bin overflows) the block runs the exact LDS selection of the row kernel
+// instead, so the result is the same index set and order either way.
+constexpr int kBandThreads = kRowThreads;  // 16 waves hide the latency of each step
+constexpr int kBandCand = 4096;  // listed keys of the bracket
+constexpr int kBandRank = 1024;  // members of the cut bin ranked directly
+
+// Maximum over the wave (every lane gets it): DPP row shifts and row
+// broadcasts, then lane 63's value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0x111, 0xF>(x));  // row_shr:1 (lanes without a source see 0)
+  x = max(x, dpp_u32<0x112, 0xF>(x));  // row_shr:2
+  x = max(x, dpp_u32<0x114, 0xF>(x));  // row_shr:4
+  x = max(x, dpp_u32<0x118, 0xF>(x));  // row_shr:8
+  x = max(x, dpp_u32<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
+  x = max(x, dpp_u32<0x143, 0xC>(x));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Popcount of m's bits below this lane, plus c.
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m, uint32_t c) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, c));
+}
+
+// The bins (of kHistBins, counted from the top) where the running count
+// from the top reaches need_a and need_b (each 0 to skip, else 1 <= need <=
+// total): written to bin[0], bin[1] (and the count above bin[0] and its own
+// count to *above_a, *count_a) by the threads that find them.  One scan.
+template <int NT>
+__device__ __forceinline__ void find_two_desc(const uint32_t* h, uint32_t need_a, uint32_t need_b,
+                                              uint32_t* tmp, uint32_t* bin, uint32_t* above_a,
+                                              uint32_t* count_a) {
+  constexpr int BPT = kHistBins / NT;
+  static_assert(BPT % 4 == 0, "16-byte reads");
+  const int tid = threadIdx.x;
+  // thread t takes bins BPT (NT - 1 - t) .. + BPT - 1, read as 16-byte words
+  const uint4* hp = reinterpret_cast<const uint4*>(h) + (NT - 1 - tid) * (BPT / 4);
+  uint32_t c[BPT];  // from the top
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int j = 0; j < BPT / 4; ++j) {
+    const uint4 hv = hp[BPT / 4 - 1 - j];
+    c[4 * j] = hv.w;
+    c[4 * j + 1] = hv.z;
+    c[4 * j + 2] = hv.y;
+    c[4 * j + 3] = hv.x;
+    sum += hv.x + hv.y + hv.z + hv.w;
+  }
+  uint32_t tot;
+  uint32_t acc = block_scan<NT>(sum, tmp, &tot);
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const uint32_t b = (uint32_t)(kHistBins - 1 - (tid * BPT + q));
+    if (acc < need_a && acc + c[q] >= need_a) {
+      bin[0] = b;
+      *above_a = acc;
+      *count_a = c[q];
+    }
+    if (acc < need_b && acc + c[q] >= need_b) bin[1] = b;
+    acc += c[q];
+  }
+  __syncthreads();
+}
+
+template <int G>  // 4G keys per thread: rows of up to 4G * kBandThreads slots
+__global__ __launch_bounds__(kBandThreads) void topk_band_kernel(
+    const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
+    int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, int32_t nwp, uint32_t force_exact) {
+  constexpr int NT = kBandThreads, NW = NT / 64, PER = 4 * G;
+  static_assert(G >= 1 && G * NW <= 64, "segment counts in one wave");
+  extern __shared__ uint32_t lds[];
+  uint32_t* hist = lds;                // kHistBins bins (later the cut bin's members)
+  uint32_t* ckey = hist + kHistBins;   // kBandCand listed keys
+  uint32_t* cslot = ckey + kBandCand;  // and their slots
+  __shared__ uint32_t tmp[NW];
+  __shared__ uint32_t s_red[3][NW];
+  __shared__ uint32_t s_cnt[G * NW];
+  __shared__ uint32_t s_bin[2], s_above, s_count, s_ncand, s_nrank, s_ties;
+  __shared__ uint64_t s_thr;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nv = max(min((int64_t)n_valid[r] + nv_add, n), (int64_t)0);
+  const float* srow = scores + (int64_t)r * n;
+  const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
+  int32_t* orow = idx_out + (int64_t)r * k;
+  if (nv <= k) {  // every visible slot is kept, in place
+    for (int64_t s = tid; s < k; s += NT) orow[s] = (s < nv) ? (sp ? sp[s] : (int32_t)s) : -1;
+    if (count_out && tid == 0) count_out[r] = (int32_t)nv;
+    return;
+  }
+  if (nv > (int64_t)PER * NT) {  // not a shape of this kernel: the exact selection
+    row_select<false, NT>(r, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, lds);
+    return;
+  }
+  const int nvi = (int)nv;
+  // Register group g of thread t holds slots 4 (g NT + t) + c, c = 0..3
+  // (16-byte loads; the host launches this kernel only for rows of a
+  // multiple of 4 slots, so a group is within the row whenever its first
+  // slot is).  The sample is group (t / 4) mod G of thread t, loaded first.
+  int ss[4];
+  uint32_t ks[4];
+  {
+    const int s0 = 4 * (((tid >> 2) % G) * NT + tid);
+    const float4 sv4 = (s0 < nvi) ? *reinterpret_cast<const float4*>(srow + s0)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float sf[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ss[j] = s0 + j;
+      ks[j] = (ss[j] < nvi) ? score_key(sf[j]) : 0u;
+    }
+  }
+  float4 v[G];
+  int4 pos[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int s0 = 4 * (g * NT + tid);
+    v[g] = (s0 < nvi) ? *reinterpret_cast<const float4*>(srow + s0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (sp) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int s0 = 4 * (g * NT + tid);
+      pos[g] = (s0 < nvi) ? *reinterpret_cast<const int4*>(sp + s0) : make_int4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kHistBins / (4 * NT); ++j)
+    reinterpret_cast<uint4*>(hist)[tid + j * NT] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) {
+    s_ncand = 0u;
+    s_nrank = 0u;
+    s_ties = 0u;
+  }
+
+  // ---- 1. the sample: its count, key range and histogram
+  {
+    uint32_t nmn = 0u, mx = 0u, c = 0u;  // per thread: ~min, max, count
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool sv = ss[j] < nvi;
+      nmn = max(nmn, sv ? ~ks[j] : 0u);
+      mx = max(mx, sv ? ks[j] : 0u);
+      c += (uint32_t)__popcll(__ballot(sv));
+    }
+    const uint32_t mn = ~wave_max_u32(nmn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+      s_red[0][wave] = mn;
+      s_red[1][wave] = mx;
+      s_red[2][wave] = c;
+    }
+  }
+  __syncthreads();
+  uint32_t bmin = 0xFFFFFFFFu, bmax = 0u, ns = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    bmin = min(bmin, s_red[0][w]);
+    bmax = max(bmax, s_red[1][w]);
+    ns += s_red[2][w];
+  }
+  // ns >= 1: slot 0 (thread 0, j = 0) is sampled and visible
+  const uint32_t span = bmax - bmin;
+  const int sh = span >= (uint32_t)kHistBins ? 32 - __clz((int)span) - 12 : 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (ss[j] < nvi) atomicAdd(&hist[(ks[j] - bmin) >> sh], 1u);
+  __syncthreads();
+  const float e = (float)k * (float)ns / (float)nvi;
+  const float m = 4.0f * sqrtf(e) + 8.0f;
+  const int r_hi = (int)floorf(e - m), r_lo = (int)ceilf(e + m);
+  // r_hi < e < ns (k < visible slots); r_lo past ns: no lower bracket
+  find_two_desc<NT>(hist, r_hi >= 1 ? (uint32_t)r_hi : 0u, r_lo <= (int)ns ? (uint32_t)r_lo : 0u,
+                    tmp, s_bin, &s_above, &s_count);
+  uint32_t H = 0xFFFFFFFFu, L = 1u;  // no finite score's key reaches 0xFFFFFFFF
+  bool hnone = true;
+  if (r_hi >= 1) {
+    const uint64_t h64 = (uint64_t)bmin + ((uint64_t)(s_bin[0] + 1u) << sh);
+    hnone = h64 >= 0xFFFFFFFFull;
+    H = hnone ? 0xFFFFFFFFu : (uint32_t)h64;
+  }
+  if (r_lo <= (int)ns) L = max(bmin + (s_bin[1] << sh), 1u);
+  // the bins are read (the find ends with a barrier): clear them for step 3
+#pragma unroll
+  for (int j = 0; j < kHistBins / (4 * NT); ++j)
+    reinterpret_cast<uint4*>(hist)[tid + j * NT] = make_uint4(0u, 0u, 0u, 0u);
+
+  // ---- 2. count at or above H, list [L, H)
+  uint32_t key[PER];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int s0 = 4 * (g * NT + tid);
+    key[4 * g] = (s0 < nvi) ? score_key(v[g].x) : 0u;
+    key[4 * g + 1] = (s0 + 1 < nvi) ? score_key(v[g].y) : 0u;
+    key[4 * g + 2] = (s0 + 2 < nvi) ? score_key(v[g].z) : 0u;
+    key[4 * g + 3] = (s0 + 3 < nvi) ? score_key(v[g].w) : 0u;
+  }
+  {
+    uint32_t na = 0u, nc = 0u;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const uint64_t mab = __ballot(key[x] >= H);
+      const uint64_t mge = __ballot(key[x] >= L);
+      na += (uint32_t)__popcll(mab);
+      nc += (uint32_t)__popcll(mge & ~mab);
+    }
+    uint32_t cb = 0u;
+    if (lane == 0) {
+      s_red[0][wave] = na;
+      if (nc) cb = atomicAdd(&s_ncand, nc);
+    }
+    cb = (uint32_t)__builtin_amdgcn_readfirstlane((int)cb);
+    if (cb + nc <= (uint32_t)kBandCand) {  // else the list overflows: the exact path below
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const bool bd = key[x] >= L && key[x] < H;
+        const uint64_t mb = __ballot(bd);
+        if (bd) {
+          const uint32_t p = lane_rank(mb, cb);
+          ckey[p] = key[x];
+          cslot[p] = (uint32_t)(4 * ((x >> 2) * NT + tid) + (x & 3));
+        }
+        cb += (uint32_t)__popcll(mb);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t A = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) A += s_red[0][w];
+  const uint32_t ncand = s_ncand;
+  if (force_exact || A >= (uint32_t)k || A + ncand < (uint32_t)k || ncand > (uint32_t)kBandCand) {
+    __syncthreads();  // every thread has read s_red and s_ncand
+    row_select<false, NT>(r, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, lds);
+    return;
+  }
+
+  // ---- 3. the (k - A)-th largest listed key: its bin relative to L, then
+  // the bin's members ranked directly
+  const uint32_t need = (uint32_t)k - A;
+  const uint32_t top = hnone ? bmax : H - 1u;  // the listed keys are below H
+  const uint32_t span2 = top > L ? top - L : 0u;
+  const int sh2 = span2 >= (uint32_t)kHistBins ? 32 - __clz((int)span2) - 12 : 0;
+  auto digit = [&](uint32_t kk) { return min((kk - L) >> sh2, (uint32_t)(kHistBins - 1)); };
+  for (uint32_t c = tid; c < ncand; c += NT) atomicAdd(&hist[digit(ckey[c])], 1u);
+  __syncthreads();
+  find_two_desc<NT>(hist, need, 0u, tmp, s_bin, &s_above, &s_count);
+  const uint32_t dc = s_bin[0], rem = need - s_above, cnt_c = s_count;
+  if (cnt_c > (uint32_t)kBandRank) {  // thousands of keys in one bin (ties): the exact selection
+    __syncthreads();
+    row_select<false, NT>(r, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, lds);
+    return;
+  }
+  uint64_t* mem = reinterpret_cast<uint64_t*>(hist);  // the bins are read: members go here
+  for (uint32_t c = tid; c < ncand; c += NT) {
+    const uint32_t kk = ckey[c];
+    if (digit(kk) == dc) mem[atomicAdd(&s_nrank, 1u)] = rank_value(kk, cslot[c]);
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < cnt_c; i += NT) {
+    const uint64_t x = mem[i];
+    uint32_t rk = 0u;
+    for (uint32_t j = 0; j < cnt_c; ++j) rk += (mem[j] > x) ? 1u : 0u;
+    if (rk + 1u == rem) s_thr = x;
+  }
+  __syncthreads();
+  const uint64_t thr = s_thr;
+  const uint32_t TK = (uint32_t)(thr >> 32), TS = rank_slot(thr);
+  for (uint32_t i = tid; i < cnt_c; i += NT)
+    if ((uint32_t)(mem[i] >> 32) == TK && rank_slot(mem[i]) != TS)
+      s_ties = 1u;  // another key equals the threshold's
+  __syncthreads();
+  const bool ties = s_ties != 0u;
+
+  // ---- 4. kept slots in slot order.  Segment (g, wave) is the 256
+  // consecutive slots 4 (g NT + 64 wave) .. + 255, lane-major; a lane's kept
+  // slots of the group take consecutive places after those of the lanes
+  // below it.
+  uint32_t sel[G], lex[G];
+  uint32_t pcv = 0u;  // lane g: the count of segment (g, wave)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t kk = key[4 * g + c];
+      const uint32_t s = (uint32_t)(4 * (g * NT + tid) + c);
+      const bool kept = ties ? (kk > TK || (kk == TK && s <= TS)) : kk >= TK;
+      bits |= kept ? (1u << c) : 0u;
+    }
+    sel[g] = bits;
+    const uint32_t cnt = (uint32_t)__popc(bits);
+    const uint32_t inc = wave_incl_scan(cnt);
+    lex[g] = inc - cnt;
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    pcv = (lane == g) ? tot : pcv;
+  }
+  if (lane < G) s_cnt[lane * NW + wave] = pcv;
+  __syncthreads();
+  // exclusive prefix of the segment counts in (g, wave) order: lane l holds
+  // entry l = g NW + wave
+  const uint32_t cl = lane < G * NW ? s_cnt[lane] : 0u;
+  const uint32_t pre = wave_incl_scan(cl) - cl;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t p = (uint32_t)__builtin_amdgcn_readlane((int)pre, g * NW + wv) + lex[g];
+    const uint32_t bits = sel[g];
+    const int s0 = 4 * (g * NT + tid);
+    const int q[4] = {pos[g].x, pos[g].y, pos[g].z, pos[g].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if ((bits >> c) & 1u) {
+        if (p < (uint32_t)k) orow[p] = sp ? q[c] : s0 + c;
+        ++p;
+      }
+    }
+  }
+  if (count_out && tid == 0) count_out[r] = k;
+}
+
 // The forced variant as the score-matrix selection sees it (the sampled
 // prefill variants leave these passes their own choice).
 static int32_t forced_select_variant() {
   const int32_t f = topk_variant_forced();
-  return f >= kTopkSampled ? (int32_t)kTopkAuto : f;
+  return (f == kTopkSampled || f == kTopkSampledFallback) ? (int32_t)kTopkAuto : f;
 }
 
 bool topk_row_pass(int32_t rows, int64_t n_max) {
   const int32_t f = forced_select_variant();
   if (f == kTopkRow) return n_max <= kRowTopkMaxN;
+  if (f == kTopkBand || f == kTopkBandExact) return n_max <= kRowTopkSmallN;
   if (f != kTopkAuto) return false;
   return (rows >= kRowTopkMinRows && n_max <= kRowTopkMaxN) || n_max <= kRowTopkSmallN;
 }
@@ -1736,11 +2090,12 @@ static hipError_t raise_row_lds() {
   static const hipError_t raised = []() {
     const int bytes = (int)((kHistBins + 2 * ((kRowTopkMaxN / 32 + 3) & ~3) + 2 * kRowCand) *
                             sizeof(uint32_t));
-    hipError_t e = hipFuncSetAttribute((const void*)topk_row_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)topk_row_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    const void* fns[] = {(const void*)topk_row_kernel<false>, (const void*)topk_row_kernel<true>,
+                         (const void*)topk_band_kernel<1>, (const void*)topk_band_kernel<2>,
+                         (const void*)topk_band_kernel<4>};
+    hipError_t e = hipSuccess;
+    for (const void* f : fns)
+      if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     return e;
   }();
   return raised;
@@ -1771,6 +2126,25 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
     const size_t lds = (size_t)(kHistBins + 2 * nwp + 2 * kRowCand) * sizeof(uint32_t);
     hipError_t e = raise_row_lds();
     if (e != hipSuccess) return e;
+    // rows of up to 2^14 slots: the key band (unless the row kernel is forced)
+    const int32_t fv = forced_select_variant();
+    // (16-byte loads: row strides of a multiple of 4 slots, aligned bases)
+    const bool aligned = n % 4 == 0 && ((uintptr_t)scores & 15u) == 0 &&
+                         ((uintptr_t)slot_pos & 15u) == 0;
+    if (fv != kTopkRow && n_max <= kRowTopkSmallN && aligned) {
+      const uint32_t exact = fv == kTopkBandExact ? 1u : 0u;
+      if (n_max <= 4 * kBandThreads)
+        CSA2_KERNEL(true, true, topk_band_kernel<1>, dim3((unsigned)rows), dim3(kBandThreads), lds,
+                    st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, exact);
+      else if (n_max <= 8 * kBandThreads)
+        CSA2_KERNEL(true, true, topk_band_kernel<2>, dim3((unsigned)rows), dim3(kBandThreads), lds,
+                    st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, exact);
+      else
+        CSA2_KERNEL(true, true, topk_band_kernel<4>, dim3((unsigned)rows), dim3(kBandThreads), lds,
+                    st, scores, n, n_valid, nv_add, slot_pos, k, idx_out, count_out, nwp, exact);
+      set_topk_last(exact ? kTopkBandExact : kTopkBand);
+      return hipGetLastError();
+    }
     // rows of more than one batch and at most kRowTopkSmallN slots keep
     // their keys in registers (a 16K pool row: 1.8 us less per step of
     // three; a 4K row loads one batch either way and is faster without)
@@ -1785,7 +2159,8 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
   }
   // A variant forced by csa2_set_topk_variant runs when the pass allows it;
   // otherwise the choice falls back to the shape's own.
-  const int32_t forced = forced_select_variant();
+  int32_t forced = forced_select_variant();
+  if (forced == kTopkBand || forced == kTopkBandExact) forced = kTopkAuto;  // rows too long for it
   // Passes whose blocks can all be resident at once take the one-wait variant.
   if (forced == kTopkAuto || forced == kTopkOneWait) {
     const int32_t nblk = topk_blocks(n_max, kTopkChunk);

@@ -183,7 +183,9 @@ def test_topk_variant_and_wait_limit_controls(L):
         assert api.set_topk_variant(api.TOPK_AUTO) == api.TOPK_AUTO   # 42 was stored as AUTO
         assert api.set_topk_variant(-3) == api.TOPK_AUTO
         assert api.set_topk_variant(api.TOPK_SAMPLED_FALLBACK) == api.TOPK_AUTO
-        assert api.set_topk_variant(api.TOPK_SAMPLED_FALLBACK + 1) == api.TOPK_SAMPLED_FALLBACK
+        assert api.set_topk_variant(api.TOPK_BAND) == api.TOPK_SAMPLED_FALLBACK
+        assert api.set_topk_variant(api.TOPK_BAND_EXACT) == api.TOPK_BAND
+        assert api.set_topk_variant(api.TOPK_BAND_EXACT + 1) == api.TOPK_BAND_EXACT
         assert api.set_topk_variant(api.TOPK_AUTO) == api.TOPK_AUTO   # one past the last: AUTO
     finally:
         api.set_topk_variant(api.TOPK_AUTO)

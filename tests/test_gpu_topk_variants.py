@@ -135,6 +135,54 @@ def test_row_variant(kind):
         _check(s, nv, k, api.TOPK_ROW)
 
 
+BAND_SHAPES = [  # (n, visible slots per row): 16 / 8 / 4 keys per thread, partial rows
+    (16384, (16384, 16383, 9000, 2049)),
+    (12000, (12000, 11999, 5000, 1025)),
+    (8192, (8192, 4097, 3000, 300)),
+    (4096, (4096, 4095, 1000, 100)),
+]
+
+
+@pytest.mark.parametrize("name,variant", [("band", api.TOPK_BAND),
+                                          ("band_exact", api.TOPK_BAND_EXACT)],
+                         ids=["band", "band_exact"])
+@pytest.mark.parametrize("n,nvs", BAND_SHAPES, ids=[str(b[0]) for b in BAND_SHAPES])
+@pytest.mark.parametrize("kind", ["normal", "ties", "salient"])
+def test_band_variant(name, variant, n, nvs, kind):
+    """One block per row of up to 2^14 slots with a sampled key band, and the
+    same block's exact path (forced): K from 1 to past the visible count."""
+    s = _scores(len(nvs), n, 80 + n % 97, kind)
+    nv = np.array(nvs, np.int32)
+    api.set_topk_variant(variant)
+    for k in (1, 33, 256, 2048, 3500, 16384):
+        _check(s, nv, k, variant)
+
+
+def test_band_is_the_automatic_choice_for_short_rows():
+    s = _scores(2, 16384, 81, "salient")
+    nv = np.array([16384, 7000], np.int32)
+    _check(s, nv, 2048, api.TOPK_BAND)
+    s = _scores(1, 4096, 82, "normal")
+    _check(s, np.array([4096], np.int32), 256, api.TOPK_BAND)
+
+
+@functools.lru_cache(maxsize=None)
+def _pool_scores():
+    rng = np.random.default_rng(83)
+    top = np.sort(rng.standard_normal(1 << 20).astype(np.float32))[-16384:]
+    return np.stack([rng.permutation(top), rng.permutation(top)])  # cached: never written
+
+
+def test_band_narrow_pool_scores():
+    """A pool's scores: the top 16384 of a million, so every key shares its
+    leading bits (the sample's own key range sets the bins)."""
+    rows = _pool_scores()
+    nv = np.array([16384, 16000], np.int32)
+    api.set_topk_variant(api.TOPK_BAND)
+    for k in (1, 2048, 8000):
+        _check(rows, nv, k, api.TOPK_BAND)
+
+
 def test_forced_variant_that_cannot_serve_falls_back():
     """ROW cannot take rows over 2^18 slots; the pass keeps its own choice."""
     s = _scores(2, 300_000, 73, "normal")
@@ -152,7 +200,8 @@ def test_slot_map_on_every_variant():
     pool = np.stack([np.sort(rng.choice(1 << 20, P, replace=False)) for _ in range(2)]).astype(np.int32)
     s = _scores(2, P, 75, "salient")
     nv = np.array([P, 9000], np.int32)
-    for name, v in [("row", api.TOPK_ROW), ("one_wait", api.TOPK_ONE_WAIT)] + SELECT_VARIANTS:
+    for name, v in [("row", api.TOPK_ROW), ("one_wait", api.TOPK_ONE_WAIT), ("band", api.TOPK_BAND),
+                    ("band_exact", api.TOPK_BAND_EXACT)] + SELECT_VARIANTS:
         api.set_topk_variant(v)
         _check(s, nv, 2048, v, slot_pos=pool)
 
