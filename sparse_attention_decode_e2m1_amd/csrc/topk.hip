@@ -1072,7 +1072,6 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nv = min((int64_t)n_valid[r] + nv_add, n);
   const int64_t start = (int64_t)blockIdx.x * kTopkChunk;
-  const int64_t wstart = start + (int64_t)wave * 64 * PL;  // wave's slots: wstart + 64j + lane
   uint32_t* rh = w.hist + (int64_t)r * w.hist_stride;
   int32_t* orow = idx_out + (int64_t)r * k;
   const int32_t* sp = slot_pos ? slot_pos + (int64_t)r * n : nullptr;
@@ -1105,24 +1104,28 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
     }
   } else {
     const float* srow = scores + (int64_t)r * n;
+    // block-relative slots: thread slot wrel + 64 j is visible iff below nvb
+    const int nvb = (int)min(nv - start, (int64_t)kTopkChunk);
+    const int wrel = wave * 64 * PL + lane;
     float v[PL];
 #pragma unroll
-    for (int j = 0; j < PL; ++j) v[j] = srow[min(wstart + 64 * j + lane, nv - 1)];
+    for (int j = 0; j < PL; ++j) v[j] = srow[start + min(wrel + 64 * j, nvb - 1)];
 #pragma unroll
-    for (int j = 0; j < PL; ++j) pos[j] = sp ? sp[min(wstart + 64 * j + lane, nv - 1)] : 0;
+    for (int j = 0; j < PL; ++j) pos[j] = sp ? sp[start + min(wrel + 64 * j, nvb - 1)] : 0;
     if (tid == 0) s_b1 = 0x7FFFFFFF;  // replaced below; keeps an inconsistent histogram harmless
     find_cut<NT>(rh, w.hist_copies, k, tmp, &s_b1);
     const uint32_t b1 = (uint32_t)s_b1;
+    // keys of slots past the visible ones are 0: below every score's key
+    // and below the cut bin's (b1 is the bin of a visible key)
+    const uint32_t klo = b1 << kHistShift, khi = klo | ((1u << kHistShift) - 1u);
     uint32_t na = 0, ne = 0;
     uint32_t keys[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
-      const int64_t s = wstart + 64 * j + lane;
-      keys[j] = score_key(v[j]);
-      s_keys[wave * 64 * PL + 64 * j + lane] = keys[j];
-      const uint32_t bin = keys[j] >> kHistShift;
-      na += (uint32_t)__popcll(__ballot(s < nv && bin > b1));
-      ne += (uint32_t)__popcll(__ballot(s < nv && bin == b1));
+      keys[j] = (wrel + 64 * j < nvb) ? score_key(v[j]) : 0u;
+      s_keys[wrel + 64 * j] = keys[j];
+      na += (uint32_t)__popcll(__ballot(keys[j] > khi));
+      ne += (uint32_t)__popcll(__ballot(keys[j] >= klo && keys[j] <= khi));
     }
     if (lane == 0) {
       wtot[0][wave] = na;
@@ -1145,12 +1148,11 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
-      const int64_t s = wstart + 64 * j + lane;
-      const bool eq = s < nv && (keys[j] >> kHistShift) == b1;
+      const bool eq = keys[j] >= klo && keys[j] <= khi;
       const uint64_t me = __ballot(eq);
       if (eq) {
         st_coh(rc + oe + (uint32_t)__popcll(me & lt),
-               ((keys[j] & 0xFFFFFu) << 12) | (uint32_t)(kTopkChunk - 1 - (s - start)));
+               ((keys[j] & 0xFFFFFu) << 12) | (uint32_t)(kTopkChunk - 1 - (wrel + 64 * j)));
         atomicAdd(l2 + ((keys[j] >> 9) & 2047u), 1u);  // first radix digit: key bits 19..9
       }
       oe += (uint32_t)__popcll(me);
@@ -1208,19 +1210,23 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   const uint64_t rec = s_rec;
   if ((rec >> 63) == 0ull) return;
   const bool none = (rec >> 62) & 1ull;
-  const uint32_t kt = (uint32_t)(rec >> 42) & 0xFFFFFu, rel = (uint32_t)(rec >> 29) & 0x1FFFu;
+  const uint32_t kt = (uint32_t)(rec >> 42) & 0xFFFFFu;
+  const int rel = (int)((rec >> 29) & 0x1FFFu);
   const uint32_t off = (uint32_t)rec & 0x7FFFu;
+  // the block's kept slots: key above KT, or equal to KT at a block-relative
+  // slot below rel (no candidate chosen: every key of the cut bin is at or
+  // below KT and rel is 0); slots past the visible ones hold key 0 < KT
   const uint32_t b1 = (uint32_t)s_b1;
+  const uint32_t KT = (b1 << kHistShift) | (none ? 0xFFFFFu : kt);
+  const int relv = none ? 0 : rel;
+  const int wrel = wave * 64 * PL + lane;
   // ---- kept slots of this block, in slot order, from offset `off`
   uint64_t msel[PL];
   uint32_t cnt = 0;
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
-    const int64_t s = wstart + 64 * j + lane;
-    const uint32_t key = s_keys[wave * 64 * PL + 64 * j + lane];
-    const uint32_t bin = key >> kHistShift, lo = key & 0xFFFFFu;
-    const bool sel = s < nv && (bin > b1 || (bin == b1 && !none &&
-                                             (lo > kt || (lo == kt && (uint32_t)(s - start) < rel))));
+    const uint32_t key = s_keys[wrel + 64 * j];
+    const bool sel = key > KT || (key == KT && wrel + 64 * j < relv);
     msel[j] = __ballot(sel);
     cnt += (uint32_t)__popcll(msel[j]);
   }
@@ -1229,12 +1235,12 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   uint32_t o = off;
 #pragma unroll
   for (int x = 0; x < NW; ++x) o += (x < wave) ? wtot[0][x] : 0u;
-  const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
-    const int64_t s = wstart + 64 * j + lane;
-    const uint32_t p = o + (uint32_t)__popcll(msel[j] & lt);
-    if (((msel[j] >> lane) & 1ull) && p < (uint32_t)k) orow[p] = sp ? pos[j] : (int32_t)s;
+    const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(msel[j] >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)msel[j], o));
+    if (((msel[j] >> lane) & 1ull) && p < (uint32_t)k)
+      orow[p] = sp ? pos[j] : (int32_t)(start + wrel + 64 * j);
     o += (uint32_t)__popcll(msel[j]);
   }
 }
