@@ -1580,8 +1580,16 @@ __device__ __forceinline__ void find_two_desc(const uint32_t* h, uint32_t need_a
     c[4 * j + 3] = hv.x;
     sum += hv.x + hv.y + hv.z + hv.w;
   }
-  uint32_t tot;
-  uint32_t acc = block_scan<NT>(sum, tmp, &tot);
+  // exclusive prefix over the block (the wave totals' slots are written
+  // again only after the barrier that ends this call)
+  constexpr int NW = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t inc = wave_incl_scan(sum);
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  uint32_t acc = inc - sum;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) acc += (x < wave) ? tmp[x] : 0u;
 #pragma unroll
   for (int q = 0; q < BPT; ++q) {
     const uint32_t b = (uint32_t)(kHistBins - 1 - (tid * BPT + q));
@@ -1793,17 +1801,20 @@ __global__ __launch_bounds__(kBandThreads) void topk_band_kernel(
   __syncthreads();
   for (uint32_t i = tid; i < cnt_c; i += NT) {
     const uint64_t x = mem[i];
-    uint32_t rk = 0u;
-    for (uint32_t j = 0; j < cnt_c; ++j) rk += (mem[j] > x) ? 1u : 0u;
-    if (rk + 1u == rem) s_thr = x;
+    uint32_t rk = 0u, eq = 0u;  // members ranked above; members of the same key (itself too)
+    for (uint32_t j = 0; j < cnt_c; ++j) {
+      const uint64_t y = mem[j];
+      rk += (y > x) ? 1u : 0u;
+      eq += ((y >> 32) == (x >> 32)) ? 1u : 0u;
+    }
+    if (rk + 1u == rem) {
+      s_thr = x;
+      s_ties = eq > 1u ? 1u : 0u;  // another key equals the threshold's
+    }
   }
   __syncthreads();
   const uint64_t thr = s_thr;
   const uint32_t TK = (uint32_t)(thr >> 32), TS = rank_slot(thr);
-  for (uint32_t i = tid; i < cnt_c; i += NT)
-    if ((uint32_t)(mem[i] >> 32) == TK && rank_slot(mem[i]) != TS)
-      s_ties = 1u;  // another key equals the threshold's
-  __syncthreads();
   const bool ties = s_ties != 0u;
 
   // ---- 4. kept slots in slot order.  Segment (g, wave) is the 256
