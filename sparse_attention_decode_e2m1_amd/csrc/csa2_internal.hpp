@@ -62,12 +62,13 @@ inline AttnSplit attn_split(int32_t K, int32_t W, int32_t rounds = 1) {
   return s;
 }
 // Rounds (of 64 entries) per attention split for a pass of `rows` rows: one,
-// unless the grid would exceed kAttnGridBlocks blocks (four times the split
-// kernel's blocks an MI355X holds at once); then doubled, up to 8, keeping
+// unless the grid would exceed kAttnGridBlocks blocks (the split kernel's
+// blocks an MI355X holds at once, two per compute unit: a grid just past it
+// would run a second wave of blocks); then doubled, up to 8, keeping
 // at least 2 splits per row (FP4 main cache only: the FP8 variant takes one
 // round).  A function of the shape alone, so the workspace query sizes the
 // partials of every pass exactly.
-constexpr int64_t kAttnGridBlocks = 2048;
+constexpr int64_t kAttnGridBlocks = 512;
 inline int32_t attn_rounds(int64_t rows, int32_t K, int32_t W, bool kv8) {
   int32_t rounds = 1;
   AttnSplit sp = attn_split(K, W, rounds);
