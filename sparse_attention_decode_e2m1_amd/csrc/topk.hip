@@ -1653,7 +1653,9 @@ __global__ __launch_bounds__(kBandThreads) void topk_band_kernel(
     }
   }
   float4 v[G];
-  int4 pos[G];
+  int4 pos[G];  // the slot map's positions (read only with a slot map)
+#pragma unroll
+  for (int g = 0; g < G; ++g) pos[g] = make_int4(0, 0, 0, 0);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int s0 = 4 * (g * NT + tid);
