@@ -792,40 +792,6 @@ __device__ __forceinline__ bool record_is(uint64_t rec, uint32_t gen) {
 
 constexpr int kBucketMax = kCoopThreads;  // candidates of the cut digit ranked directly
 
-// Digit d of a 2048-bin histogram held BPT bins per thread (thread t: bins
-// [t*BPT, (t+1)*BPT)) with count(> d) < rem <= count(>= d): *above =
-// count(> d), *cnt = count(d).  All NT threads call it.
-template <int NT>
-__device__ __forceinline__ uint32_t pick_digit(Bins<2048 / NT> cv, uint32_t rem, uint32_t* tmp,
-                                               uint32_t* above, uint32_t* cnt) {
-  constexpr int BPT = 2048 / NT;
-  __shared__ uint32_t s_pick[3];
-  if (threadIdx.x == 0) s_pick[0] = s_pick[1] = s_pick[2] = 0u;
-  uint32_t sum = 0;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) sum += cv.v[j];
-  uint32_t tot;
-  const uint32_t ex = block_scan<NT>(sum, tmp, &tot);
-  uint32_t acc = tot - ex - sum;
-  if (acc < rem && acc + sum >= rem) {
-#pragma unroll
-    for (int j = BPT - 1; j >= 0; --j) {
-      if (acc < rem && acc + cv.v[j] >= rem) {
-        s_pick[0] = BPT * threadIdx.x + j;
-        s_pick[1] = acc;
-        s_pick[2] = cv.v[j];
-      }
-      acc += cv.v[j];
-    }
-  }
-  __syncthreads();
-  const uint32_t d = s_pick[0];
-  *above = s_pick[1];
-  *cnt = s_pick[2];
-  __syncthreads();
-  return d;
-}
-
 // The completing block of row r (every block of the row has published its
 // counts, candidates and first-digit bins): the threshold among the
 // candidates, each block's count of chosen candidates, the blocks' output
@@ -842,11 +808,13 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
                               uint32_t gen) {
   constexpr int NT = kCoopThreads, NW = kCoopWaves, CH = kTopkChunk, BPT = 2048 / NT;
   uint32_t* cntE = smem;                    // candidates per block
-  uint32_t* chosen = cntE + NT;             // chosen candidates per block
+  uint32_t* chosen = cntE + NT;             // chosen candidates per block (register pass)
   uint32_t* rhist = chosen + NT;            // 2048 radix bins (many ties only)
   uint64_t* bucket = reinterpret_cast<uint64_t*>(rhist + 2048);  // kBucketMax
   uint32_t* pcs = reinterpret_cast<uint32_t*>(bucket + kBucketMax);  // kCoopCP x NW counts
-  __shared__ uint32_t s_tot[2][NW];
+  __shared__ uint32_t chosen2[kCoopThreads];  // chosen candidates per block (the other passes)
+  __shared__ uint32_t s_tot[3][NW];           // per wave: kept, candidates, first-digit bins
+  __shared__ uint32_t s_pick0[3];             // the first cut digit, the count above it, its count
   __shared__ uint32_t s_nb, s_rest;
   __shared__ uint64_t s_thr;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -878,23 +846,32 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
   Bins<BPT> g0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) g0.v[j] = ld_coh(l2 + BPT * tid + j);
-  // ---- totals (kept, candidates); per-block candidate counts to LDS
+  // ---- totals (kept, candidates, first-digit bins by wave); per-block
+  // candidate counts to LDS
+  uint32_t gsum = 0u;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) gsum += g0.v[j];
+  const uint32_t gincl = wave_incl_scan(gsum);  // bins of this wave's threads up to this one
   {
     const uint32_t sa = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ca), 63);
     const uint32_t se = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ce), 63);
+    const uint32_t sg = (uint32_t)__builtin_amdgcn_readlane((int)gincl, 63);
     if (lane == 0) {
       s_tot[0][wave] = sa;
       s_tot[1][wave] = se;
+      s_tot[2][wave] = sg;
     }
   }
   if (tid < nblk) {
     cntE[tid] = ce;
     chosen[tid] = 0u;
+    chosen2[tid] = 0u;
   }
   if (tid == 0) {
     s_nb = 0u;
     s_thr = ~0ull;
     s_rest = 0u;
+    s_pick0[0] = s_pick0[1] = s_pick0[2] = 0u;
   }
   __syncthreads();
   if (ce > (uint32_t)spec) s_rest = 1u;  // some block has candidates beyond the first round trip
@@ -930,26 +907,50 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
     }
   };
   auto for_all = [&](auto&& f) { for_all_u([&](uint64_t x, bool) { f(x); }); };
-  // chosen[b] += lanes with ch set whose candidate is in block b (one LDS
+  // chosen2[b] += lanes with ch set whose candidate is in block b (one LDS
   // add per distinct block of the wave)
   auto add_chosen = [&](bool ch, uint32_t b, bool uni) {
     uint64_t pend = __ballot(ch);
     if (uni) {
-      if (pend && lane == __ffsll((unsigned long long)pend) - 1) atomicAdd(&chosen[b], (uint32_t)__popcll(pend));
+      if (pend && lane == __ffsll((unsigned long long)pend) - 1) atomicAdd(&chosen2[b], (uint32_t)__popcll(pend));
       return;
     }
     while (pend) {
       const int l = __ffsll((unsigned long long)pend) - 1;
       const uint32_t bl = (uint32_t)__builtin_amdgcn_readlane((int)b, l);
       const uint64_t mm = __ballot(ch && b == bl);
-      if (lane == l) atomicAdd(&chosen[bl], (uint32_t)__popcll(mm));
+      if (lane == l) atomicAdd(&chosen2[bl], (uint32_t)__popcll(mm));
       pend &= ~mm;
     }
   };
   uint64_t thr = ~0ull;  // rank values (low 52 bits) >= thr are chosen; ~0: none
   if (need > 0) {
-    uint32_t above0, cnt0;
-    const uint32_t d0 = pick_digit<NT>(g0, need, tmp, &above0, &cnt0);
+    // the first digit d0 with count(> d0) < need <= count(>= d0): thread t
+    // holds bins [t BPT, (t+1) BPT); the bins above its own are the total
+    // less the bins up to it
+    {
+      uint32_t gbel = gincl, gtot = 0u;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) {
+        const uint32_t c = s_tot[2][x];
+        gbel += (x < wave) ? c : 0u;
+        gtot += c;
+      }
+      uint32_t acc = gtot - gbel;  // bins of higher threads
+      if (acc < need && acc + gsum >= need) {
+#pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+          if (acc < need && acc + g0.v[j] >= need) {
+            s_pick0[0] = BPT * tid + j;
+            s_pick0[1] = acc;
+            s_pick0[2] = g0.v[j];
+          }
+          acc += g0.v[j];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t d0 = s_pick0[0], above0 = s_pick0[1], cnt0 = s_pick0[2];
     const uint32_t rem = need - min(above0, need);
     const bool whole = cnt0 == rem;
     // one pass: digits above d0 chosen (d0 too when its bucket is taken
@@ -992,6 +993,7 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
       }
       __syncthreads();
       // block b's candidates are registers' lanes [b*spec, (b+1)*spec): spec/64 waves' counts
+      // (chosen[] is written here only, by its own thread; the other passes add to chosen2[])
       if (tid < nblk) {
         uint32_t c = 0;
         for (int f0 = tid * spec; f0 < (tid + 1) * spec; f0 += 64) c += pcs[(f0 / NT) * NW + (f0 % NT) / 64];
@@ -1007,8 +1009,8 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
           if (p < (uint32_t)kBucketMax) bucket[p] = x;
         }
       });
+      __syncthreads();  // (the register pass ended with one)
     }
-    __syncthreads();
     const uint64_t low52 = (1ull << 52) - 1;
     if (whole) {
       thr = (uint64_t)d0 << 41;
@@ -1036,9 +1038,19 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
     }
   }
   __syncthreads();
-  // ---- output offsets: kept and chosen slots of the blocks before
-  uint32_t tot;
-  const uint32_t off = block_scan<NT>((tid < nblk) ? ca + chosen[tid] : 0u, tmp, &tot);
+  // ---- output offsets: kept and chosen slots of the blocks before (by the
+  // first wave alone when the row has at most 64 blocks)
+  const bool one_wave = nblk <= 64;
+  if (one_wave && wave != 0) return;
+  const uint32_t vb = (tid < nblk) ? ca + chosen[tid] + chosen2[tid] : 0u;
+  uint32_t tot, off;
+  if (one_wave) {
+    const uint32_t inc = wave_incl_scan(vb);
+    off = inc - vb;
+    tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  } else {
+    off = block_scan<NT>(vb, tmp, &tot);
+  }
   // the chosen candidates are those with (lo, ~slot) >= thr: with lo == kt,
   // the slots up to slot_t
   const bool none = thr == ~0ull;
@@ -1051,7 +1063,7 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
     else st_coh(recs + tid, rec);
   }
   const uint32_t kept = min(tot, (uint32_t)k);  // k unless the histogram disagreed with the scores
-  for (uint32_t i = kept + tid; i < (uint32_t)k; i += NT) orow[i] = -1;
+  for (uint32_t i = kept + tid; i < (uint32_t)k; i += one_wave ? 64u : (uint32_t)NT) orow[i] = -1;
   if (count_out && tid == 0) count_out[r] = (int32_t)kept;
 }
 
