@@ -825,15 +825,18 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, void* ws, 
       if (mode == CSA2_MODE_FULL && a->P > 0) {
         int32_t* pool_out = a->pool_out + (size_t)r0 * a->P;
         int32_t* pcount = a->pool_count_out + r0;
-        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
-                                    pcount, L.tw, st),
-                 "pool select launch");
         // the pool's scores gathered into a dense row (with the histogram its
-        // selection starts from, unless it takes one block per row)
+        // selection starts from, unless it takes one block per row): by the
+        // one-wait selection itself as it writes the pool, else by a kernel
         const bool prow = topk_row_pass(nr, a->P);
-        CSA2_LAUNCH(4, PROF_STREAM, launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
-                                      prow ? nullptr : L.tw.hist, L.tw.hist_stride, L.tw.hist_copies, st),
-                 "pool gather launch");
+        bool gathered = false;
+        CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.scores, nr, L.n_out, qpos, 1, n_max, nullptr, a->P, pool_out,
+                                    pcount, L.tw, st, false, prow ? L.pscores : nullptr, &gathered),
+                 "pool select launch");
+        if (!gathered)
+          CSA2_LAUNCH(4, PROF_STREAM, launch_gather_scores(L.scores, L.n_out, pool_out, a->P, pcount, nr, L.pscores,
+                                        prow ? nullptr : L.tw.hist, L.tw.hist_stride, L.tw.hist_copies, st),
+                   "pool gather launch");
         CSA2_LAUNCH(2, PROF_STREAM, launch_topk_select(L.pscores, nr, a->P, pcount, 0, a->P, pool_out, a->K, idx,
                                     nullptr, L.tw, st, prow),
                  "top-k select launch");

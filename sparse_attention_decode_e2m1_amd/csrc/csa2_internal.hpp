@@ -239,7 +239,8 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st,
-                              bool row_ok = false);
+                              bool row_ok = false, float* gather_out = nullptr,
+                              bool* gathered = nullptr);
 hipError_t launch_sparse_attn(const uint16_t* q, int32_t rows, int32_t T, int32_t D, int32_t dv,
                               const uint8_t* codes, const uint8_t* scales, int64_t cap,
                               const int32_t* idx, int32_t K, const uint8_t* swa,

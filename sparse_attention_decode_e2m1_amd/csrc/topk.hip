@@ -1070,7 +1070,10 @@ __device__ void coop_complete(int r, int64_t nv, int32_t k, int nblk, int32_t* _
 __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_coop_kernel(
     const float* __restrict__ scores, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t nv_add, const int32_t* __restrict__ slot_pos, int32_t k, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, TopkWs w, uint32_t gen, uint32_t wait_limit) {
+    int32_t* __restrict__ count_out, TopkWs w, uint32_t gen, uint32_t wait_limit,
+    float* __restrict__ gout) {
+  // gout (optional, row stride k): each kept slot's score at its output
+  // place (a candidate pool's scores, gathered for the selection inside it)
   constexpr int NT = kCoopThreads, NW = kCoopWaves, PL = kCoopPL;
   extern __shared__ uint64_t smem64[];
   uint32_t* smem = reinterpret_cast<uint32_t*>(smem64);
@@ -1094,7 +1097,10 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       const int64_t s = start + j * NT + tid;
-      if (s < nv) orow[s] = sp ? sp[s] : (int32_t)s;
+      if (s < nv) {
+        orow[s] = sp ? sp[s] : (int32_t)s;
+        if (gout) gout[(int64_t)r * k + s] = scores[(int64_t)r * n + s];
+      }
     }
     if (blockIdx.x == 0) {
       for (int64_t j = nv + tid; j < k; j += NT) orow[j] = -1;
@@ -1251,8 +1257,13 @@ __global__ __launch_bounds__(kCoopThreads) __attribute__((amdgpu_waves_per_eu(4,
   for (int j = 0; j < PL; ++j) {
     const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(msel[j] >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)msel[j], o));
-    if (((msel[j] >> lane) & 1ull) && p < (uint32_t)k)
+    if (((msel[j] >> lane) & 1ull) && p < (uint32_t)k) {
       orow[p] = sp ? pos[j] : (int32_t)(start + wrel + 64 * j);
+      if (gout) {  // the score back from its key (-0 comes back as +0, the same key)
+        const uint32_t key = s_keys[wrel + 64 * j];
+        gout[(int64_t)r * k + p] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+      }
+    }
     o += (uint32_t)__popcll(msel[j]);
   }
 }
@@ -2150,7 +2161,8 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
                               const int32_t* n_valid, int32_t nv_add, int64_t n_max,
                               const int32_t* slot_pos, int32_t k, int32_t* idx_out,
                               int32_t* count_out, const TopkWs& w, hipStream_t st,
-                              bool row_ok) {
+                              bool row_ok, float* gather_out, bool* gathered) {
+  if (gathered) *gathered = false;
   // Many rows, no histogram built: one block per row.
   if (row_ok && topk_row_pass(rows, n_max)) {
     const int32_t nwp = (int32_t)(((n + 31) / 32 + 3) & ~3);
@@ -2199,7 +2211,8 @@ hipError_t launch_topk_select(const float* scores, int32_t rows, int64_t n,
         (int64_t)rows * nblk <= coop_capacity()) {
       CSA2_KERNEL(true, true, topk_coop_kernel, dim3((unsigned)nblk, (unsigned)rows),
                   dim3(kCoopThreads), kCoopLds, st, scores, n, n_valid, nv_add, slot_pos, k,
-                  idx_out, count_out, w, next_generation(), wait_limit());
+                  idx_out, count_out, w, next_generation(), wait_limit(), gather_out);
+      if (gathered) *gathered = gather_out != nullptr;
       set_topk_last(kTopkOneWait);
       return hipGetLastError();
     }
