@@ -173,6 +173,14 @@ def _pool_scores():
     return np.stack([rng.permutation(top), rng.permutation(top)])  # cached: never written
 
 
+def test_band_needs_rows_of_whole_16_byte_words():
+    """A row stride that is not a multiple of 4 slots cannot take the key
+    band's 16-byte loads: the automatic choice is the row kernel, same result."""
+    s = _scores(2, 4099, 84, "normal")
+    nv = np.array([4099, 3001], np.int32)
+    _check(s, nv, 256, api.TOPK_ROW)
+
+
 def test_band_narrow_pool_scores():
     """A pool's scores: the top 16384 of a million, so every key shares its
     leading bits (the sample's own key range sets the bins)."""
