@@ -486,7 +486,7 @@ hipError_t launch_index_score(const uint8_t* codes, const uint8_t* scales, int32
   } while (0)
   switch (DI / 128) {
     case 1:
-      if (HI <= 4) CSA2_IS_LAUNCH(1, 4, 8);
+      if (HI <= 4) CSA2_IS_LAUNCH(1, 4, 4);
       else if (HI <= 8) CSA2_IS_LAUNCH(1, 2, 8);
       else CSA2_IS_LAUNCH(1, 1, 4);
       break;
